@@ -1,0 +1,261 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+One step = one MSA prefill of a 32768-token sequence (64 query heads, 4 KV
+heads, head_dim 128, index dim 64, B_k 128, k 16, planted-needle index keys)
+followed by one decode step of 64 sequences with 131072-token caches (same
+heads; planted index keys per sequence). Inputs are generated on the device
+before timing and stay resident in HBM.
+
+Prints one JSON line. `value` is the prefill sparse-attention throughput
+F_main / t_prefill, where F_main = 4 * d * hpg * sum over (query, group) of the
+attended token count and t_prefill is the whole prefill call (index branch
+included). Decode KV GB/s (algorithmic bytes / whole decode call) is reported
+alongside, with per-stage times from the profiled entry points and the
+roofline of the dominant kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MSA prefill sparse-attn TFLOP/s (% MFMA peak) + decode KV GB/s @128K ctx"
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+
+# Bench workload
+N_PREFILL, HQ, G, D, DI, BK, TOPK = 32768, 64, 4, 128, 64, 128, 16
+DEC_B, DEC_L = 64, 131072
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic work ------------------------------------------------------
+
+def attended_tokens(i: int, topk: int, bk: int = BK) -> int:
+    """|T| for query row i: every selected block older than the own block is
+    full, the own block contributes i % bk + 1 keys, and |Sel| = min(k, b_loc+1)."""
+    b_loc = i // bk
+    return bk * (min(topk, b_loc + 1) - 1) + (i % bk + 1)
+
+
+def prefill_flops(rows, n_groups=G, hpg=HQ // G, d=D, topk=TOPK):
+    t = sum(attended_tokens(int(i), topk) for i in rows)
+    return 4.0 * d * hpg * n_groups * t
+
+
+def prefill_flops_full(n, **kw):
+    # closed form summed per block for speed
+    topk = kw.get("topk", TOPK)
+    tot = 0
+    for blk in range((n + BK - 1) // BK):
+        lo, hi = blk * BK, min(n, (blk + 1) * BK)
+        cnt = hi - lo
+        tot += cnt * BK * (min(topk, blk + 1) - 1) + sum(range(1, cnt + 1))
+    return 4.0 * kw.get("d", D) * kw.get("hpg", HQ // G) * kw.get("n_groups", G) * tot
+
+
+def index_flops_full(n, topk=TOPK):
+    tot = 0
+    for i_blk in range((n + BK - 1) // BK):
+        cnt = min(n, (i_blk + 1) * BK) - i_blk * BK
+        if i_blk >= topk:
+            tot += cnt * BK * i_blk
+    return 2.0 * DI * G * tot
+
+
+def decode_bytes(ctx_lens, topk=TOPK):
+    tot = 0
+    for L in ctx_lens:
+        i = L - 1
+        b_loc = i // BK
+        scored = BK * b_loc if b_loc >= topk else 0
+        tot += scored * DI * 2                                # k_idx keys scored
+        tot += G * attended_tokens(i, topk) * 2 * D * 2       # K and V of the attended tokens
+        tot += HQ * D * 2 * 2 + G * DI * 2                    # q, out, q_idx
+    return float(tot)
+
+
+# ---- device inputs -----------------------------------------------------------
+
+def make_inputs(torch, dev):
+    import msa_synth as syn
+    dims = syn.Dims(num_q_heads=HQ, num_kv_heads=G, head_dim=D, index_dim=DI, block_size=BK, topk=TOPK)
+    pin = syn.PrefillInputs(N_PREFILL, dims, 0, "planted", n_planted=8)
+    pre = [t(device=dev)[None].contiguous() for t in (pin.q, pin.k, pin.v, pin.q_idx, pin.k_idx)]
+    dec = syn.DecodeInputs(DEC_B, DEC_L, dims, 0)
+    q = torch.stack([dec.q(b, dev) for b in range(DEC_B)]).contiguous()
+    qi = torch.stack([dec.q_idx(b, dev) for b in range(DEC_B)]).contiguous()
+    kc = torch.empty((DEC_B, DEC_L, G, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    kic = torch.empty((DEC_B, DEC_L, DI), dtype=torch.bfloat16, device=dev)
+    for b in range(DEC_B):
+        kc[b] = dec.k_cache(b, device=dev)
+        vc[b] = dec.v_cache(b, device=dev)
+        kic[b] = dec.k_idx_cache(b, device=dev)
+    lens = torch.tensor(dec.ctx_lens, dtype=torch.int32, device=dev)
+    return pin, pre, (q, qi, kc, vc, kic, lens), dec
+
+
+# ---- CPU baseline (the oracle) -------------------------------------------------
+
+def cpu_baseline(pin, budget_s=15.0):
+    from oracle import msa_oracle as mo
+    import msa_synth as syn
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    f = mo.to_f64
+    t0 = time.time()
+    ki, k, v = f(pin.k_idx()), f(pin.k()), f(pin.v())
+    log(f"cpu_baseline: host inputs {time.time() - t0:.1f}s")
+    rows_all = syn.stratified_rows(N_PREFILL, 4096, BK, 0, TOPK)
+    rng = np.random.default_rng(1)
+    rng.shuffle(rows_all)
+    done, flops, spent = 0, 0.0, 0.0
+    chunk = 16
+    while spent < budget_s and done < len(rows_all):
+        rows = np.sort(rows_all[done:done + chunk])
+        q, qi = f(pin.q(rows)), f(pin.q_idx(rows))
+        t = time.time()
+        mo.prefill_rows(rows, q, qi, ki, k, v, block_size=BK, topk=TOPK)
+        spent += time.time() - t
+        flops += prefill_flops(rows)
+        done += len(rows)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{done} random rows of the 32768-token prefill workload (selection + attention, "
+                      f"float64 numpy), {spent:.1f}s of oracle time"}
+
+
+# ---- main ---------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--profile-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_long_07_amd as msa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    msa.load()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    pin, pre, dec_in, dec = make_inputs(torch, dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    p = msa.params(HQ, G, D, DI, BK, TOPK)
+    ws_p = torch.empty(msa.prefill_workspace_bytes(p, 1, N_PREFILL), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(msa.decode_workspace_bytes(p, DEC_B, DEC_L), dtype=torch.uint8, device=dev)
+    out_p = torch.empty_like(pre[0])
+    out_d = torch.empty_like(dec_in[0])
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        msa.prefill(*pre, topk=TOPK, workspace=ws_p, out=out_p)
+        if evs:
+            evs[1].record()
+        msa.decode(*dec_in, topk=TOPK, workspace=ws_d, out=out_d)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = wall * 1e3 / args.steps
+
+    # per-stage times (profiled entry points: HIP events on the launch stream)
+    pst, dst = [], []
+    for _ in range(args.profile_reps):
+        ms = []
+        msa.prefill(*pre, topk=TOPK, workspace=ws_p, out=out_p, stage_ms=ms)
+        pst.append(ms)
+        ms = []
+        msa.decode(*dec_in, topk=TOPK, workspace=ws_d, out=out_d, stage_ms=ms)
+        dst.append(ms)
+    pst = np.mean(np.array(pst), axis=0)
+    dst = np.mean(np.array(dst), axis=0)
+
+    f_main = prefill_flops_full(N_PREFILL)
+    f_idx = index_flops_full(N_PREFILL)
+    dbytes = decode_bytes(dec.ctx_lens)
+    value = f_main / (pre_ms * 1e-3) / 1e12
+    attn_ms = float(pst[3])
+    attn_tflops = f_main / (attn_ms * 1e-3) / 1e12
+    t_main_ms = float(pst[2] + pst[3] + pst[4])
+    dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
+    dec_idx_bytes = sum((BK * ((L - 1) // BK) if (L - 1) // BK >= TOPK else 0) * DI * 2 for L in dec.ctx_lens)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded Irwin-Hall ~N(0,1) bf16 Q/K/V, integer index keys with planted needles",
+        "config": {"workload": "prefill N=32768 (64q/4kv, d=128, d_idx=64, B_k=128, k=16) + decode 64 x 131072",
+                   "global_batch": 1, "seq_len": N_PREFILL, "decode_batch": DEC_B, "decode_ctx": DEC_L,
+                   "parallelism": "single GPU"},
+        "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
+        "prefill": {"ms": round(pre_ms, 4), "F_main_tflop": round(f_main / 1e12, 4),
+                    "F_idx_tflop": round(f_idx / 1e12, 4),
+                    "stage_ms": {k: round(float(x), 4) for k, x in zip(msa.PREFILL_STAGES, pst)},
+                    "main_branch_tflops": round(f_main / (t_main_ms * 1e-3) / 1e12, 2),
+                    "end_to_end_tflops": round((f_main + f_idx) / (pre_ms * 1e-3) / 1e12, 2),
+                    "index_tflops": round(f_idx / (float(pst[0]) * 1e-3) / 1e12, 2)},
+        "decode": {"ms": round(dec_ms, 4), "bytes_gb": round(dbytes / 1e9, 4), "GB/s": round(dec_gbs, 1),
+                   "pct_of_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
+                   "stage_ms": {k: round(float(x), 4) for k, x in zip(msa.DECODE_STAGES, dst)},
+                   "index_GB/s": round(dec_idx_bytes / (float(dst[0]) * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": "k_attn_prefill", "bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+"""Python binding of libmsa, the MI355X MiniMax Sparse Attention hot path.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/msa.h. torch supplies device
+memory (inputs, outputs, workspace) and the current stream. There is no CPU or
+eager fallback: if libmsa.so is missing the import of the library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+
+MSA_OK = 0
+_STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_UNSUPPORTED",
+           -3: "MSA_ERR_WORKSPACE_TOO_SMALL", -4: "MSA_ERR_HIP"}
+
+EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_decode_workspace_bytes", "msa_decode",
+            "msa_prefill_profiled", "msa_decode_profiled", "msa_index_scores", "msa_select_blocks",
+            "msa_status_string")
+PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "combine")
+DECODE_STAGES = ("index_score", "select", "attn", "combine")
+
+
+class MsaParams(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmsa.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"{p} not found: build it with `python -m block_sparse_long_07_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    P = ctypes.POINTER(MsaParams)
+    lib.msa_prefill_workspace_bytes.argtypes = [P, i32, i64]
+    lib.msa_prefill_workspace_bytes.restype = sz
+    lib.msa_prefill.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_prefill.restype = ctypes.c_int
+    lib.msa_decode_workspace_bytes.argtypes = [P, i32, i64]
+    lib.msa_decode_workspace_bytes.restype = sz
+    lib.msa_decode.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_decode.restype = ctypes.c_int
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.msa_prefill_profiled.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, fp]
+    lib.msa_prefill_profiled.restype = ctypes.c_int
+    lib.msa_decode_profiled.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, fp]
+    lib.msa_decode_profiled.restype = ctypes.c_int
+    lib.msa_index_scores.argtypes = [P, i64, vp, vp, vp, vp]
+    lib.msa_index_scores.restype = ctypes.c_int
+    lib.msa_select_blocks.argtypes = [P, i64, vp, vp, vp]
+    lib.msa_select_blocks.restype = ctypes.c_int
+    lib.msa_status_string.argtypes = [ctypes.c_int]
+    lib.msa_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def params(num_q_heads=64, num_kv_heads=4, head_dim=128, index_dim=64, block_size=128, topk=16,
+           softmax_scale: Optional[float] = None) -> MsaParams:
+    return MsaParams(num_q_heads, num_kv_heads, head_dim, index_dim, block_size, topk,
+                     float(softmax_scale) if softmax_scale else 0.0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, what: str):
+    if status != MSA_OK:
+        raise MsaError(status, what)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def prefill_workspace_bytes(p: MsaParams, batch: int, seq_len: int) -> int:
+    return int(load().msa_prefill_workspace_bytes(ctypes.byref(p), batch, seq_len))
+
+
+def prefill(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale=None,
+            want_sel=False, want_lse=False, workspace: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, stage_ms: Optional[list] = None):
+    """Causal MSA prefill. q [B,N,Hq,d], k/v [B,N,G,d], q_idx [B,N,G,d_idx],
+    k_idx [B,N,d_idx], all bf16 on one device. Returns (out, sel or None, lse or None).
+    With stage_ms (a list) the profiled entry point runs, synchronises, and the
+    per-stage milliseconds (PREFILL_STAGES order) are appended to it."""
+    lib = load()
+    B, N, Hq, d = q.shape
+    G = k.shape[2]
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (q_idx, "q_idx"), (k_idx, "k_idx")):
+        _need(t, torch.bfloat16, name)
+    p = params(Hq, G, d, q_idx.shape[-1], block_size, topk, softmax_scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    sel = torch.empty((B, G, N, topk), dtype=torch.int32, device=dev) if want_sel else None
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    nbytes = int(lib.msa_prefill_workspace_bytes(ctypes.byref(p), B, N))
+    if nbytes == 0:
+        raise MsaError(-2, "msa_prefill_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    args = (ctypes.byref(p), B, N, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
+            _ptr(out), _ptr(sel), _ptr(lse), _ptr(workspace), nbytes, _stream(dev))
+    if stage_ms is None:
+        _check(lib.msa_prefill(*args), "msa_prefill")
+    else:
+        ms = (ctypes.c_float * len(PREFILL_STAGES))()
+        _check(lib.msa_prefill_profiled(*args, ms), "msa_prefill_profiled")
+        stage_ms.extend(float(x) for x in ms)
+    return out, sel, lse
+
+
+def decode_workspace_bytes(p: MsaParams, batch: int, max_ctx: int) -> int:
+    return int(load().msa_decode_workspace_bytes(ctypes.byref(p), batch, max_ctx))
+
+
+def decode(q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, *, topk=16, block_size=128,
+           softmax_scale=None, want_sel=False, want_lse=False,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           stage_ms: Optional[list] = None):
+    """One decode step. q [B,Hq,d], q_idx [B,G,d_idx], k_cache/v_cache
+    [B,max_ctx,G,d], k_idx_cache [B,max_ctx,d_idx] (bf16), ctx_lens int32 [B]
+    on the device (the new token is row ctx_lens[b]-1). Returns (out, sel, lse)."""
+    lib = load()
+    B, Hq, d = q.shape
+    max_ctx, G = k_cache.shape[1], k_cache.shape[2]
+    for t, name in ((q, "q"), (q_idx, "q_idx"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                    (k_idx_cache, "k_idx_cache")):
+        _need(t, torch.bfloat16, name)
+    _need(ctx_lens, torch.int32, "ctx_lens")
+    p = params(Hq, G, d, q_idx.shape[-1], block_size, topk, softmax_scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    sel = torch.empty((B, G, topk), dtype=torch.int32, device=dev) if want_sel else None
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    nbytes = int(lib.msa_decode_workspace_bytes(ctypes.byref(p), B, max_ctx))
+    if nbytes == 0:
+        raise MsaError(-1, "msa_decode_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    args = (ctypes.byref(p), B, max_ctx, _ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache),
+            _ptr(k_idx_cache), _ptr(ctx_lens), _ptr(out), _ptr(sel), _ptr(lse),
+            _ptr(workspace), nbytes, _stream(dev))
+    if stage_ms is None:
+        _check(lib.msa_decode(*args), "msa_decode")
+    else:
+        ms = (ctypes.c_float * len(DECODE_STAGES))()
+        _check(lib.msa_decode_profiled(*args, ms), "msa_decode_profiled")
+        stage_ms.extend(float(x) for x in ms)
+    return out, sel, lse
+
+
+def index_scores(q_idx, k_idx, *, num_q_heads=None, topk=16, block_size=128, scores=None):
+    """Pooled index scores of one sequence: q_idx [N,G,d_idx], k_idx [N,d_idx]
+    -> scores fp32 [N,G,nb] (defined for rows whose own block is >= topk, b < own block)."""
+    lib = load()
+    N, G, di = q_idx.shape
+    _need(q_idx, torch.bfloat16, "q_idx")
+    _need(k_idx, torch.bfloat16, "k_idx")
+    nb = (N + block_size - 1) // block_size
+    p = params(num_q_heads or 16 * G, G, 128, di, block_size, topk)
+    if scores is None:
+        scores = torch.full((N, G, nb), float("nan"), dtype=torch.float32, device=q_idx.device)
+    _check(lib.msa_index_scores(ctypes.byref(p), N, _ptr(q_idx), _ptr(k_idx), _ptr(scores),
+                                _stream(q_idx.device)), "msa_index_scores")
+    return scores
+
+
+def select_blocks(scores, *, topk=16, block_size=128, sel=None):
+    """Top-k block selection from pooled scores [N,G,nb] -> sel int32 [G,N,topk]."""
+    lib = load()
+    N, G, nb = scores.shape
+    _need(scores, torch.float32, "scores")
+    p = params(16 * G, G, 128, 64, block_size, topk)
+    if sel is None:
+        sel = torch.empty((G, N, topk), dtype=torch.int32, device=scores.device)
+    _check(lib.msa_select_blocks(ctypes.byref(p), N, _ptr(scores), _ptr(sel), _stream(scores.device)),
+           "msa_select_blocks")
+    return sel
+
+
+def status_string(status: int) -> str:
+    return load().msa_status_string(status).decode()

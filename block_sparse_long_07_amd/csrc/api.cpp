@@ -1,0 +1,399 @@
+// C ABI of libmsa: argument validation, workspace carving and the launch
+// sequence of the MSA prefill and decode hot path on one MI355X.
+//
+// Prefill, per sequence and per window of up to kWindowMax query rows:
+//   index scores -> top-k selection -> reverse index + tile schedule ->
+//   persistent KV-outer attention -> combine.
+// Windows bound the workspace (block scores and partials grow with the rows of
+// a window, not with the sequence), which is what makes 1M-token prefill fit.
+// Decode: index scores -> selection -> per-(sequence, group, slot) attention ->
+// combine.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "msa.h"
+#include "msa_launch.h"
+
+namespace {
+
+using namespace msa;
+
+constexpr int64_t kWindowMax = 65536;  // query rows per prefill window
+constexpr int kTileQ = 16;             // queries per KV-outer tile
+constexpr int64_t kMaxSeq = 1 << 20;   // LDS reverse-index masks cover <= 8192 blocks
+constexpr size_t kAlign = 256;
+
+struct Shape {
+  int Hq, G, k;
+  float scale_log2;
+};
+
+msa_status check_params(const msa_params* p, Shape* s) {
+  if (!p) return MSA_ERR_INVALID_ARG;
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0 || p->index_dim <= 0 ||
+      p->block_size <= 0 || p->topk <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (p->num_q_heads % p->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
+  if (p->head_dim != kHeadDim || p->index_dim != kIndexDim || p->block_size != kBlock ||
+      p->num_q_heads / p->num_kv_heads != kHpg || p->num_kv_heads > 8 || p->topk > kMaxTopk)
+    return MSA_ERR_UNSUPPORTED;
+  if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARG;
+  s->Hq = p->num_q_heads;
+  s->G = p->num_kv_heads;
+  s->k = p->topk;
+  const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  s->scale_log2 = scale * 1.4426950408889634f;
+  return MSA_OK;
+}
+
+inline bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// entries of rows [a, b): G * sum_i min(k, floor(i/128) + 1)
+int64_t entries_in(int64_t a, int64_t b, int G, int k) {
+  int64_t e = 0;
+  for (int64_t blk = a / kBlock; blk * kBlock < b; ++blk) {
+    const int64_t lo = std::max(a, blk * kBlock), hi = std::min(b, (blk + 1) * kBlock);
+    e += (hi - lo) * std::min<int64_t>(k, blk + 1);
+  }
+  return e * G;
+}
+
+struct PrefillLayout {
+  int64_t W;  // window rows
+  int nb;     // blocks of the sequence
+  int64_t nch, Lc, nblk, e_cap, tile_cap, slots;
+  size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, part_o, part_lse, total;
+};
+
+bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
+  if (N <= 0 || N > kMaxSeq) return false;
+  L->nb = (int)cdiv(N, kBlock);
+  L->W = std::min<int64_t>(cdiv(N, kBlock) * kBlock, kWindowMax);
+  L->nch = cdiv(L->W, 64);
+  L->Lc = (int64_t)s.G * L->nb * L->nch;
+  L->nblk = cdiv(L->Lc, 4096);
+  if (L->nblk > 16384) return false;
+  L->e_cap = L->W * s.G * s.k;
+  L->tile_cap = cdiv(L->e_cap, kTileQ) + (int64_t)s.G * L->nb;
+  L->slots = L->W * s.G * s.k;
+  size_t off = 0;
+  L->sblk = off;       off += up((size_t)L->W * s.G * L->nb * sizeof(float));
+  L->sel = off;        off += up((size_t)L->W * s.G * s.k * sizeof(int32_t));
+  L->chunkcnt = off;   off += up((size_t)L->Lc * sizeof(int32_t));
+  L->chunkoff = off;   off += up((size_t)(L->Lc + 1) * sizeof(int32_t));
+  L->bsum = off;       off += up((size_t)(L->nblk + 1) * sizeof(int32_t));
+  L->entries = off;    off += up((size_t)L->e_cap * sizeof(int32_t));
+  L->tile_start = off; off += up((size_t)((int64_t)s.G * L->nb + 1) * sizeof(int32_t));
+  L->tiles = off;      off += up((size_t)L->tile_cap * 4 * sizeof(int32_t));
+  L->tile_info = off;  off += up(4 * sizeof(int32_t));
+  L->part_o = off;     off += up((size_t)L->slots * kHpg * kHeadDim * sizeof(uint16_t));
+  L->part_lse = off;   off += up((size_t)L->slots * kHpg * sizeof(float));
+  L->total = off;
+  return true;
+}
+
+struct DecodeLayout {
+  int nb;
+  size_t sblk, sel, part_o, part_lse, total;
+};
+
+bool decode_layout(const Shape& s, int32_t B, int64_t max_ctx, DecodeLayout* L) {
+  if (B <= 0 || max_ctx <= 0) return false;
+  L->nb = (int)cdiv(max_ctx, kBlock);
+  const size_t items = (size_t)B * s.G * s.k;
+  size_t off = 0;
+  L->sblk = off;     off += up((size_t)B * s.G * L->nb * sizeof(float));
+  L->sel = off;      off += up(items * sizeof(int32_t));
+  L->part_o = off;   off += up(items * kHpg * kHeadDim * sizeof(uint16_t));
+  L->part_lse = off; off += up(items * kHpg * sizeof(float));
+  L->total = off;
+  return true;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+msa_status finish() { return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+size_t msa_prefill_workspace_bytes(const msa_params* p, int32_t batch, int64_t seq_len) {
+  Shape s;
+  PrefillLayout L;
+  if (batch <= 0 || check_params(p, &s) != MSA_OK || !prefill_layout(s, seq_len, &L)) return 0;
+  return L.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Records a HIP event at every stage boundary when profiling (ev != nullptr).
+struct StageClock {
+  std::vector<hipEvent_t>* ev;
+  hipStream_t st;
+  void mark() {
+    if (!ev) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) == hipSuccess) {
+      (void)hipEventRecord(e, st);
+      ev->push_back(e);
+    }
+  }
+};
+
+msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, const void* q, const void* k,
+                       const void* v, const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
+                       float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                       std::vector<hipEvent_t>* ev) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  if (batch <= 0 || seq_len <= 0) return MSA_ERR_INVALID_ARG;
+  if (seq_len > kMaxSeq) return MSA_ERR_UNSUPPORTED;
+  for (const void* ptr : {q, k, v, q_idx, k_idx, (const void*)out})
+    if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
+  if ((sel_out && !aligned(sel_out, 4)) || (lse_out && !aligned(lse_out, 4))) return MSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  PrefillLayout L;
+  if (!prefill_layout(s, seq_len, &L)) return MSA_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.total) return MSA_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  StageClock clk{ev, hs};
+  const int64_t N = seq_len;
+  const int G = s.G, Hq = s.Hq, K = s.k;
+  for (int32_t bi = 0; bi < batch; ++bi) {
+    const uint16_t* qs = static_cast<const uint16_t*>(q) + (int64_t)bi * N * Hq * kHeadDim;
+    const uint16_t* ks = static_cast<const uint16_t*>(k) + (int64_t)bi * N * G * kHeadDim;
+    const uint16_t* vs = static_cast<const uint16_t*>(v) + (int64_t)bi * N * G * kHeadDim;
+    const uint16_t* qis = static_cast<const uint16_t*>(q_idx) + (int64_t)bi * N * G * kIndexDim;
+    const uint16_t* kis = static_cast<const uint16_t*>(k_idx) + (int64_t)bi * N * kIndexDim;
+    uint16_t* os = static_cast<uint16_t*>(out) + (int64_t)bi * N * Hq * kHeadDim;
+    int32_t* sels = sel_out ? sel_out + (int64_t)bi * G * N * K : nullptr;
+    float* lses = lse_out ? lse_out + (int64_t)bi * N * Hq : nullptr;
+    for (int64_t w0 = 0; w0 < N; w0 += L.W) {
+      const int64_t Wn = std::min(L.W, N - w0);
+      const int nbw = (int)((w0 + Wn - 1) / kBlock + 1);
+      clk.mark();
+      // 1. index scores for query blocks that have more than k-1 older blocks
+      LaunchIndexPrefill ia{qis, kis, at<float>(workspace, L.sblk), N, w0,
+                            (int)std::max<int64_t>(K, w0 / kBlock), nbw, L.nb, G};
+      launch_index_prefill(ia, hs);
+      clk.mark();
+      // 2. top-k selection
+      int32_t* selw = sels ? sels + w0 * K : at<int32_t>(workspace, L.sel);
+      const int64_t gstride = sels ? N * K : L.W * K;
+      LaunchSelect sa{at<float>(workspace, L.sblk), L.nb, selw, gstride, K, Wn, G, K, w0, nullptr};
+      launch_select(sa, hs);
+      clk.mark();
+      // 3. reverse index and tile schedule
+      const int64_t e_w = entries_in(w0, w0 + Wn, G, K);
+      const int64_t tile_cap = cdiv(e_w, kTileQ) + (int64_t)G * nbw;
+      LaunchCsr ca{selw, gstride, K, w0, (int)Wn, nbw, G,
+                   at<int32_t>(workspace, L.chunkcnt), at<int32_t>(workspace, L.chunkoff),
+                   at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
+                   at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
+                   at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap};
+      launch_csr_and_tiles(ca, hs);
+      clk.mark();
+      // 4. persistent KV-outer attention
+      LaunchAttnPrefill aa{qs, ks, vs, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
+                           at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
+                           at<float>(workspace, L.part_lse), N, w0, G, nbw, K, s.scale_log2,
+                           (int)std::min<int64_t>(2 * cu_count(), tile_cap)};
+      launch_attn_prefill(aa, hs);
+      clk.mark();
+      // 5. combine
+      LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse),
+                       os + w0 * Hq * kHeadDim, lses ? lses + w0 * Hq : nullptr, Wn, G, K, w0, nullptr};
+      launch_combine(cb, hs);
+      clk.mark();
+    }
+  }
+  return finish();
+}
+
+// Sums the stage durations of a profiled call (marks come in groups of
+// nstage + 1 per window) into stage_ms after synchronising on the last mark.
+msa_status collect(std::vector<hipEvent_t>& ev, int nstage, float* stage_ms, msa_status st) {
+  for (int i = 0; i < nstage; ++i) stage_ms[i] = 0.f;
+  if (st == MSA_OK && !ev.empty()) {
+    if (hipEventSynchronize(ev.back()) != hipSuccess) st = MSA_ERR_HIP;
+    const size_t per = (size_t)nstage + 1;
+    for (size_t w = 0; st == MSA_OK && w + per <= ev.size(); w += per) {
+      for (int i = 0; i < nstage; ++i) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev[w + i], ev[w + i + 1]) != hipSuccess) st = MSA_ERR_HIP;
+        stage_ms[i] += ms;
+      }
+    }
+  }
+  for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_prefill(const msa_params* p, int32_t batch, int64_t seq_len, const void* q, const void* k,
+                       const void* v, const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
+                       float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_prefill(p, batch, seq_len, q, k, v, q_idx, k_idx, out, sel_out, lse_out, workspace, workspace_bytes,
+                     stream, nullptr);
+}
+
+msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len, const void* q,
+                                const void* k, const void* v, const void* q_idx, const void* k_idx, void* out,
+                                int32_t* sel_out, float* lse_out, void* workspace, size_t workspace_bytes,
+                                void* stream, float* stage_ms) {
+  if (!stage_ms) return MSA_ERR_INVALID_ARG;
+  std::vector<hipEvent_t> ev;
+  msa_status st = run_prefill(p, batch, seq_len, q, k, v, q_idx, k_idx, out, sel_out, lse_out, workspace,
+                              workspace_bytes, stream, &ev);
+  return collect(ev, 5, stage_ms, st);
+}
+
+size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx) {
+  Shape s;
+  DecodeLayout L;
+  if (check_params(p, &s) != MSA_OK || !decode_layout(s, batch, max_ctx, &L)) return 0;
+  return L.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const void* q, const void* q_idx,
+                      const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                      const int32_t* ctx_lens, void* out, int32_t* sel_out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream, std::vector<hipEvent_t>* ev) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  if (batch <= 0 || max_ctx <= 0 || max_ctx > (int64_t)INT32_MAX) return MSA_ERR_INVALID_ARG;
+  for (const void* ptr : {q, q_idx, k_cache, v_cache, k_idx_cache, (const void*)out})
+    if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
+  if (!ctx_lens || !aligned(ctx_lens, 4)) return MSA_ERR_INVALID_ARG;
+  if ((sel_out && !aligned(sel_out, 4)) || (lse_out && !aligned(lse_out, 4))) return MSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  DecodeLayout L;
+  if (!decode_layout(s, batch, max_ctx, &L)) return MSA_ERR_INVALID_ARG;
+  if (workspace_bytes < L.total) return MSA_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  StageClock clk{ev, hs};
+  clk.mark();
+  int32_t* sel = sel_out ? sel_out : at<int32_t>(workspace, L.sel);
+  LaunchIndexDecode ia{static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx_cache), ctx_lens,
+                       at<float>(workspace, L.sblk), max_ctx, L.nb, batch, s.G, s.k};
+  launch_index_decode(ia, hs);
+  clk.mark();
+  LaunchSelect sa{at<float>(workspace, L.sblk), L.nb, sel, s.k, (int64_t)s.G * s.k, batch, s.G, s.k, 0, ctx_lens};
+  launch_select(sa, hs);
+  clk.mark();
+  LaunchAttnDecode aa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                      static_cast<const uint16_t*>(v_cache), ctx_lens, sel, at<uint16_t>(workspace, L.part_o),
+                      at<float>(workspace, L.part_lse), max_ctx, batch, s.G, s.k, s.scale_log2};
+  launch_attn_decode(aa, hs);
+  clk.mark();
+  LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse),
+                   static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, 0, ctx_lens};
+  launch_combine(cb, hs);
+  clk.mark();
+  return finish();
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const void* q, const void* q_idx,
+                      const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                      const int32_t* ctx_lens, void* out, int32_t* sel_out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return run_decode(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out, lse_out,
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_ctx, const void* q,
+                               const void* q_idx, const void* k_cache, const void* v_cache,
+                               const void* k_idx_cache, const int32_t* ctx_lens, void* out, int32_t* sel_out,
+                               float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                               float* stage_ms) {
+  if (!stage_ms) return MSA_ERR_INVALID_ARG;
+  std::vector<hipEvent_t> ev;
+  msa_status st = run_decode(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out,
+                             lse_out, workspace, workspace_bytes, stream, &ev);
+  return collect(ev, 4, stage_ms, st);
+}
+
+msa_status msa_index_scores(const msa_params* p, int64_t seq_len, const void* q_idx, const void* k_idx,
+                            float* scores, void* stream) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  if (seq_len <= 0) return MSA_ERR_INVALID_ARG;
+  if (seq_len > kMaxSeq) return MSA_ERR_UNSUPPORTED;
+  if (!q_idx || !k_idx || !scores || !aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 4))
+    return MSA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const int nb = (int)cdiv(seq_len, kBlock);
+  LaunchIndexPrefill ia{static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), scores, seq_len,
+                        0, s.k, nb, nb, s.G};
+  launch_index_prefill(ia, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+msa_status msa_select_blocks(const msa_params* p, int64_t seq_len, const float* scores, int32_t* sel_out,
+                             void* stream) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  if (seq_len <= 0) return MSA_ERR_INVALID_ARG;
+  if (!scores || !sel_out || !aligned(scores, 4) || !aligned(sel_out, 4)) return MSA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const int nb = (int)cdiv(seq_len, kBlock);
+  LaunchSelect sa{scores, nb, sel_out, seq_len * s.k, s.k, seq_len, s.G, s.k, 0, nullptr};
+  launch_select(sa, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+}  // extern "C"

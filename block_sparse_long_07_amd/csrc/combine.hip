@@ -1,0 +1,56 @@
+// Second phase of the two-phase combine [pnsm, section 7]: merge the <= k
+// softmax partials of every (query, head) without atomics.
+//
+// Slot u of row rr and group g carries o_u (normalised, bf16) and
+// lse2_u = m_u + log2(l_u). With M = max_u lse2_u and w_u = 2^(lse2_u - M):
+//   out = sum_u w_u o_u / sum_u w_u,    lse = (M + log2 sum_u w_u) * ln 2.
+// The number of valid slots is min(k, b_loc + 1), the size of the selection.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// One workgroup per (row rr, group g); thread t: head t/16, dims 8*(t%16)..+7.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o,
+                                                 const float* __restrict__ part_lse, uint16_t* __restrict__ out,
+                                                 float* __restrict__ lse_out, int G, int topk, int64_t row0,
+                                                 const int32_t* __restrict__ ctx_lens) {
+  const int64_t rg = blockIdx.x;
+  const int64_t rr = rg / G;
+  const int g = (int)(rg % G);
+  const int t = threadIdx.x, h = t >> 4, d0 = (t & 15) * 8;
+  const int b_loc = ctx_lens ? (ctx_lens[rr] - 1) / kBlock : (int)((row0 + rr) / kBlock);
+  const int nsel = min(topk, b_loc + 1);
+  const int64_t slot0 = rg * topk;
+  float M = -__builtin_inff();
+  for (int u = 0; u < nsel; ++u) M = fmaxf(M, part_lse[(slot0 + u) * kHpg + h]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int u = 0; u < nsel; ++u) {
+    const float w = __builtin_amdgcn_exp2f(part_lse[(slot0 + u) * kHpg + h] - M);
+    wsum += w;
+    const u32x4 o = ld16(part_o + ((slot0 + u) * kHpg + h) * kHeadDim + d0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += w * bf2f(o[e] & 0xffffu);
+      acc[2 * e + 1] += w * bf2f(o[e] >> 16);
+    }
+  }
+  const float inv = 1.0f / wsum;
+  const int Hq = G * kHpg;
+  u32x4 res;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) res[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + (rr * Hq + g * kHpg + h) * kHeadDim + d0) = res;
+  if (lse_out && (t & 15) == 0)
+    lse_out[rr * Hq + g * kHpg + h] = (M + __builtin_amdgcn_logf(wsum)) * 0.69314718055994530942f;
+}
+
+void launch_combine(const LaunchCombine& a, hipStream_t st) {
+  const int64_t n = a.nrows * a.G;
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)n), dim3(256), 0, st, a.part_o, a.part_lse, a.out, a.lse_out, a.G,
+                     a.topk, a.row0, a.ctx_lens);
+}
+
+}  // namespace msa

@@ -1,0 +1,183 @@
+// Index Branch scoring with block max-pooling on gfx950 MFMA.
+//
+// For a query row i of group g and an older key block b, the pooled score is
+//   S[i, g, b] = max over the B_k keys j of block b of q_idx[i, g, :] . k_idx[j, :]
+// (raw dot products, no scale and no exponential: ranking raw scores selects the
+// same blocks as ranking their softmax [pnsm, section 7; yhxrc, 二], and block
+// scores are max-pooled [yifor, 設計核心]). The local block is always selected,
+// so it is never scored: with query tiles aligned to B_k the causal mask is the
+// loop bound b < b_loc and no per-token mask is needed.
+//
+// Contraction on MFMA: S^T tile (16 keys x 16 rows) = K (16 x 32 dims) * Q^T
+// (32 dims x 16 rows), two steps over d_idx = 64. Each lane then holds four keys
+// of one row, so the pooling max is three in-lane maxima per tile plus two
+// cross-lane steps per block.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+// One workgroup (4 waves) per (query block qb, chunk of kKC key blocks); it
+// covers the 128*G index rows (i, g) of the query block, 32*G per wave.
+constexpr int kKC = 8;
+
+template <int G>
+__global__ __launch_bounds__(256) void k_index_prefill(const uint16_t* __restrict__ q_idx,
+                                                       const uint16_t* __restrict__ k_idx,
+                                                       float* __restrict__ sblk, int64_t n_tokens,
+                                                       int64_t row0, int qb_begin, int nb) {
+  constexpr int RT = 2 * G;  // 16-row tiles per wave
+  const int qb = qb_begin + (int)blockIdx.y;
+  const int kb0 = (int)blockIdx.x * kKC;
+  if (kb0 >= qb) return;
+  const int kb1 = min(kb0 + kKC, qb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, qd = lane >> 4;
+
+  // flat index row (i*G + g) of this wave's first row
+  const int64_t flat0 = (int64_t)qb * kBlock * G + (int64_t)wave * 32 * G;
+  const int64_t flat_end = n_tokens * G;
+
+  bf16x8 qop[RT][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t row = flat0 + rt * 16 + c;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < flat_end) v = ld16(q_idx + row * kIndexDim + 32 * s + 8 * qd);
+      qop[rt][s] = as_bf16x8(v);
+    }
+  }
+
+  for (int kb = kb0; kb < kb1; ++kb) {
+    float mx[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) mx[rt] = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint16_t* krow = k_idx + ((int64_t)kb * kBlock + 16 * t + c) * kIndexDim + 8 * qd;
+      const bf16x8 a0 = as_bf16x8(ld16(krow));
+      const bf16x8 a1 = as_bf16x8(ld16(krow + 32));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16x16x32(a0, qop[rt][0], acc);
+        acc = mfma16x16x32(a1, qop[rt][1], acc);
+        mx[rt] = fmaxf(mx[rt], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      mx[rt] = fmaxf(mx[rt], shfl_xor_f(mx[rt], 16));
+      mx[rt] = fmaxf(mx[rt], shfl_xor_f(mx[rt], 32));
+    }
+    // all four lane groups now hold the block maxima; group qd stores tiles rt = qd mod 4
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int64_t row = flat0 + rt * 16 + c;
+      if ((rt & 3) == qd && row < flat_end) sblk[(row - row0 * G) * nb + kb] = mx[rt];
+    }
+  }
+}
+
+// Decode: one row per (sequence, group); one workgroup per (sequence, chunk of
+// kDecKB key blocks), each wave scoring whole key blocks. The shared index key
+// cache is streamed once with non-temporal loads; lanes c < G of the MFMA
+// column dimension carry the G index query heads.
+constexpr int kDecKB = 16;
+
+template <int G>
+__global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict__ q_idx,
+                                                      const uint16_t* __restrict__ k_idx,
+                                                      const int32_t* __restrict__ ctx_lens,
+                                                      float* __restrict__ sblk, int64_t max_ctx,
+                                                      int nb, int topk) {
+  const int sq = (int)blockIdx.y;
+  const int L = ctx_lens[sq];
+  const int b_loc = (L - 1) / kBlock;
+  if (b_loc < topk) return;  // every older block is selected; no scores needed
+  const int kb0 = (int)blockIdx.x * kDecKB;
+  if (kb0 >= b_loc) return;
+  const int kb1 = min(kb0 + kDecKB, b_loc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, qd = lane >> 4;
+
+  bf16x8 qop[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < G) v = ld16(q_idx + ((int64_t)sq * G + c) * kIndexDim + 32 * s + 8 * qd);
+    qop[s] = as_bf16x8(v);
+  }
+  const uint16_t* kbase = k_idx + (int64_t)sq * max_ctx * kIndexDim;
+
+  for (int kb = kb0 + wave; kb < kb1; kb += 4) {
+    u32x4 a[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint16_t* krow = kbase + ((int64_t)kb * kBlock + 16 * t + c) * kIndexDim + 8 * qd;
+      a[t][0] = ld16_nt(krow);
+      a[t][1] = ld16_nt(krow + 32);
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16x16x32(as_bf16x8(a[t][0]), qop[0], acc);
+      acc = mfma16x16x32(as_bf16x8(a[t][1]), qop[1], acc);
+      mx = fmaxf(mx, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    if (qd == 0 && c < G) sblk[((int64_t)sq * G + c) * nb + kb] = mx;
+  }
+}
+
+template <int G>
+static void launch_prefill_g(const LaunchIndexPrefill& a, hipStream_t st) {
+  const int n_qb = a.qb_end - a.qb_begin;
+  if (n_qb <= 0) return;
+  const int chunks = (a.qb_end - 1 + kKC - 1) / kKC;
+  dim3 grid(chunks, n_qb);
+  hipLaunchKernelGGL(k_index_prefill<G>, grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.sblk, a.n_tokens,
+                     a.row0, a.qb_begin, a.nb);
+}
+
+void launch_index_prefill(const LaunchIndexPrefill& a, hipStream_t st) {
+  switch (a.G) {
+    case 1: launch_prefill_g<1>(a, st); break;
+    case 2: launch_prefill_g<2>(a, st); break;
+    case 3: launch_prefill_g<3>(a, st); break;
+    case 4: launch_prefill_g<4>(a, st); break;
+    case 5: launch_prefill_g<5>(a, st); break;
+    case 6: launch_prefill_g<6>(a, st); break;
+    case 7: launch_prefill_g<7>(a, st); break;
+    case 8: launch_prefill_g<8>(a, st); break;
+    default: break;
+  }
+}
+
+template <int G>
+static void launch_decode_g(const LaunchIndexDecode& a, hipStream_t st) {
+  const int chunks = (a.nb + kDecKB - 1) / kDecKB;
+  dim3 grid(chunks, a.batch);
+  hipLaunchKernelGGL(k_index_decode<G>, grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.ctx_lens, a.sblk,
+                     a.max_ctx, a.nb, a.topk);
+}
+
+void launch_index_decode(const LaunchIndexDecode& a, hipStream_t st) {
+  switch (a.G) {
+    case 1: launch_decode_g<1>(a, st); break;
+    case 2: launch_decode_g<2>(a, st); break;
+    case 3: launch_decode_g<3>(a, st); break;
+    case 4: launch_decode_g<4>(a, st); break;
+    case 5: launch_decode_g<5>(a, st); break;
+    case 6: launch_decode_g<6>(a, st); break;
+    case 7: launch_decode_g<7>(a, st); break;
+    case 8: launch_decode_g<8>(a, st); break;
+    default: break;
+  }
+}
+
+}  // namespace msa

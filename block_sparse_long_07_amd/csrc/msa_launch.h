@@ -1,0 +1,115 @@
+// Host-side launch descriptors of the MSA kernels (internal to libmsa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kHeadDim = 128;  // d
+constexpr int kIndexDim = 64;  // d_idx
+constexpr int kBlock = 128;    // B_k
+constexpr int kHpg = 16;       // query heads per GQA group
+constexpr int kMaxTopk = 16;
+
+struct LaunchIndexPrefill {
+  const uint16_t* q_idx;  // [n_tokens, G, 64] of one sequence
+  const uint16_t* k_idx;  // [n_tokens, 64]
+  float* sblk;            // rows (i - row0)*G + g, row stride nb
+  int64_t n_tokens;
+  int64_t row0;           // first row of the window (multiple of 128)
+  int qb_begin, qb_end;   // query blocks scored: [qb_begin, qb_end)
+  int nb;                 // row stride of sblk
+  int G;
+};
+void launch_index_prefill(const LaunchIndexPrefill& a, hipStream_t st);
+
+struct LaunchIndexDecode {
+  const uint16_t* q_idx;  // [batch, G, 64]
+  const uint16_t* k_idx;  // [batch, max_ctx, 64]
+  const int32_t* ctx_lens;
+  float* sblk;            // [(s*G + g)*nb + b]
+  int64_t max_ctx;
+  int nb, batch, G, topk;
+};
+void launch_index_decode(const LaunchIndexDecode& a, hipStream_t st);
+
+// Selection over rows r = rr*G + g of sblk (row stride nb). b_loc of row rr is
+// (row0 + rr)/128 (prefill) or (ctx_lens[rr] - 1)/128 (decode, ctx_lens != null).
+struct LaunchSelect {
+  const float* sblk;
+  int nb;
+  int32_t* sel;           // sel[g*sel_gstride + rr*sel_rstride + u]
+  int64_t sel_gstride, sel_rstride;
+  int64_t nrows;          // rr count
+  int G, topk;
+  int64_t row0;
+  const int32_t* ctx_lens;
+};
+void launch_select(const LaunchSelect& a, hipStream_t st);
+
+// Reverse index (CSR) of one window's selections: for each (g, b) the entries
+// (i_rel << 4 | u) of the queries that selected b, ascending in i.
+struct LaunchCsr {
+  const int32_t* sel;     // sel[g*sel_gstride + i_rel*topk + u]
+  int64_t sel_gstride;
+  int topk;
+  int64_t row0;           // absolute first row of the window
+  int nrows;              // window rows
+  int nbw;                // blocks visible to the window: (row0 + nrows - 1)/128 + 1
+  int G;
+  int32_t* chunkcnt;      // [G*nbw*nch]
+  int32_t* chunkoff;      // [G*nbw*nch + 1]
+  int32_t* bsum;          // scan scratch
+  int32_t* entries;
+  int32_t* tile_start;    // [G*nbw + 1]
+  int32_t* tiles;         // [T_cap][4] = (list, begin, len, 0)
+  int32_t* tile_info;     // [0] tiles, [1] queue counter
+  int tile_q;             // queries per tile
+  int64_t tile_cap;
+};
+void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st);
+
+struct LaunchAttnPrefill {
+  const uint16_t* q;      // [n_tokens, Hq, 128]
+  const uint16_t* k;      // [n_tokens, G, 128]
+  const uint16_t* v;
+  const int32_t* entries;
+  const int32_t* tiles;
+  int32_t* tile_info;
+  uint16_t* part_o;       // [slot][16][128] bf16, slot = (i_rel*G + g)*topk + u
+  float* part_lse;        // [slot][16], log2 domain
+  int64_t n_tokens, row0;
+  int G, nbw, topk;
+  float scale_log2;
+  int grid;               // persistent workgroups
+};
+void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st);
+
+struct LaunchAttnDecode {
+  const uint16_t* q;      // [batch, Hq, 128]
+  const uint16_t* k;      // [batch, max_ctx, G, 128]
+  const uint16_t* v;
+  const int32_t* ctx_lens;
+  const int32_t* sel;     // [(s*G + g)*topk + u]
+  uint16_t* part_o;
+  float* part_lse;
+  int64_t max_ctx;
+  int batch, G, topk;
+  float scale_log2;
+};
+void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st);
+
+struct LaunchCombine {
+  const uint16_t* part_o;
+  const float* part_lse;
+  uint16_t* out;          // row rr at out + rr*Hq*128
+  float* lse_out;         // optional, row rr at lse_out + rr*Hq
+  int64_t nrows;
+  int G, topk;
+  int64_t row0;
+  const int32_t* ctx_lens;
+};
+void launch_combine(const LaunchCombine& a, hipStream_t st);
+
+}  // namespace msa

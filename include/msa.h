@@ -1,0 +1,167 @@
+/*
+ * msa.h - C ABI of the MI355X (gfx950) MiniMax Sparse Attention hot path.
+ *
+ * MSA replaces dense causal attention with two branches [yifor, 設計核心;
+ * yhxrc, 二 "MSA是怎么做的"; pnsm, section 2]:
+ *   Index Branch - for every query token i and GQA group g, raw (exp-free)
+ *     scores q_idx[i,g] . k_idx[j] over earlier keys, max-pooled per block of
+ *     B_k keys; the query's own block floor(i/B_k) is always selected and the
+ *     other k-1 blocks are the best-scoring older blocks (ties: lower index).
+ *   Main Branch - exact softmax attention of the group's query heads over the
+ *     tokens j <= i of the selected blocks only.
+ * The prefill main branch is organised KV-outer ("outer gather Q") [pnsm,
+ * section 7; yhxrc, 二; yololab, "KV Outer Gather Q是什麼？"]: each selected
+ * (group, KV block) is staged once and every query that selected it is
+ * computed against it, producing softmax partials that a second pass merges
+ * without atomics ("two-phase combine", [pnsm, section 7]).
+ *
+ * Page keys used in citations:
+ *   [pnsm]    "MiniMax Sparse Attention：一篇读懂百万上下文时代的稀疏注意力工程化路线" (pnsm.cn)
+ *   [yifor]   "MiniMax Sparse Attention (MSA): a Two-Branch Block-Sparse Attention Trained
+ *             on a 109B-Parameter MoE With a 3T-Token Budget" (yifor-blog)
+ *   [yhxrc]   MSA/NSA/DSA/MoBA comparison article (yhxrc.cn)
+ *   [yololab] MiniMax M3 / MSA overview (yololab.net)
+ *
+ * Conventions for every entry point:
+ *   - All tensors are device pointers to contiguous row-major memory, 16-byte
+ *     aligned; bf16 means IEEE bfloat16 stored as uint16.
+ *   - The caller owns every buffer (inputs, outputs, workspace). The library
+ *     never allocates, frees or synchronises; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and the call returns at once.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error status nothing has been launched. MSA_ERR_HIP reports a failed
+ *     launch (hipGetLastError); asynchronous device faults surface at the
+ *     caller's next synchronisation.
+ *   - Calls are reentrant; concurrent calls need distinct workspaces.
+ *   - Supported shapes: head_dim 128, index_dim 64, block_size 128,
+ *     num_q_heads / num_kv_heads == 16, 1 <= num_kv_heads <= 8, 1 <= topk <= 16.
+ *     Anything else returns MSA_ERR_UNSUPPORTED.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1,        /* null/misaligned pointer, non-positive size, Hq % Hkv != 0 */
+  MSA_ERR_UNSUPPORTED = -2,        /* a shape outside the supported set above */
+  MSA_ERR_WORKSPACE_TOO_SMALL = -3,
+  MSA_ERR_HIP = -4
+} msa_status;
+
+typedef struct {
+  int32_t num_q_heads;   /* Hq: query heads (64 in the pages' model, section 8 of [pnsm]) */
+  int32_t num_kv_heads;  /* G: KV heads = GQA groups = index query heads (4) */
+  int32_t head_dim;      /* d = 128 */
+  int32_t index_dim;     /* d_idx = 64: width of q_idx / k_idx */
+  int32_t block_size;    /* B_k = 128 keys per selectable block [pnsm, section 2] */
+  int32_t topk;          /* k blocks per (query, group), the forced local block included (16) */
+  float softmax_scale;   /* main-branch logit scale; <= 0 selects 1/sqrt(head_dim) */
+} msa_params;
+
+/* Bytes of device workspace msa_prefill needs for `batch` sequences of
+ * `seq_len` tokens (the same for any batch: sequences are processed in turn).
+ * Returns 0 for invalid or unsupported arguments. */
+size_t msa_prefill_workspace_bytes(const msa_params* p, int32_t batch, int64_t seq_len);
+
+/* Causal MSA prefill of `batch` independent sequences of `seq_len` tokens.
+ *   q      bf16 [batch, seq_len, Hq, d]       query heads; head h belongs to group h / 16
+ *   k, v   bf16 [batch, seq_len, G, d]        main-branch keys / values
+ *   q_idx  bf16 [batch, seq_len, G, d_idx]    one index query head per group
+ *   k_idx  bf16 [batch, seq_len, d_idx]       the shared index key head
+ *   out    bf16 [batch, seq_len, Hq, d]       attention output (fp32 accumulation,
+ *                                              rounded to nearest even)
+ *   sel_out  optional int32 [batch, G, seq_len, topk]: selected block ids per
+ *            (group, query), ascending, padded with -1 (NULL: not written)
+ *   lse_out  optional fp32 [batch, seq_len, Hq]: natural-log sum of exp of the
+ *            scaled logits over the attended tokens (NULL: not written)
+ *   workspace  >= msa_prefill_workspace_bytes(p, batch, seq_len) bytes
+ * Block selection is exact for index projections whose dot products are exact
+ * in fp32 (e.g. small integers); ties go to the lower block index. */
+msa_status msa_prefill(const msa_params* p, int32_t batch, int64_t seq_len,
+                       const void* q, const void* k, const void* v,
+                       const void* q_idx, const void* k_idx,
+                       void* out, int32_t* sel_out, float* lse_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace msa_decode needs. Returns 0 on invalid arguments. */
+size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx);
+
+/* One decode step for `batch` sequences. Decode is prefill's last row: the new
+ * token's K, V and k_idx must already be appended to the caches at row
+ * ctx_lens[b]-1, and its query attends causally to rows 0..ctx_lens[b]-1
+ * [yhxrc, 二: the index re-scores and re-selects blocks for every new token].
+ *   q            bf16 [batch, Hq, d]           the new token's query heads
+ *   q_idx        bf16 [batch, G, d_idx]        the new token's index query heads
+ *   k_cache, v_cache  bf16 [batch, max_ctx, G, d]
+ *   k_idx_cache  bf16 [batch, max_ctx, d_idx]
+ *   ctx_lens     device int32 [batch], 1 <= ctx_lens[b] <= max_ctx (device values
+ *                are not checked on the host; out-of-range values are undefined)
+ *   out          bf16 [batch, Hq, d]
+ *   sel_out      optional int32 [batch, G, topk] (ascending, -1 padded)
+ *   lse_out      optional fp32 [batch, Hq] */
+msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx,
+                      const void* q, const void* q_idx,
+                      const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                      const int32_t* ctx_lens,
+                      void* out, int32_t* sel_out, float* lse_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Profiling variants -------------------------------------------------
+ * Same work and arguments as msa_prefill / msa_decode, plus HIP events recorded
+ * on `stream` at every stage boundary. They synchronise on the last event and
+ * return in stage_ms the duration of each stage, summed over sequences and
+ * windows:
+ *   prefill (5): index scores, top-k selection, reverse index + tile schedule,
+ *                KV-outer attention, combine
+ *   decode  (4): index scores, top-k selection, attention, combine
+ * stage_ms must not be NULL (MSA_ERR_INVALID_ARG). */
+msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len,
+                                const void* q, const void* k, const void* v,
+                                const void* q_idx, const void* k_idx,
+                                void* out, int32_t* sel_out, float* lse_out,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                float* stage_ms);
+msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_ctx,
+                               const void* q, const void* q_idx,
+                               const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                               const int32_t* ctx_lens,
+                               void* out, int32_t* sel_out, float* lse_out,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               float* stage_ms);
+
+/* ---- Stage entry points (Index Branch only) ------------------------------
+ * For callers that need the selection alone, and for per-stage parity tests. */
+
+/* Pooled index scores [yifor, 設計核心: max-pooling per block] of one sequence:
+ *   scores fp32 [seq_len, G, nb] with nb = ceil(seq_len / block_size).
+ * For every query row i whose own block b_loc = i / B_k is >= topk (rows that
+ * have more than k-1 older blocks to choose from), scores[i, g, b] for
+ * b < b_loc is max over keys j of block b of q_idx[i,g] . k_idx[j]. Every other
+ * entry is left untouched. No workspace. */
+msa_status msa_index_scores(const msa_params* p, int64_t seq_len,
+                            const void* q_idx, const void* k_idx,
+                            float* scores, void* stream);
+
+/* Top-k selection [pnsm, section 7: exp-free top-k; yhxrc, 二] from pooled
+ * scores laid out as msa_index_scores writes them:
+ *   sel_out int32 [G, seq_len, topk]: the block b_loc plus the topk-1 best older
+ *   blocks (ties: lower index), ascending, -1 padded. Rows with b_loc < topk
+ *   select every block 0..b_loc and never read `scores`. No workspace. */
+msa_status msa_select_blocks(const msa_params* p, int64_t seq_len,
+                             const float* scores, int32_t* sel_out, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* msa_status_string(msa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

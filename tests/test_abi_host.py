@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/msa.h declares, sizes workspaces, and rejects invalid
+arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_07_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "msa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(msa.LIB_PATH):
+        from block_sparse_long_07_amd import build
+        build.build()
+    return msa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(msa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "MSA_OK"), (-1, "MSA_ERR_INVALID_ARG"), (-2, "MSA_ERR_UNSUPPORTED"),
+                       (-3, "MSA_ERR_WORKSPACE_TOO_SMALL"), (-4, "MSA_ERR_HIP")]:
+        assert msa.status_string(code) == name
+
+
+def test_workspace_sizes(lib):
+    p = msa.params()
+    small = msa.prefill_workspace_bytes(p, 1, 2048)
+    big = msa.prefill_workspace_bytes(p, 1, 32768)
+    assert 0 < small < big
+    # windows bound the workspace: 1M tokens needs no more than 4x 128K
+    assert msa.prefill_workspace_bytes(p, 1, 1 << 20) < 4 * msa.prefill_workspace_bytes(p, 1, 131072)
+    assert msa.decode_workspace_bytes(p, 64, 131072) > 0
+    assert msa.prefill_workspace_bytes(p, 1, 0) == 0
+    assert msa.prefill_workspace_bytes(p, 1, (1 << 20) + 1) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, -2), ("index_dim", 32, -2), ("block_size", 64, -2), ("topk", 17, -2),
+    ("topk", 0, -1), ("num_kv_heads", 3, -1), ("num_q_heads", 32, -2), ("num_kv_heads", 0, -1),
+])
+def test_prefill_rejects_bad_params(lib, field, value, status):
+    p = msa.params()
+    setattr(p, field, value)
+    dummy = ctypes.c_void_p(4096)
+    st = lib.msa_prefill(ctypes.byref(p), 1, 256, dummy, dummy, dummy, dummy, dummy, dummy, None, None,
+                         dummy, 1 << 40, None)
+    assert st == status
+
+
+def test_prefill_rejects_bad_pointers_and_workspace(lib):
+    p = msa.params()
+    ok = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    need = lib.msa_prefill_workspace_bytes(ctypes.byref(p), 1, 256)
+    args = [ok] * 6
+    assert lib.msa_prefill(ctypes.byref(p), 1, 256, *args, None, None, ok, need - 1, None) == -3
+    assert lib.msa_prefill(ctypes.byref(p), 1, 256, *args, None, None, None, need, None) == -1
+    assert lib.msa_prefill(ctypes.byref(p), 1, 256, mis, *args[1:], None, None, ok, need, None) == -1
+    assert lib.msa_prefill(ctypes.byref(p), 1, 256, None, *args[1:], None, None, ok, need, None) == -1
+    assert lib.msa_prefill(ctypes.byref(p), 0, 256, *args, None, None, ok, need, None) == -1
+    assert lib.msa_prefill(ctypes.byref(p), 1, (1 << 20) + 1, *args, None, None, ok, need, None) == -2
+    assert lib.msa_prefill(None, 1, 256, *args, None, None, ok, need, None) == -1
+
+
+def test_decode_rejects_bad_args(lib):
+    p = msa.params()
+    ok = ctypes.c_void_p(1 << 20)
+    need = lib.msa_decode_workspace_bytes(ctypes.byref(p), 2, 4096)
+    args = [ok] * 5
+    assert lib.msa_decode(ctypes.byref(p), 2, 4096, *args, None, ok, None, None, ok, need, None) == -1
+    assert lib.msa_decode(ctypes.byref(p), 2, 4096, *args, ok, ok, None, None, ok, need - 1, None) == -3
+    assert lib.msa_decode(ctypes.byref(p), 0, 4096, *args, ok, ok, None, None, ok, need, None) == -1
+    p.topk = 20
+    assert lib.msa_decode(ctypes.byref(p), 2, 4096, *args, ok, ok, None, None, ok, need, None) == -2
+
+
+def test_stage_entry_points_reject_bad_args(lib):
+    p = msa.params()
+    ok = ctypes.c_void_p(1 << 20)
+    assert lib.msa_index_scores(ctypes.byref(p), 0, ok, ok, ok, None) == -1
+    assert lib.msa_index_scores(ctypes.byref(p), 256, None, ok, ok, None) == -1
+    assert lib.msa_select_blocks(ctypes.byref(p), 256, ok, None, None) == -1
+    p.block_size = 64
+    assert lib.msa_select_blocks(ctypes.byref(p), 256, ok, ok, None) == -2

@@ -1,0 +1,213 @@
+"""GPU parity of the HIP path (called through the C ABI) against the float64
+oracle on the same seeded inputs.
+
+Bar: block selection bit-exact (integer-valued index projections make every
+score exact in fp32); pooled scores exactly equal; outputs within max-abs 2e-2
+and relative L2 5e-3 (bf16 in/out, fp32 accumulation); lse within 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_07_amd as msa
+import msa_synth as syn
+from oracle import msa_oracle as mo
+from tests._parity import (compare_lse, compare_out, log, oracle_prefill, prefill_device_inputs, timed)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    msa.load()  # raises if the HIP library is missing: no fallback exists
+    yield
+    torch.cuda.empty_cache()
+
+
+def dims(G, topk):
+    return syn.Dims(num_q_heads=16 * G, num_kv_heads=G, head_dim=128, index_dim=64, block_size=128, topk=topk)
+
+
+def run_prefill(inp, topk, **kw):
+    q, k, v, qi, ki = prefill_device_inputs(inp)
+    out, sel, lse = msa.prefill(q, k, v, qi, ki, topk=topk, want_sel=True, want_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out[0], sel[0], lse[0]
+
+
+def check_prefill(inp, topk, rows, label):
+    log(f"case {label}: N={inp.n} G={inp.dims.num_kv_heads} k={topk} recipe={inp.recipe} rows={len(rows)}")
+    with timed("gpu"):
+        out, sel, lse = run_prefill(inp, topk)
+    with timed("oracle"):
+        ref = oracle_prefill(inp, rows, topk)
+    rows_t = torch.as_tensor(rows, device=sel.device)
+    got_sel = sel[:, rows_t].permute(1, 0, 2).cpu().numpy()   # [R, G, k]
+    mism = np.argwhere(got_sel != ref["sel"])
+    assert mism.size == 0, f"selection mismatch at {mism[:5].tolist()}"
+    compare_out(out[rows_t], ref["out"], f"{label} out")
+    compare_lse(lse[rows_t], ref["lse"], f"{label}")
+
+
+# ---------------------------------------------------------------------------
+
+def test_generator_cpu_equals_gpu():
+    inp = syn.PrefillInputs(4096, dims(4, 16), 7, "planted")
+    rows = [0, 1, 777, 4095]
+    for fn in (inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx):
+        assert torch.equal(fn(rows).cpu(), fn(rows, device="cuda").cpu())
+
+
+@pytest.mark.parametrize("G,n,recipe,topk", [(1, 2048, "tiny", 4), (4, 4096, "planted", 16), (2, 3000, "tiny", 3)])
+def test_index_scores_exact(G, n, recipe, topk):
+    inp = syn.PrefillInputs(n, dims(G, topk), 3, recipe)
+    qi = inp.q_idx(device="cuda").contiguous()
+    ki = inp.k_idx(device="cuda").contiguous()
+    sc = msa.index_scores(qi, ki, topk=topk)
+    torch.cuda.synchronize()
+    rows = [r for r in syn.stratified_rows(n, 256, 128, 3, topk) if r // 128 >= topk]
+    ref = oracle_prefill(inp, rows, topk, want_scores=True)
+    got = sc.cpu().numpy()
+    for r, i in enumerate(rows):
+        b_loc = i // 128
+        assert np.array_equal(got[i, :, :b_loc], ref["scores"][r]), f"row {i}"
+
+
+@pytest.mark.parametrize("topk", [1, 2, 4, 16])
+def test_select_exact_with_ties(topk):
+    n, G = 5000, 4
+    nb = (n + 127) // 128
+    g = torch.Generator().manual_seed(topk)
+    scores = torch.randint(-2, 3, (n, G, nb), generator=g).float()
+    sel = msa.select_blocks(scores.cuda().contiguous(), topk=topk)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    s = scores.numpy().astype(np.float64)
+    for i in range(0, n, 7):
+        b_loc = i // 128
+        for gg in range(G):
+            want = mo.select_blocks(s[i, gg, :b_loc], b_loc, topk)
+            assert got[gg, i].tolist() == want.tolist(), (i, gg)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prefill_tiny_all_rows(seed):
+    inp = syn.PrefillInputs(2048, dims(1, 4), seed, "tiny")
+    check_prefill(inp, 4, np.arange(2048), f"tiny seed{seed}")
+
+
+@pytest.mark.parametrize("n,G,topk,recipe", [
+    (1, 1, 4, "tiny"), (127, 1, 4, "tiny"), (128, 2, 4, "tiny"), (129, 1, 4, "tiny"),
+    (1000, 2, 4, "planted"), (2500, 4, 16, "planted"), (1920, 1, 1, "tiny"), (640, 2, 16, "tiny"),
+    (4321, 3, 7, "tiny"),
+])
+def test_prefill_edge_and_ragged(n, G, topk, recipe):
+    inp = syn.PrefillInputs(n, dims(G, topk), 5, recipe, n_planted=2)
+    check_prefill(inp, topk, np.arange(n), f"edge n{n}")
+
+
+def test_prefill_deterministic_and_poisoned_workspace():
+    inp = syn.PrefillInputs(4096, dims(2, 8), 9, "tiny")
+    q, k, v, qi, ki = prefill_device_inputs(inp)
+    p = msa.params(32, 2, topk=8)
+    nbytes = msa.prefill_workspace_bytes(p, 1, 4096)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws.view(torch.float32)[: nbytes // 4].fill_(float("nan"))
+    o1, s1, l1 = msa.prefill(q, k, v, qi, ki, topk=8, want_sel=True, want_lse=True, workspace=ws)
+    o1, s1, l1 = o1.clone(), s1.clone(), l1.clone()
+    ws.view(torch.int32)[: nbytes // 4].fill_(-12345)
+    o2, s2, l2 = msa.prefill(q, k, v, qi, ki, topk=8, want_sel=True, want_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    assert torch.isfinite(o1.float()).all()
+
+
+def test_prefill_batch_of_two():
+    a = syn.PrefillInputs(1500, dims(2, 4), 21, "tiny")
+    b = syn.PrefillInputs(1500, dims(2, 4), 22, "tiny")
+    ta, tb = prefill_device_inputs(a), prefill_device_inputs(b)
+    cat = [torch.cat([x, y]).contiguous() for x, y in zip(ta, tb)]
+    out, sel, lse = msa.prefill(*cat, topk=4, want_sel=True, want_lse=True)
+    torch.cuda.synchronize()
+    for bi, inp in enumerate((a, b)):
+        rows = np.arange(0, 1500, 3)
+        ref = oracle_prefill(inp, rows, 4)
+        rt = torch.as_tensor(rows, device="cuda")
+        assert np.array_equal(sel[bi][:, rt].permute(1, 0, 2).cpu().numpy(), ref["sel"])
+        compare_out(out[bi][rt], ref["out"], f"batch{bi}")
+
+
+# ---- decode ---------------------------------------------------------------
+
+class _RowsF64:
+    """Row-indexed float64 view of a device bf16 tensor (indexes on the device,
+    converts only the rows the oracle touches)."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, idx):
+        if isinstance(idx, tuple):
+            idx = tuple(torch.as_tensor(np.asarray(i), device=self.t.device) if not isinstance(i, (int, slice))
+                        else i for i in idx)
+        elif not isinstance(idx, (int, slice)):
+            idx = torch.as_tensor(np.asarray(idx), device=self.t.device)
+        return mo.to_f64(self.t[idx])
+
+
+def decode_case(B, max_ctx, ctx_lens, topk, seed, label):
+    G = 4
+    dec = syn.DecodeInputs(B, max_ctx, dims(G, topk), seed, ctx_lens=ctx_lens)
+    log(f"case {label}: B={B} max_ctx={max_ctx} k={topk}")
+    with timed("inputs"):
+        q = torch.stack([dec.q(b, "cuda") for b in range(B)]).contiguous()
+        qi = torch.stack([dec.q_idx(b, "cuda") for b in range(B)]).contiguous()
+        kc = torch.empty((B, max_ctx, G, 128), dtype=torch.bfloat16, device="cuda")
+        vc = torch.empty_like(kc)
+        kic = torch.empty((B, max_ctx, 64), dtype=torch.bfloat16, device="cuda")
+        for b in range(B):
+            kc[b] = dec.k_cache(b, device="cuda")
+            vc[b] = dec.v_cache(b, device="cuda")
+            kic[b] = dec.k_idx_cache(b, device="cuda")
+        lens = torch.tensor(dec.ctx_lens, dtype=torch.int32, device="cuda")
+    with timed("gpu"):
+        out, sel, lse = msa.decode(q, qi, kc, vc, kic, lens, topk=topk, want_sel=True, want_lse=True)
+        torch.cuda.synchronize()
+    with timed("oracle"):
+        for b in range(B):
+            L = dec.ctx_lens[b]
+            # q/q_idx of the new token regenerated on the CPU; caches read row-wise
+            ref = mo.decode_seq(mo.to_f64(dec.q(b)), mo.to_f64(dec.q_idx(b)), mo.to_f64(kic[b, :L]),
+                                _RowsF64(kc[b]), _RowsF64(vc[b]), L, block_size=128, topk=topk)
+            got_sel = sel[b].cpu().numpy()
+            assert np.array_equal(got_sel, ref["sel"]), f"seq {b}: {got_sel} vs {ref['sel']}"
+            compare_out(out[b], ref["out"], f"{label} seq{b}")
+            compare_lse(lse[b], ref["lse"], f"{label} seq{b}")
+
+
+def test_decode_ragged_small():
+    decode_case(7, 3000, [1, 128, 129, 1500, 2048, 2999, 3000], 16, 4, "decode ragged")
+
+
+def test_decode_topk4_short():
+    decode_case(3, 700, [700, 300, 5], 4, 8, "decode k4")
+
+
+@pytest.mark.timeout(900)
+def test_decode_128k_bench_config():
+    decode_case(64, 131072, None, 16, 0, "decode 64x128K")
+
+
+# ---- bench-size prefill (sampled rows) ---------------------------------------
+
+@pytest.mark.timeout(900)
+def test_prefill_32k_bench_config_sampled():
+    n, topk = 32768, 16
+    inp = syn.PrefillInputs(n, dims(4, topk), 0, "planted", n_planted=8)
+    extra = sorted({b for g in inp.planted.values() for b in g})
+    rows = syn.stratified_rows(n, 4096, 128, 0, topk, extra=extra)
+    check_prefill(inp, topk, rows, "prefill 32K")
