@@ -80,7 +80,9 @@ struct PrefillLayout {
   int64_t W;  // window rows
   int nb;     // blocks of the sequence
   int64_t nch, Lc, nblk, e_cap, tile_cap, slots;
-  size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, part_o, part_lse, total;
+  int64_t nunits;
+  size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, part_o, part_lse, dense_cnt,
+      dense_list, dense_o, dense_lse, total;
 };
 
 bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
@@ -106,6 +108,11 @@ bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
   L->tile_info = off;  off += up(4 * sizeof(int32_t));
   L->part_o = off;     off += up((size_t)L->slots * kHpg * kHeadDim * sizeof(uint16_t));
   L->part_lse = off;   off += up((size_t)L->slots * kHpg * sizeof(float));
+  L->nunits = cdiv(L->W, 16);
+  L->dense_cnt = off;  off += up((size_t)s.G * L->nunits * sizeof(int32_t));
+  L->dense_list = off; off += up((size_t)s.G * L->nunits * s.k * sizeof(int32_t));
+  L->dense_o = off;    off += up((size_t)L->W * s.G * kHpg * kHeadDim * sizeof(uint16_t));
+  L->dense_lse = off;  off += up((size_t)L->W * s.G * kHpg * sizeof(float));
   L->total = off;
   return true;
 }
@@ -224,14 +231,22 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
       // 3. reverse index and tile schedule
       const int64_t e_w = entries_in(w0, w0 + Wn, G, K);
       const int64_t tile_cap = cdiv(e_w, kTileQ) + (int64_t)G * nbw;
+      const int nunits = (int)cdiv(Wn, 16);
+      int32_t* dcnt = at<int32_t>(workspace, L.dense_cnt);
+      int32_t* dlist = at<int32_t>(workspace, L.dense_list);
       LaunchCsr ca{selw, gstride, K, w0, (int)Wn, nbw, G,
                    at<int32_t>(workspace, L.chunkcnt), at<int32_t>(workspace, L.chunkoff),
                    at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
                    at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
-                   at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap};
+                   at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist, nunits};
       launch_csr_and_tiles(ca, hs);
       clk.mark();
-      // 4. persistent KV-outer attention
+      // 4. attention: query-stationary over unit-shared blocks, then KV-outer
+      uint16_t* ow = os + w0 * Hq * kHeadDim;
+      float* lw = lses ? lses + w0 * Hq : nullptr;
+      LaunchAttnDense da{qs, ks, vs, dcnt, dlist, at<uint16_t>(workspace, L.dense_o),
+                         at<float>(workspace, L.dense_lse), ow, lw, N, w0, (int)Wn, nunits, G, K, s.scale_log2};
+      launch_attn_dense(da, hs);
       LaunchAttnPrefill aa{qs, ks, vs, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
                            at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
                            at<float>(workspace, L.part_lse), N, w0, G, nbw, K, s.scale_log2,
@@ -239,8 +254,9 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
       launch_attn_prefill(aa, hs);
       clk.mark();
       // 5. combine
-      LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse),
-                       os + w0 * Hq * kHeadDim, lses ? lses + w0 * Hq : nullptr, Wn, G, K, w0, nullptr};
+      LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse), selw, gstride, dcnt,
+                       dlist, at<uint16_t>(workspace, L.dense_o), at<float>(workspace, L.dense_lse), nunits,
+                       ow, lw, Wn, G, K, w0, nullptr};
       launch_combine(cb, hs);
       clk.mark();
     }
@@ -334,8 +350,9 @@ msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const
                       at<float>(workspace, L.part_lse), max_ctx, batch, s.G, s.k, s.scale_log2};
   launch_attn_decode(aa, hs);
   clk.mark();
-  LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse),
-                   static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, 0, ctx_lens};
+  LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse), nullptr, 0, nullptr,
+                   nullptr, nullptr, nullptr, 0, static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, 0,
+                   ctx_lens};
   launch_combine(cb, hs);
   clk.mark();
   return finish();

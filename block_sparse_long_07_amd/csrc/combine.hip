@@ -11,10 +11,18 @@
 namespace msa {
 
 // One workgroup per (row rr, group g); thread t: head t/16, dims 8*(t%16)..+7.
+// Prefill rows may carry one extra partial from the dense pass covering the
+// blocks shared by the row's whole 16-row unit; their slots are then skipped
+// (both lists are ascending, so one merge walk finds them). Rows whose every
+// selected block was shared were written by the dense pass and are skipped.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o,
                                                  const float* __restrict__ part_lse, uint16_t* __restrict__ out,
                                                  float* __restrict__ lse_out, int G, int topk, int64_t row0,
-                                                 const int32_t* __restrict__ ctx_lens) {
+                                                 const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ sel,
+                                                 int64_t sel_gstride, const int32_t* __restrict__ dense_cnt,
+                                                 const int32_t* __restrict__ dense_list,
+                                                 const uint16_t* __restrict__ dense_o,
+                                                 const float* __restrict__ dense_lse, int nunits) {
   const int64_t rg = blockIdx.x;
   const int64_t rr = rg / G;
   const int g = (int)(rg % G);
@@ -22,14 +30,52 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
   const int b_loc = ctx_lens ? (ctx_lens[rr] - 1) / kBlock : (int)((row0 + rr) / kBlock);
   const int nsel = min(topk, b_loc + 1);
   const int64_t slot0 = rg * topk;
+
+  // slots covered by the dense pass (bit u set), via a merge walk of two ascending lists
+  uint32_t skip = 0u;
+  int nd = 0;
+  const int32_t* dl = nullptr;
+  if (dense_cnt) {
+    const int unit = (int)(rr >> 4);
+    nd = dense_cnt[g * nunits + unit];
+    if (nd == nsel) return;  // written in full by the dense pass
+    dl = dense_list + ((int64_t)g * nunits + unit) * topk;
+    const int32_t* srow = sel + (int64_t)g * sel_gstride + rr * topk;
+    int j = 0;
+    for (int u = 0; u < nsel && j < nd; ++u) {
+      const int b = srow[u];
+      while (j < nd && dl[j] < b) ++j;
+      if (j < nd && dl[j] == b) {
+        skip |= 1u << u;
+        ++j;
+      }
+    }
+  }
   float M = -__builtin_inff();
-  for (int u = 0; u < nsel; ++u) M = fmaxf(M, part_lse[(slot0 + u) * kHpg + h]);
+  float dl2 = -__builtin_inff();
+  if (nd > 0) {
+    dl2 = __builtin_nontemporal_load(dense_lse + rg * kHpg + h);
+    M = dl2;
+  }
+  for (int u = 0; u < nsel; ++u)
+    if (!((skip >> u) & 1u)) M = fmaxf(M, __builtin_nontemporal_load(part_lse + (slot0 + u) * kHpg + h));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int u = 0; u < nsel; ++u) {
-    const float w = __builtin_amdgcn_exp2f(part_lse[(slot0 + u) * kHpg + h] - M);
+  if (nd > 0) {
+    const float w = __builtin_amdgcn_exp2f(dl2 - M);
     wsum += w;
-    const u32x4 o = ld16(part_o + ((slot0 + u) * kHpg + h) * kHeadDim + d0);
+    const u32x4 o = ld16_nt(dense_o + (rg * kHpg + h) * kHeadDim + d0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += w * bf2f(o[e] & 0xffffu);
+      acc[2 * e + 1] += w * bf2f(o[e] >> 16);
+    }
+  }
+  for (int u = 0; u < nsel; ++u) {
+    if ((skip >> u) & 1u) continue;
+    const float w = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(part_lse + (slot0 + u) * kHpg + h) - M);
+    wsum += w;
+    const u32x4 o = ld16_nt(part_o + ((slot0 + u) * kHpg + h) * kHeadDim + d0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] += w * bf2f(o[e] & 0xffffu);
@@ -50,7 +96,8 @@ void launch_combine(const LaunchCombine& a, hipStream_t st) {
   const int64_t n = a.nrows * a.G;
   if (n <= 0) return;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)n), dim3(256), 0, st, a.part_o, a.part_lse, a.out, a.lse_out, a.G,
-                     a.topk, a.row0, a.ctx_lens);
+                     a.topk, a.row0, a.ctx_lens, a.sel, a.sel_gstride, a.dense_cnt, a.dense_list, a.dense_o,
+                     a.dense_lse, a.nunits);
 }
 
 }  // namespace msa

@@ -21,6 +21,7 @@ namespace msa {
 
 constexpr int kChunk = 64;       // rows per chunk (one 64-bit mask word)
 constexpr int kScanTile = 4096;  // elements per scan workgroup (256 threads x 16)
+constexpr int kUnit = 16;        // rows per dense unit
 
 __device__ __forceinline__ void chunk_masks(const int32_t* __restrict__ sel, int64_t sel_gstride, int topk,
                                             int g, int i0, int nq, int bmax, unsigned long long* mask) {
@@ -34,9 +35,25 @@ __device__ __forceinline__ void chunk_masks(const int32_t* __restrict__ sel, int
   __syncthreads();
 }
 
+// Bits of `m` that belong to 16-row units of the chunk in which every valid row
+// selected the block: those (unit, block) pairs go to the dense pass.
+__device__ __forceinline__ unsigned long long dense_bits(unsigned long long m, int nq) {
+  unsigned long long d = 0ull;
+#pragma unroll
+  for (int s = 0; s < kChunk / kUnit; ++s) {
+    const int r0 = s * kUnit;
+    if (r0 >= nq) break;
+    const int n = min(kUnit, nq - r0);
+    const unsigned long long full = ((n == 64) ? ~0ull : ((1ull << n) - 1ull)) << r0;
+    if ((m & full) == full) d |= full;
+  }
+  return d;
+}
+
 __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ sel, int64_t sel_gstride,
                                                    int topk, int64_t row0, int nrows, int nbw, int nch,
-                                                   int32_t* __restrict__ chunkcnt) {
+                                                   int32_t* __restrict__ chunkcnt, int32_t* __restrict__ dense_cnt,
+                                                   int32_t* __restrict__ dense_list, int nunits) {
   extern __shared__ unsigned long long mask[];
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int i0 = chunk * kChunk;
@@ -44,8 +61,27 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
   const int bmax = (int)((row0 + i0 + nq - 1) / kBlock);
   chunk_masks(sel, sel_gstride, topk, g, i0, nq, bmax, mask);
   for (int b = threadIdx.x; b < nbw; b += blockDim.x) {
-    const int cnt = (b <= bmax) ? __popcll(mask[b]) : 0;
+    int cnt = 0;
+    if (b <= bmax) {
+      const unsigned long long m = mask[b];
+      cnt = __popcll(m & ~dense_bits(m, nq));
+    }
     chunkcnt[((int64_t)g * nbw + b) * nch + chunk] = cnt;
+  }
+  // dense list of each 16-row unit, in ascending block order: every shared block
+  // is among the first row's selections, which are ascending.
+  const int s = threadIdx.x;
+  if (s < kChunk / kUnit && s * kUnit < nq) {
+    const int unit = (i0 >> 4) + s;
+    const int32_t* row = sel + (int64_t)g * sel_gstride + (int64_t)(i0 + s * kUnit) * topk;
+    const int n = min(kUnit, nq - s * kUnit);
+    const unsigned long long full = ((1ull << n) - 1ull) << (s * kUnit);
+    int nd = 0;
+    for (int u = 0; u < topk; ++u) {
+      const int b = row[u];
+      if (b >= 0 && b <= bmax && (mask[b] & full) == full) dense_list[((int64_t)g * nunits + unit) * topk + nd++] = b;
+    }
+    dense_cnt[g * nunits + unit] = nd;
   }
 }
 
@@ -64,7 +100,9 @@ __global__ __launch_bounds__(256) void k_csr_scatter(const int32_t* __restrict__
     const int b = s[e];
     if (b < 0 || b > bmax) continue;
     const int ql = e / topk, u = e % topk;
-    const unsigned long long below = mask[b] & ((1ull << ql) - 1ull);
+    const unsigned long long m = mask[b] & ~dense_bits(mask[b], nq);
+    if (!((m >> ql) & 1ull)) continue;  // handled by the dense pass
+    const unsigned long long below = m & ((1ull << ql) - 1ull);
     const int64_t pos = chunkoff[((int64_t)g * nbw + b) * nch + chunk] + __popcll(below);
     entries[pos] = ((i0 + ql) << 4) | u;
   }
@@ -218,7 +256,7 @@ void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st) {
   const size_t lds = (size_t)a.nbw * sizeof(unsigned long long);
   dim3 grid(nch, a.G);
   hipLaunchKernelGGL(k_csr_count, grid, dim3(256), lds, st, a.sel, a.sel_gstride, a.topk, a.row0, a.nrows,
-                     a.nbw, nch, a.chunkcnt);
+                     a.nbw, nch, a.chunkcnt, a.dense_cnt, a.dense_list, a.nunits);
   const int64_t n = (int64_t)a.G * a.nbw * nch;
   const int nblk = (int)((n + kScanTile - 1) / kScanTile);
   hipLaunchKernelGGL(k_scan_reduce, dim3(nblk), dim3(256), 0, st, a.chunkcnt, n, a.bsum);

@@ -83,8 +83,8 @@ __global__ __launch_bounds__(256) void k_index_prefill(const uint16_t* __restric
 
 // Decode: one row per (sequence, group); one workgroup per (sequence, chunk of
 // kDecKB key blocks), each wave scoring whole key blocks. The shared index key
-// cache is streamed once with non-temporal loads; lanes c < G of the MFMA
-// column dimension carry the G index query heads.
+// cache is streamed once (the two half-row loads of a key row hit the same L2
+// line); lanes c < G of the MFMA column dimension carry the G index query heads.
 constexpr int kDecKB = 16;
 
 template <int G>
@@ -117,8 +117,8 @@ __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint16_t* krow = kbase + ((int64_t)kb * kBlock + 16 * t + c) * kIndexDim + 8 * qd;
-      a[t][0] = ld16_nt(krow);
-      a[t][1] = ld16_nt(krow + 32);
+      a[t][0] = ld16(krow);
+      a[t][1] = ld16(krow + 32);
     }
     float mx = -__builtin_inff();
 #pragma unroll

@@ -42,7 +42,14 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return u >> 16;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
 
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 

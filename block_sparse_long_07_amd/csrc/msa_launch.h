@@ -67,6 +67,9 @@ struct LaunchCsr {
   int32_t* tile_info;     // [0] tiles, [1] queue counter
   int tile_q;             // queries per tile
   int64_t tile_cap;
+  int32_t* dense_cnt;     // [G][nunits]: blocks shared by all queries of a 16-row unit
+  int32_t* dense_list;    // [G][nunits][topk], ascending
+  int nunits;             // ceil(nrows / 16)
 };
 void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st);
 
@@ -86,6 +89,22 @@ struct LaunchAttnPrefill {
 };
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st);
 
+struct LaunchAttnDense {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* dense_cnt;
+  const int32_t* dense_list;
+  uint16_t* dense_o;      // [(i_rel*G + g)][16][128] bf16
+  float* dense_lse;       // [(i_rel*G + g)][16]
+  uint16_t* out;          // window's first row
+  float* lse_out;         // optional, window's first row
+  int64_t n_tokens, row0;
+  int nrows, nunits, G, topk;
+  float scale_log2;
+};
+void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st);
+
 struct LaunchAttnDecode {
   const uint16_t* q;      // [batch, Hq, 128]
   const uint16_t* k;      // [batch, max_ctx, G, 128]
@@ -103,6 +122,14 @@ void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st);
 struct LaunchCombine {
   const uint16_t* part_o;
   const float* part_lse;
+  // prefill only (null for decode): the unit-shared blocks and their partial
+  const int32_t* sel;     // sel[g*sel_gstride + rr*topk + u]
+  int64_t sel_gstride;
+  const int32_t* dense_cnt;
+  const int32_t* dense_list;
+  const uint16_t* dense_o;
+  const float* dense_lse;
+  int nunits;
   uint16_t* out;          // row rr at out + rr*Hq*128
   float* lse_out;         // optional, row rr at lse_out + rr*Hq
   int64_t nrows;

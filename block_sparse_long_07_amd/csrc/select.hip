@@ -20,6 +20,8 @@
 
 namespace msa {
 
+constexpr int64_t kWaveRowsMax = 16384;
+
 template <int KM1>
 __global__ __launch_bounds__(64) void k_select(const float* __restrict__ sblk, int nb,
                                                int32_t* __restrict__ sel, int64_t sel_gstride,
@@ -107,14 +109,110 @@ __global__ __launch_bounds__(64) void k_select(const float* __restrict__ sblk, i
   out[KM1] = b_loc;
 }
 
+// Few rows with many candidates (decode): one wave per row. Lane l ranks the
+// candidates b = l, l+64, ... (ascending, so the same register insertion keeps
+// its k-1 best with ties to the lower index); the 64 lane lists are then merged
+// by k-1 rounds of a wave-wide arg-max over the list heads, each round popping
+// the winner's head.
+template <int KM1>
+__global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sblk, int nb,
+                                                    int32_t* __restrict__ sel, int64_t sel_gstride,
+                                                    int64_t sel_rstride, int G, int64_t row0,
+                                                    const int32_t* __restrict__ ctx_lens) {
+  const int lane = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int64_t rr = r / G;
+  const int g = (int)(r % G);
+  const int b_loc = ctx_lens ? (ctx_lens[rr] - 1) / kBlock : (int)((row0 + rr) / kBlock);
+  int32_t* out = sel + (int64_t)g * sel_gstride + rr * sel_rstride;
+  if (b_loc <= KM1) {
+    if (lane <= KM1) out[lane] = (lane <= b_loc) ? lane : -1;
+    return;
+  }
+  if constexpr (KM1 == 0) {
+    if (lane == 0) out[0] = b_loc;
+  } else {
+    float v[KM1];
+    int id[KM1];
+#pragma unroll
+    for (int t = 0; t < KM1; ++t) {
+      v[t] = -__builtin_inff();
+      id[t] = 0x7fffffff;
+    }
+    const float* row = sblk + r * (int64_t)nb;
+    for (int b = lane; b < b_loc; b += 64) {
+      float cv = row[b];
+      if (cv > v[KM1 - 1]) {
+        int ci = b;
+        bool shift = false;
+#pragma unroll
+        for (int t = 0; t < KM1; ++t) {
+          shift = shift || (cv > v[t]);
+          const float nv = shift ? cv : v[t];
+          const int ni = shift ? ci : id[t];
+          cv = shift ? v[t] : cv;
+          ci = shift ? id[t] : ci;
+          v[t] = nv;
+          id[t] = ni;
+        }
+      }
+    }
+    int chosen[KM1];
+#pragma unroll
+    for (int rd = 0; rd < KM1; ++rd) {
+      float bv = v[0];
+      int bi = id[0];
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float ov = __shfl_xor(bv, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        const bool take = ov > bv || (ov == bv && oi < bi);
+        bv = take ? ov : bv;
+        bi = take ? oi : bi;
+      }
+      chosen[rd] = bi;
+      if (id[0] == bi) {  // the winning lane pops its head
+#pragma unroll
+        for (int t = 0; t + 1 < KM1; ++t) {
+          v[t] = v[t + 1];
+          id[t] = id[t + 1];
+        }
+        v[KM1 - 1] = -__builtin_inff();
+        id[KM1 - 1] = 0x7fffffff;
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < KM1; ++a) {
+#pragma unroll
+      for (int t = 0; t + 1 < KM1 - a; ++t) {
+        const int lo = min(chosen[t], chosen[t + 1]);
+        const int hi = max(chosen[t], chosen[t + 1]);
+        chosen[t] = lo;
+        chosen[t + 1] = hi;
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < KM1; ++u) out[u] = chosen[u];
+      out[KM1] = b_loc;
+    }
+  }
+}
+
 void launch_select(const LaunchSelect& a, hipStream_t st) {
   const int64_t rows = a.nrows * a.G;
   if (rows <= 0) return;
-  dim3 grid((unsigned)((rows + 63) / 64));
+  // thread-per-row needs many rows to fill the GPU; below that, wave-per-row
+  const bool per_wave = rows <= kWaveRowsMax;
+  dim3 grid((unsigned)(per_wave ? rows : (rows + 63) / 64));
 #define MSA_SEL_CASE(K)                                                                                 \
   case K:                                                                                               \
-    hipLaunchKernelGGL(k_select<K - 1>, grid, dim3(64), 0, st, a.sblk, a.nb, a.sel, a.sel_gstride,      \
-                       a.sel_rstride, a.nrows, a.G, a.row0, a.ctx_lens);                                \
+    if (per_wave)                                                                                       \
+      hipLaunchKernelGGL(k_select_wave<K - 1>, grid, dim3(64), 0, st, a.sblk, a.nb, a.sel,              \
+                         a.sel_gstride, a.sel_rstride, a.G, a.row0, a.ctx_lens);                        \
+    else                                                                                                \
+      hipLaunchKernelGGL(k_select<K - 1>, grid, dim3(64), 0, st, a.sblk, a.nb, a.sel, a.sel_gstride,    \
+                         a.sel_rstride, a.nrows, a.G, a.row0, a.ctx_lens);                              \
     break;
   switch (a.topk) {
     MSA_SEL_CASE(1)

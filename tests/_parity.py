@@ -31,7 +31,7 @@ def prefill_device_inputs(inp: syn.PrefillInputs, device="cuda"):
     return q, k, v, qi, ki
 
 
-def oracle_prefill(inp: syn.PrefillInputs, rows, topk, want_scores=False, kv_host=None, threads=8):
+def oracle_prefill(inp: syn.PrefillInputs, rows, topk, want_scores=False, kv_host=None, threads=16):
     """Oracle on the given rows; inputs regenerated on the CPU from the seed
     (kv_host: optional pre-generated (k_idx, k, v) float64 arrays)."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -41,14 +41,30 @@ def oracle_prefill(inp: syn.PrefillInputs, rows, topk, want_scores=False, kv_hos
     q = mo.to_f64(inp.q(rows))
     qi = mo.to_f64(inp.q_idx(rows))
     bk = inp.dims.block_size
-    parts = np.array_split(np.arange(len(rows)), max(1, min(threads, len(rows) // 16)))
+    parts = np.array_split(np.arange(len(rows)), max(1, min(4 * threads, len(rows) // 16)))
+
+    done = [0]
+    t0 = time.time()
 
     def run(ix):
-        return mo.prefill_rows(rows[ix], q[ix], qi[ix], ki, k, v, block_size=bk, topk=topk,
-                               want_scores=want_scores)
+        r = mo.prefill_rows(rows[ix], q[ix], qi[ix], ki, k, v, block_size=bk, topk=topk,
+                            want_scores=want_scores)
+        done[0] += len(ix)
+        if len(rows) >= 1024:
+            log(f"    oracle rows {done[0]}/{len(rows)} ({time.time() - t0:.0f}s)")
+        return r
 
-    with ThreadPoolExecutor(len(parts)) as ex:
-        res = list(ex.map(run, parts))
+    try:  # one BLAS thread per worker: the workers already use every core
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limit = None
+    try:
+        with ThreadPoolExecutor(min(threads, len(parts))) as ex:
+            res = list(ex.map(run, parts))
+    finally:
+        if limit is not None:
+            limit.unregister()
     out = {key: np.concatenate([r[key] for r in res]) for key in ("sel", "out", "lse")}
     if want_scores:
         out["scores"] = [s for r in res for s in r["scores"]]
