@@ -215,9 +215,9 @@ def main():
     f_idx = index_flops_full(N_PREFILL)
     dbytes = decode_bytes(dec.ctx_lens)
     value = f_main / (pre_ms * 1e-3) / 1e12
-    attn_ms = float(pst[3])
+    attn_ms = float(pst[3] + pst[4])
     attn_tflops = f_main / (attn_ms * 1e-3) / 1e12
-    t_main_ms = float(pst[2] + pst[3] + pst[4])
+    t_main_ms = float(pst[2] + pst[3] + pst[4] + pst[5])
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
     dec_idx_bytes = sum((BK * ((L - 1) // BK) if (L - 1) // BK >= TOPK else 0) * DI * 2 for L in dec.ctx_lens)
 
@@ -248,7 +248,7 @@ def main():
                    "pct_of_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
                    "stage_ms": {k: round(float(x), 4) for k, x in zip(msa.DECODE_STAGES, dst)},
                    "index_GB/s": round(dec_idx_bytes / (float(dst[0]) * 1e-3) / 1e9, 1)},
-        "roofline": {"kernel": "k_attn_prefill", "bound": "mfma", "achieved": round(attn_tflops, 2),
+        "roofline": {"kernel": "k_attn_dense + k_attn_prefill", "bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
                      "traffic": None},
     }

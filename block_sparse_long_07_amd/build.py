@@ -35,6 +35,9 @@ def build(verbose: bool = False) -> str:
            "-Wall", "-Wno-unused-function",
            # packed fp32 instructions are kept out of all device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # inputs are finite (NaN inputs are undefined behaviour of the ABI):
+           # max/min need no NaN-quieting canonicalisation
+           "-fno-honor-nans", "-mno-amdgpu-ieee",
            "-I", INCLUDE, "-I", CSRC, "-o", tmp] + sources()
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -241,19 +241,20 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
                    at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist, nunits};
       launch_csr_and_tiles(ca, hs);
       clk.mark();
-      // 4. attention: query-stationary over unit-shared blocks, then KV-outer
+      // 4. attention: query-stationary over unit-shared blocks, 5. then KV-outer
       uint16_t* ow = os + w0 * Hq * kHeadDim;
       float* lw = lses ? lses + w0 * Hq : nullptr;
       LaunchAttnDense da{qs, ks, vs, dcnt, dlist, at<uint16_t>(workspace, L.dense_o),
                          at<float>(workspace, L.dense_lse), ow, lw, N, w0, (int)Wn, nunits, G, K, s.scale_log2};
       launch_attn_dense(da, hs);
+      clk.mark();
       LaunchAttnPrefill aa{qs, ks, vs, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
                            at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
                            at<float>(workspace, L.part_lse), N, w0, G, nbw, K, s.scale_log2,
-                           (int)std::min<int64_t>(2 * cu_count(), tile_cap)};
+                           (int)std::min<int64_t>(cu_count(), tile_cap)};
       launch_attn_prefill(aa, hs);
       clk.mark();
-      // 5. combine
+      // 6. combine
       LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse), selw, gstride, dcnt,
                        dlist, at<uint16_t>(workspace, L.dense_o), at<float>(workspace, L.dense_lse), nunits,
                        ow, lw, Wn, G, K, w0, nullptr};
@@ -302,7 +303,7 @@ msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_
   std::vector<hipEvent_t> ev;
   msa_status st = run_prefill(p, batch, seq_len, q, k, v, q_idx, k_idx, out, sel_out, lse_out, workspace,
                               workspace_bytes, stream, &ev);
-  return collect(ev, 5, stage_ms, st);
+  return collect(ev, 6, stage_ms, st);
 }
 
 size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx) {

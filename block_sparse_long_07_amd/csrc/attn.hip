@@ -2,81 +2,99 @@
 // organised KV-outer ("outer gather Q") [pnsm, section 7; yhxrc, 二;
 // yololab, "KV Outer Gather Q是什麼？"].
 //
-// Prefill: a persistent grid drains the tile queue built by the reverse index.
-// A tile is (group g, KV block b, up to tile_q queries that selected b). The
-// workgroup stages K_b row-major and V_b transposed in LDS once, then each wave
-// gathers the 16 query heads of one query at a time (4 KiB, contiguous in the
-// [N, Hq, d] layout) and computes, on MFMA,
-//   S^T (128 keys x 16 heads) = K_b (128 x 128) . Q^T        (32 MFMA 16x16x32)
-//   P^T = exp2(S^T * scale*log2e - m),  l = sum P, per head
-//   O^T (128 d x 16 heads)   = V_b^T (128 x 128 keys) . P^T  (32 MFMA)
-// The S^T orientation puts one head's scores in one lane column, so the softmax
+// Prefill has two passes. Blocks selected by every query of a 16-query unit
+// (the query's own block, sink-like or planted blocks) are computed
+// query-stationary: one workgroup per (unit, group) keeps the 16 queries' Q and
+// running softmax state in registers and streams the unit's shared blocks
+// through LDS (k_attn_dense). Every other (query, block) pair goes KV-outer: a
+// persistent grid drains the tile queue built by the reverse index, a tile being
+// (group g, KV block b, up to 16 queries that selected b); the block is staged
+// once and each wave gathers the 16 query heads of a query (4 KiB, contiguous in
+// the [N, Hq, d] layout) (k_attn_prefill). Both compute, on MFMA 16x16x32 bf16,
+//   S^T (128 keys x 16 heads) = K_b (128 x 128) . Q^T        (32 MFMA)
+//   P^T = 2^(S^T * scale*log2e - m),  l = sum P, per head
+//   O^T (128 d x 16 heads)  += V_b^T (128 x 128 keys) . P^T  (32 MFMA)
+// The S^T orientation puts one head's scores in one lane column, so softmax
 // reductions are in-lane plus two cross-lane steps, and the P^T accumulator
 // fragments feed the second contraction directly as its B operand (the key
 // order inside a 32-key step is permuted identically in V^T's A operand).
-// Output: one softmax partial per (query, head, selected slot): o/l rounded to
-// bf16 and lse2 = m + log2(l); merged later by the combine pass (two-phase
-// combine without atomics [pnsm, section 7]). Causal masking is needed only when
-// b is the query's own block.
+// KV-outer outputs one softmax partial per (query, head, selected slot), o/l
+// rounded to bf16 plus lse2 = m*c + log2(l); the combine pass merges them
+// without atomics (two-phase combine [pnsm, section 7]). Causal masking is
+// needed only in the query's own block.
 //
-// Decode: one wave per (sequence, group, selected slot) with the same
-// contraction on a single query.
+// K_b and V_b travel HBM -> LDS by direct LDS loads (global_load_lds, 16 bytes
+// per lane, no registers), double-buffered so the next block streams in while
+// the current one is computed. Both stay row-major in LDS (256 B per key row);
+// the V^T operand is read with the transposing ds_read_b64_tr_b16. XOR
+// swizzles of the 16-byte (K) and 32-byte (V) chunks keep the operand reads
+// free of bank conflicts.
+//
+// Decode: one workgroup per (sequence, group, selected slot); four waves stage
+// the block, one computes the 16 heads.
 #include "msa_device.h"
 #include "msa_launch.h"
 
 namespace msa {
 
-constexpr int KS = 136;  // LDS row stride (bf16) of K_b  [128 keys][128 d]
-constexpr int VS = 136;  // LDS row stride (bf16) of V_b^T [128 d][128 keys]
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+// LDS byte pointers stay in the local address space (32-bit addressing, no
+// generic-pointer checks)
+typedef __attribute__((address_space(3))) char lds_char;
 
-// Stage K_b row-major into Ks (128 keys x 128 d, padded rows). `rstride` is the
-// element distance between consecutive keys; keys >= nvalid are zero-filled.
-template <int NTHR>
-__device__ __forceinline__ void stage_k(uint16_t* Ks, const uint16_t* krow0, int64_t rstride, int nvalid, int tid) {
-#pragma unroll
-  for (int p = 0; p < 2048 / NTHR; ++p) {
-    const int it = p * NTHR + tid;
-    const int r = it >> 4, cc = it & 15;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (r < nvalid) val = ld16(krow0 + (int64_t)r * rstride + cc * 8);
-    *reinterpret_cast<u32x4*>(&Ks[r * KS + cc * 8]) = val;
+constexpr int kStage = 65536;  // bytes per staged block: K then V, 128 rows x 256 B each
+constexpr int kVOff = 32768;
+
+// Issue the direct-to-LDS loads of K_b and V_b (rows key0.., row stride
+// `rstride` elements) into one stage. Slot s (16 B) of the K half holds row
+// s/16, chunk (s%16) ^ (row & 15); of the V half, row s/16, 32-byte chunk
+// ((s%16)/2) ^ (row & 7), half (s%2). Rows at or past `nvalid` repeat the last
+// valid row, so every staged value is finite (those keys are masked).
+__device__ __forceinline__ void stage_block(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
+                                            int64_t rstride, int nvalid, int wave, int nwaves) {
+  const int lane = threadIdx.x & 63;
+  for (int s0 = wave * 64; s0 < 2048; s0 += nwaves * 64) {
+    const int slot = s0 + lane;
+    const int r = slot >> 4, p = slot & 15;
+    const int64_t row = (int64_t)min(r, nvalid - 1) * rstride;
+    const int ck = p ^ (r & 15);
+    const int cv = (((p >> 1) ^ (r & 7)) << 1) | (p & 1);
+    __builtin_amdgcn_global_load_lds(kr0 + row + ck * 8, (lds_void*)(stage + s0 * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vr0 + row + cv * 8, (lds_void*)(stage + kVOff + s0 * 16), 16, 0, 0);
   }
 }
 
-// Stage V_b transposed into Vt [d][key]. Work item `it` (0..511) covers key
-// quad kq (4 keys) x d-chunk dc (8 dims): kq = it%16 + 16*(it/256), dc =
-// (it/16)%16. Within a wave kq varies fastest, which keeps both the global
-// reads and the transposed 8-byte LDS writes free of bank conflicts.
-template <int NTHR>
-__device__ __forceinline__ void stage_vt(uint16_t* Vt, const uint16_t* vrow0, int64_t rstride, int nvalid,
-                                         int tid) {
-#pragma unroll
-  for (int p = 0; p < 512 / NTHR; ++p) {
-    const int it = p * NTHR + tid;
-    const int kq = (it & 15) | ((it >> 8) << 4);
-    const int dc = (it >> 4) & 15;
-    u32x4 rows[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int key = 4 * kq + rr;
-      rows[rr] = (u32x4){0u, 0u, 0u, 0u};
-      if (key < nvalid) rows[rr] = ld16(vrow0 + (int64_t)key * rstride + dc * 8);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      const uint32_t b0 = (rows[0][w] >> sh) & 0xffffu, b1 = (rows[1][w] >> sh) & 0xffffu;
-      const uint32_t b2 = (rows[2][w] >> sh) & 0xffffu, b3 = (rows[3][w] >> sh) & 0xffffu;
-      u32x2 pk2 = {b0 | (b1 << 16), b2 | (b3 << 16)};
-      *reinterpret_cast<u32x2*>(&Vt[(dc * 8 + e) * VS + 4 * kq]) = pk2;
-    }
-  }
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// K A-operand of key tile t, d-step st: lane (c, qd) holds K[16t + c][32st + 8qd .. +7].
+__device__ __forceinline__ bf16x8 lds_k(const lds_char* stage, int t, int st, int c, int qd) {
+  const int p = (4 * st + qd) ^ c;  // (16t + c) & 15 == c
+  const u32x4 v = *(const lds_u32x4*)(stage + (16 * t + c) * 256 + p * 16);
+  return as_bf16x8(v);
+}
+
+// V^T A-operand of d-tile dt, key step st: lane (c, qd) holds V[kappa][16dt + c]
+// for kappa = 32st + 4qd + {0..3} and 32st + 16 + 4qd + {0..3}. Each transposing
+// read gives lane j of a 16-lane group element (4r + j/4, j%4) of the 16 x 4
+// matrix whose row i is the 4 elements addressed by lane i; lane i therefore
+// addresses row 32st + 4qd + i/4 (+16), dims 16dt + 4(i%4) .. +3.
+__device__ __forceinline__ bf16x8 lds_vt(const lds_char* stage, int dt, int st, int c, int qd) {
+  const lds_char* vb = stage + kVOff;
+  const int r1 = 32 * st + 4 * qd + (c >> 2), r2 = r1 + 16;
+  const int off = 8 * (c & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + r1 * 256 + ((dt ^ (r1 & 7)) << 5) + off));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + r2 * 256 + ((dt ^ (r2 & 7)) << 5) + off));
+  return as_bf16x8((u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
 }
 
 // Per-wave state of QN queries (16 heads each) against staged blocks.
 //   qop: Q^T B-operands (4 steps over d); s: S^T / P^T fragments of the current
 //   block; o: O^T accumulators (head = lane & 15, d = 16*dt + 4*(lane/16) + r);
-//   m, l: running max (log2 domain) and denominator per head.
+//   m, l: running max of the raw scores and softmax denominator per head.
 template <int QN>
 struct QueryGroup {
   bf16x8 qop[QN][4];
@@ -91,14 +109,14 @@ __device__ __forceinline__ void load_q(QueryGroup<QN>& qg, int n, const uint16_t
   for (int st = 0; st < 4; ++st) qg.qop[n][st] = as_bf16x8(ld16(qrow + 32 * st));
 }
 
-// S^T = K_b . Q^T for the QN queries (4 steps over d per 16-key tile).
+// S^T = K_b . Q^T for the QN queries.
 template <int QN>
-__device__ __forceinline__ void scores(QueryGroup<QN>& qg, const uint16_t* Ks) {
+__device__ __forceinline__ void scores(QueryGroup<QN>& qg, const lds_char* stage_in) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
-  // An opaque zero offset keeps the K fragment reads inside the query loop
-  // (otherwise they are hoisted across queries into ~128 extra registers).
-  int lds_off = 0;
-  asm volatile("" : "+v"(lds_off));
+  // An opaque copy of the stage pointer keeps the K fragment reads inside the
+  // query loop (otherwise they are hoisted across queries into many registers).
+  const lds_char* stage = stage_in;
+  asm volatile("" : "+v"(stage));
 #pragma unroll
   for (int n = 0; n < QN; ++n)
 #pragma unroll
@@ -107,8 +125,7 @@ __device__ __forceinline__ void scores(QueryGroup<QN>& qg, const uint16_t* Ks) {
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const bf16x8 a =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(&Ks[lds_off + (16 * t + c) * KS + 32 * st + 8 * qd]));
+      const bf16x8 a = lds_k(stage, t, st, c, qd);
 #pragma unroll
       for (int n = 0; n < QN; ++n) qg.s[n][t] = mfma16x16x32(a, qg.qop[n][st], qg.s[n][t]);
     }
@@ -121,11 +138,11 @@ __device__ __forceinline__ void scores(QueryGroup<QN>& qg, const uint16_t* Ks) {
 // logit scale is folded into the exponent: p = 2^(s*c - m*c), m tracked on raw
 // scores. FIRST: the state is fresh (no rescaling of O and l needed).
 template <int QN, bool FIRST>
-__device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const uint16_t* Vt, const int* lim,
+__device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* stage_in, const int* lim,
                                            float scale_log2) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
-  int lds_off = 0;
-  asm volatile("" : "+v"(lds_off));
+  const lds_char* stage = stage_in;
+  asm volatile("" : "+v"(stage));
   bf16x8 pop[QN][4];
 #pragma unroll
   for (int n = 0; n < QN; ++n) {
@@ -177,10 +194,7 @@ __device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const uint16_t* V
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const uint16_t* vp = &Vt[lds_off + (16 * dt + c) * VS + 32 * st + 4 * qd];
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-      const bf16x8 a = as_bf16x8((u32x4){lo[0], lo[1], hi[0], hi[1]});
+      const bf16x8 a = lds_vt(stage, dt, st, c, qd);
 #pragma unroll
       for (int n = 0; n < QN; ++n) {
         if (FIRST && st == 0)
@@ -208,53 +222,76 @@ __device__ __forceinline__ void store_normalised(const f32x4 (&o)[8], float m, f
 }
 
 constexpr int kAttnQN = 2;
+constexpr int kAttnWaves = 8;
 
-// Sparse (KV-outer) part: persistent workgroups drain the tile queue. Each wave
-// takes QN queries of the tile at a time; the next group's Q is loaded into the
-// Q registers as soon as the current scores are formed, so its latency overlaps
-// the softmax and the P.V contraction.
-__global__ __launch_bounds__(256, 2) void k_attn_prefill(
+// Sparse (KV-outer) part: one persistent workgroup per CU drains the tile
+// queue. The next tile is claimed and its block streamed into the other LDS
+// stage while the current tile is computed. Each wave takes QN queries of the
+// tile per pass; the next group's Q is loaded into the Q registers as soon as
+// the current scores are formed.
+__global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ tiles, int32_t* __restrict__ tile_info,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int64_t n_tokens, int64_t row0, int G,
     int nbw, int topk, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * VS];
-  __shared__ int s_tile;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
+  __shared__ int s_t[2];
+  lds_char* lds = (lds_char*)lds_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, qd = lane >> 4;
   const int T = tile_info[0];
   const int Hq = G * kHpg;
+  const int64_t rstride = (int64_t)G * kHeadDim;
 
-  for (;;) {
-    if (tid == 0) s_tile = atomicAdd(&tile_info[1], 1);
-    __syncthreads();
-    const int t = s_tile;
-    if (t >= T) break;
-    const int l = tiles[4 * t + 0];
-    const int begin = tiles[4 * t + 1];
-    const int len = tiles[4 * t + 2];
-    const int g = l / nbw, b = l % nbw;
+  if (tid == 0) s_t[0] = atomicAdd(&tile_info[1], 1);
+  __syncthreads();
+  int tcur = s_t[0];
+  int begin = 0, len = 0, g = 0, b = 0;
+  if (tcur < T) {
+    const int l = tiles[4 * tcur];
+    begin = tiles[4 * tcur + 1];
+    len = tiles[4 * tcur + 2];
+    g = l / nbw;
+    b = l % nbw;
     const int64_t key0 = (int64_t)b * kBlock;
-    const int nvalid = (int)min<int64_t>(kBlock, n_tokens - key0);
-
-    QueryGroup<kAttnQN> qg;
-    int ent[kAttnQN];
-    int e0 = wave * kAttnQN;
-    if (e0 < len) {
+    stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
+                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
+  }
+  QueryGroup<kAttnQN> qg;
+  int ent[kAttnQN];
+  int e0 = wave * kAttnQN;
+  // Q of the wave's current group; `have_q` says it is already loaded
+  bool have_q = false;
+  auto fetch_group = [&](int tb, int tg, int tlen, int e) {
 #pragma unroll
-      for (int n = 0; n < kAttnQN; ++n) {
-        ent[n] = entries[begin + min(e0 + n, len - 1)];
-        const int64_t i = row0 + (ent[n] >> 4);
-        load_q(qg, n, q + ((i * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
-      }
+    for (int n = 0; n < kAttnQN; ++n) {
+      ent[n] = entries[tb + min(e + n, tlen - 1)];
+      const int64_t i = row0 + (ent[n] >> 4);
+      load_q(qg, n, q + ((i * Hq) + tg * kHpg + c) * kHeadDim + 8 * qd);
     }
-    stage_k<256>(Ks, k + (key0 * G + g) * kHeadDim, (int64_t)G * kHeadDim, nvalid, tid);
-    stage_vt<256>(Vt, v + (key0 * G + g) * kHeadDim, (int64_t)G * kHeadDim, nvalid, tid);
-    __syncthreads();
-
-    for (; e0 < len; e0 += 4 * kAttnQN) {
-      scores(qg, Ks);
+  };
+  for (int j = 0; tcur < T; ++j) {
+    if (tid == 0) s_t[(j + 1) & 1] = atomicAdd(&tile_info[1], 1);
+    if (!have_q && e0 < len) fetch_group(begin, g, len, e0);
+    wait_loads();
+    __syncthreads();  // stage j&1 is complete; stage (j+1)&1 is free; s_t visible
+    const int tnext = s_t[(j + 1) & 1];
+    int nbegin = 0, nlen = 0, ng = 0, nb2 = 0;
+    if (tnext < T) {
+      const int l2 = tiles[4 * tnext];
+      nbegin = tiles[4 * tnext + 1];
+      nlen = tiles[4 * tnext + 2];
+      ng = l2 / nbw;
+      nb2 = l2 % nbw;
+      const int64_t k2 = (int64_t)nb2 * kBlock;
+      stage_block(lds + ((j + 1) & 1) * kStage, k + (k2 * G + ng) * kHeadDim, v + (k2 * G + ng) * kHeadDim,
+                  rstride, (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
+    }
+    const int64_t key0 = (int64_t)b * kBlock;
+    const lds_char* stage = lds + (j & 1) * kStage;
+    have_q = false;
+    for (; e0 < len; e0 += kAttnWaves * kAttnQN) {
+      scores(qg, stage);
       int lim[kAttnQN], cur[kAttnQN];
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
@@ -262,16 +299,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(
         const int64_t i = row0 + (cur[n] >> 4);
         lim[n] = ((i >> 7) == b) ? (int)(i - key0) : kBlock;  // causal limit inside the own block
       }
-      const int e1 = e0 + 4 * kAttnQN;
-      if (e1 < len) {  // prefetch the next group's Q into the (now free) Q registers
-#pragma unroll
-        for (int n = 0; n < kAttnQN; ++n) {
-          ent[n] = entries[begin + min(e1 + n, len - 1)];
-          const int64_t i = row0 + (ent[n] >> 4);
-          load_q(qg, n, q + ((i * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
-        }
+      // prefetch the wave's next group (in this tile, else the first of the next
+      // tile) into the Q registers, which the scores no longer need
+      const int e1 = e0 + kAttnWaves * kAttnQN;
+      if (e1 < len) {
+        fetch_group(begin, g, len, e1);
+      } else if (wave * kAttnQN < nlen) {
+        fetch_group(nbegin, ng, nlen, wave * kAttnQN);
+        have_q = true;
       }
-      softmax_pv<kAttnQN, true>(qg, Vt, lim, scale_log2);
+      softmax_pv<kAttnQN, true>(qg, stage, lim, scale_log2);
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
         if (e0 + n < len) {
@@ -281,33 +318,45 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(
         }
       }
     }
-    __syncthreads();
+    tcur = tnext;
+    begin = nbegin;
+    len = nlen;
+    g = ng;
+    b = nb2;
+    e0 = wave * kAttnQN;
   }
 }
 
 // Dense part: blocks selected by every query of a 16-query unit are computed
 // query-stationary (FlashAttention-style online softmax over the unit's shared
-// blocks, K/V staged once per block for all 16 queries). One workgroup of 8
-// waves per (unit, group), two queries per wave. A unit whose every selected
-// block is shared writes the final output directly; otherwise its single
-// partial is merged with the KV-outer partials by the combine pass.
+// blocks; each block is staged once for all 16 queries, the next one streaming
+// into the other stage meanwhile). One workgroup of 8 waves per (unit, group),
+// two queries per wave. A unit whose every selected block is shared writes the
+// final output directly; otherwise its single partial is merged with the
+// KV-outer partials by the combine pass.
 __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ dense_cnt, const int32_t* __restrict__ dense_list, uint16_t* __restrict__ dense_o,
     float* __restrict__ dense_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t n_tokens,
     int64_t row0, int nrows, int nunits, int G, int topk, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * VS];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
+  lds_char* lds = (lds_char*)lds_raw;
   const int unit = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
+  const int64_t rstride = (int64_t)G * kHeadDim;
   const int nd = dense_cnt[g * nunits + unit];
   const int32_t* list = dense_list + ((int64_t)g * nunits + unit) * topk;
   const int i_rel0 = unit * 16 + wave * kAttnQN;
   const int b_loc = (int)((row0 + unit * 16) / kBlock);
   const bool final_out = nd == min(topk, b_loc + 1);
 
+  if (nd > 0) {
+    const int64_t key0 = (int64_t)list[0] * kBlock;
+    stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
+                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
+  }
   QueryGroup<kAttnQN> qg;
   int lim[kAttnQN];
 #pragma unroll
@@ -322,18 +371,21 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   for (int d = 0; d < nd; ++d) {
     const int b = list[d];
     const int64_t key0 = (int64_t)b * kBlock;
-    const int nvalid = (int)min<int64_t>(kBlock, n_tokens - key0);
-    stage_k<512>(Ks, k + (key0 * G + g) * kHeadDim, (int64_t)G * kHeadDim, nvalid, tid);
-    stage_vt<512>(Vt, v + (key0 * G + g) * kHeadDim, (int64_t)G * kHeadDim, nvalid, tid);
-    __syncthreads();
+    wait_loads();
+    __syncthreads();  // stage d&1 complete; stage (d+1)&1 free
+    if (d + 1 < nd) {
+      const int64_t k2 = (int64_t)list[d + 1] * kBlock;
+      stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim,
+                  rstride, (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
+    }
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) {
       const int64_t i = row0 + min(i_rel0 + n, nrows - 1);
       lim[n] = (b == b_loc) ? (int)(i - key0) : kBlock;
     }
-    scores(qg, Ks);
-    softmax_pv<kAttnQN, false>(qg, Vt, lim, scale_log2);
-    __syncthreads();
+    const lds_char* stage = lds + (d & 1) * kStage;
+    scores(qg, stage);
+    softmax_pv<kAttnQN, false>(qg, stage, lim, scale_log2);
   }
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
@@ -359,39 +411,41 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   }
 }
 
-__global__ __launch_bounds__(64) void k_attn_decode(const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v,
-                                                    const int32_t* __restrict__ ctx_lens,
-                                                    const int32_t* __restrict__ sel,
-                                                    uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-                                                    int64_t max_ctx, int G, int topk, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * VS];
+// Decode: one workgroup per (sequence, group, selected slot). All four waves
+// stage the block; wave 0 computes the 16 heads.
+__global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ v,
+                                                     const int32_t* __restrict__ ctx_lens,
+                                                     const int32_t* __restrict__ sel,
+                                                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
+                                                     int64_t max_ctx, int G, int topk, float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kStage];
+  lds_char* lds = (lds_char*)lds_raw;
   const int item = blockIdx.x;
   const int sq = item / (G * topk), g = (item / topk) % G;
   const int b = sel[item];
   if (b < 0) return;
-  const int tid = threadIdx.x, c = tid & 15, qd = tid >> 4;
+  const int tid = threadIdx.x, wave = tid >> 6, c = tid & 15, qd = (tid >> 4) & 3;
   const int64_t i = ctx_lens[sq] - 1;
   const int64_t key0 = (int64_t)b * kBlock;
-  const int nvalid = (int)min<int64_t>(kBlock, max_ctx - key0);
   const int Hq = G * kHpg;
   const int64_t base = ((int64_t)sq * max_ctx * G + key0 * G + g) * kHeadDim;
+  stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(kBlock, max_ctx - key0), wave, 4);
   QueryGroup<1> qg;
-  load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
-  stage_k<64>(Ks, k + base, (int64_t)G * kHeadDim, nvalid, tid);
-  stage_vt<64>(Vt, v + base, (int64_t)G * kHeadDim, nvalid, tid);
+  if (wave == 0) load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
+  wait_loads();
   __syncthreads();
+  if (wave != 0) return;
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
-  scores(qg, Ks);
-  softmax_pv<1, true>(qg, Vt, lim, scale_log2);
+  scores(qg, lds);
+  softmax_pv<1, true>(qg, lds, lim, scale_log2);
   store_normalised(qg.o[0], qg.m[0], qg.l[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                    part_lse + (int64_t)item * kHpg);
 }
 
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_prefill, dim3(a.grid), dim3(256), 0, st, a.q, a.k, a.v, a.entries, a.tiles,
+  hipLaunchKernelGGL(k_attn_prefill, dim3(a.grid), dim3(512), 0, st, a.q, a.k, a.v, a.entries, a.tiles,
                      a.tile_info, a.part_o, a.part_lse, a.n_tokens, a.row0, a.G, a.nbw, a.topk, a.scale_log2);
 }
 
@@ -405,7 +459,7 @@ void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st) {
   const int items = a.batch * a.G * a.topk;
   if (items <= 0) return;
-  hipLaunchKernelGGL(k_attn_decode, dim3(items), dim3(64), 0, st, a.q, a.k, a.v, a.ctx_lens, a.sel, a.part_o,
+  hipLaunchKernelGGL(k_attn_decode, dim3(items), dim3(256), 0, st, a.q, a.k, a.v, a.ctx_lens, a.sel, a.part_o,
                      a.part_lse, a.max_ctx, a.G, a.topk, a.scale_log2);
 }
 

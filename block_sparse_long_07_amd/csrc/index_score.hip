@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_index_prefill(const uint16_t* __restric
 // kDecKB key blocks), each wave scoring whole key blocks. The shared index key
 // cache is streamed once (the two half-row loads of a key row hit the same L2
 // line); lanes c < G of the MFMA column dimension carry the G index query heads.
-constexpr int kDecKB = 16;
+constexpr int kDecKB = 8;
 
 template <int G>
 __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict__ q_idx,
@@ -112,25 +112,36 @@ __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict
   }
   const uint16_t* kbase = k_idx + (int64_t)sq * max_ctx * kIndexDim;
 
-  for (int kb = kb0 + wave; kb < kb1; kb += 4) {
-    u32x4 a[8][2];
+  // two key blocks per iteration: all 32 loads are issued before the first MFMA
+  for (int kb = kb0 + wave; kb < kb1; kb += 8) {
+    const int kb2 = kb + 4;
+    const bool two = kb2 < kb1;
+    u32x4 a[2][8][2];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint16_t* krow = kbase + ((int64_t)kb * kBlock + 16 * t + c) * kIndexDim + 8 * qd;
-      a[t][0] = ld16(krow);
-      a[t][1] = ld16(krow + 32);
-    }
-    float mx = -__builtin_inff();
+    for (int h = 0; h < 2; ++h) {
+      const int blk = h ? (two ? kb2 : kb) : kb;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16x16x32(as_bf16x8(a[t][0]), qop[0], acc);
-      acc = mfma16x16x32(as_bf16x8(a[t][1]), qop[1], acc);
-      mx = fmaxf(mx, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+      for (int t = 0; t < 8; ++t) {
+        const uint16_t* krow = kbase + ((int64_t)blk * kBlock + 16 * t + c) * kIndexDim + 8 * qd;
+        a[h][t][0] = ld16(krow);
+        a[h][t][1] = ld16(krow + 32);
+      }
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (qd == 0 && c < G) sblk[((int64_t)sq * G + c) * nb + kb] = mx;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16x16x32(as_bf16x8(a[h][t][0]), qop[0], acc);
+        acc = mfma16x16x32(as_bf16x8(a[h][t][1]), qop[1], acc);
+        mx = fmaxf(mx, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+      }
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const int blk = h ? kb2 : kb;
+      if (qd == 0 && c < G && (h == 0 || two)) sblk[((int64_t)sq * G + c) * nb + blk] = mx;
+    }
   }
 }
 

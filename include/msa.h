@@ -118,8 +118,8 @@ msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx,
  * on `stream` at every stage boundary. They synchronise on the last event and
  * return in stage_ms the duration of each stage, summed over sequences and
  * windows:
- *   prefill (5): index scores, top-k selection, reverse index + tile schedule,
- *                KV-outer attention, combine
+ *   prefill (6): index scores, top-k selection, reverse index + tile schedule,
+ *                attention over unit-shared blocks, KV-outer attention, combine
  *   decode  (4): index scores, top-k selection, attention, combine
  * stage_ms must not be NULL (MSA_ERR_INVALID_ARG). */
 msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len,
