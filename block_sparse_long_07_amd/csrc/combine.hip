@@ -26,39 +26,42 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
   const int64_t rg = blockIdx.x;
   const int64_t rr = rg / G;
   const int g = (int)(rg % G);
-  const int t = threadIdx.x, h = t >> 4, d0 = (t & 15) * 8;
+  const int t = threadIdx.x, lane = t & 63, h = t >> 4, d0 = (t & 15) * 8;
   const int b_loc = ctx_lens ? (ctx_lens[rr] - 1) / kBlock : (int)((row0 + rr) / kBlock);
   const int nsel = min(topk, b_loc + 1);
   const int64_t slot0 = rg * topk;
 
-  // slots covered by the dense pass (bit u set), via a merge walk of two ascending lists
-  uint32_t skip = 0u;
+  // slots whose block was covered by the dense pass: lane u < nsel tests its
+  // block against the unit's shared list; one ballot gives the wave the mask
+  uint64_t skip = 0ull;
   int nd = 0;
-  const int32_t* dl = nullptr;
   if (dense_cnt) {
     const int unit = (int)(rr >> 4);
     nd = dense_cnt[g * nunits + unit];
     if (nd == nsel) return;  // written in full by the dense pass
-    dl = dense_list + ((int64_t)g * nunits + unit) * topk;
-    const int32_t* srow = sel + (int64_t)g * sel_gstride + rr * topk;
-    int j = 0;
-    for (int u = 0; u < nsel && j < nd; ++u) {
-      const int b = srow[u];
-      while (j < nd && dl[j] < b) ++j;
-      if (j < nd && dl[j] == b) {
-        skip |= 1u << u;
-        ++j;
-      }
+    const int32_t* dl = dense_list + ((int64_t)g * nunits + unit) * topk;
+    bool covered = false;
+    if (lane < nsel) {
+      const int b = sel[(int64_t)g * sel_gstride + rr * topk + lane];
+      for (int j = 0; j < nd; ++j) covered |= (dl[j] == b);
     }
+    skip = __ballot(covered);
   }
+  const uint64_t use = ((nsel >= 64) ? ~0ull : ((1ull << nsel) - 1ull)) & ~skip;
+
+  float lse_u[kMaxTopk];
   float M = -__builtin_inff();
+#pragma unroll
+  for (int u = 0; u < kMaxTopk; ++u) {
+    lse_u[u] = -__builtin_inff();
+    if ((use >> u) & 1ull) lse_u[u] = __builtin_nontemporal_load(part_lse + (slot0 + u) * kHpg + h);
+    M = fmaxf(M, lse_u[u]);
+  }
   float dl2 = -__builtin_inff();
   if (nd > 0) {
     dl2 = __builtin_nontemporal_load(dense_lse + rg * kHpg + h);
-    M = dl2;
+    M = fmaxf(M, dl2);
   }
-  for (int u = 0; u < nsel; ++u)
-    if (!((skip >> u) & 1u)) M = fmaxf(M, __builtin_nontemporal_load(part_lse + (slot0 + u) * kHpg + h));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (nd > 0) {
@@ -71,9 +74,10 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
       acc[2 * e + 1] += w * bf2f(o[e] >> 16);
     }
   }
-  for (int u = 0; u < nsel; ++u) {
-    if ((skip >> u) & 1u) continue;
-    const float w = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(part_lse + (slot0 + u) * kHpg + h) - M);
+#pragma unroll
+  for (int u = 0; u < kMaxTopk; ++u) {
+    if (!((use >> u) & 1ull)) continue;
+    const float w = __builtin_amdgcn_exp2f(lse_u[u] - M);
     wsum += w;
     const u32x4 o = ld16_nt(part_o + ((slot0 + u) * kHpg + h) * kHeadDim + d0);
 #pragma unroll

@@ -18,15 +18,37 @@
 namespace msa {
 
 // One workgroup (4 waves) per (query block qb, chunk of kKC key blocks); it
-// covers the 128*G index rows (i, g) of the query block, 32*G per wave.
+// covers the 128*G index rows (i, g) of the query block, 32*G per wave. Each
+// 16 KiB key block is loaded once per workgroup straight into LDS
+// (global_load_lds, double-buffered) and read as MFMA operands by all waves.
+// LDS layout: 128 rows of 128 B; 16-byte chunk x of row r sits at chunk
+// position x ^ ((r >> 1) & 7), which keeps the operand reads conflict-free.
 constexpr int kKC = 8;
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+__device__ __forceinline__ void stage_kidx(lds_char* dst, const uint16_t* src_rows, int wave) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int s0 = (it * 4 + wave) * 64;
+    const int slot = s0 + lane;
+    const int r = slot >> 3, p = slot & 7;
+    const int x = p ^ ((r >> 1) & 7);
+    __builtin_amdgcn_global_load_lds(src_rows + r * kIndexDim + x * 8, (lds_void*)(dst + s0 * 16), 16, 0, 0);
+  }
+}
+
 template <int G>
-__global__ __launch_bounds__(256) void k_index_prefill(const uint16_t* __restrict__ q_idx,
-                                                       const uint16_t* __restrict__ k_idx,
-                                                       float* __restrict__ sblk, int64_t n_tokens,
-                                                       int64_t row0, int qb_begin, int nb) {
+__global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __restrict__ q_idx,
+                                                          const uint16_t* __restrict__ k_idx,
+                                                          float* __restrict__ sblk, int64_t n_tokens,
+                                                          int64_t row0, int qb_begin, int nb) {
   constexpr int RT = 2 * G;  // 16-row tiles per wave
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * 16384];
+  lds_char* lds = (lds_char*)lds_raw;
   const int qb = qb_begin + (int)blockIdx.y;
   const int kb0 = (int)blockIdx.x * kKC;
   if (kb0 >= qb) return;
@@ -34,10 +56,11 @@ __global__ __launch_bounds__(256) void k_index_prefill(const uint16_t* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, qd = lane >> 4;
 
+  stage_kidx(lds, k_idx + (int64_t)kb0 * kBlock * kIndexDim, wave);
+
   // flat index row (i*G + g) of this wave's first row
   const int64_t flat0 = (int64_t)qb * kBlock * G + (int64_t)wave * 32 * G;
   const int64_t flat_end = n_tokens * G;
-
   bf16x8 qop[RT][2];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -51,20 +74,27 @@ __global__ __launch_bounds__(256) void k_index_prefill(const uint16_t* __restric
   }
 
   for (int kb = kb0; kb < kb1; ++kb) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block kb staged; the other stage is free
+    if (kb + 1 < kb1)
+      stage_kidx(lds + ((kb + 1 - kb0) & 1) * 16384, k_idx + (int64_t)(kb + 1) * kBlock * kIndexDim, wave);
+    const lds_char* st = lds + ((kb - kb0) & 1) * 16384;
     float mx[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) mx[rt] = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint16_t* krow = k_idx + ((int64_t)kb * kBlock + 16 * t + c) * kIndexDim + 8 * qd;
-      const bf16x8 a0 = as_bf16x8(ld16(krow));
-      const bf16x8 a1 = as_bf16x8(ld16(krow + 32));
+      const int r = 16 * t + c;
+      const int sw = (c >> 1) & 7;
+      const u32x4 v0 = *(const lds_u32x4*)(st + r * 128 + ((qd ^ sw) << 4));
+      const u32x4 v1 = *(const lds_u32x4*)(st + r * 128 + (((4 + qd) ^ sw) << 4));
+      const bf16x8 a0 = as_bf16x8(v0), a1 = as_bf16x8(v1);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mfma16x16x32(a0, qop[rt][0], acc);
         acc = mfma16x16x32(a1, qop[rt][1], acc);
-        mx[rt] = fmaxf(mx[rt], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        mx[rt] = fmaxf(fmaxf(mx[rt], fmaxf(acc[0], acc[1])), fmaxf(acc[2], acc[3]));
       }
     }
 #pragma unroll
