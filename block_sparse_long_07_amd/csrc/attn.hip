@@ -93,20 +93,32 @@ __device__ __forceinline__ bf16x8 lds_vt(const lds_char* stage, int dt, int st, 
 
 // Per-wave state of QN queries (16 heads each) against staged blocks.
 //   qop: Q^T B-operands (4 steps over d); s: S^T / P^T fragments of the current
-//   block; o: O^T accumulators (head = lane & 15, d = 16*dt + 4*(lane/16) + r);
-//   m, l: running max of the raw scores and softmax denominator per head.
+//   block; o[0..7]: O^T accumulators (head = lane & 15, d = 16*dt + 4*(lane/16)
+//   + r); o[8]: every element is the softmax denominator of the lane's head
+//   (see softmax_pv); m: reference max of the raw scores per head.
 template <int QN>
 struct QueryGroup {
   bf16x8 qop[QN][4];
   f32x4 s[QN][8];
-  f32x4 o[QN][8];
-  float m[QN], l[QN];
+  f32x4 o[QN][9];
+  float m[QN];
 };
 
 template <int QN>
 __device__ __forceinline__ void load_q(QueryGroup<QN>& qg, int n, const uint16_t* qrow) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) qg.qop[n][st] = as_bf16x8(ld16(qrow + 32 * st));
+}
+
+// Running state before the first block: reference max -inf, zero accumulators.
+template <int QN>
+__device__ __forceinline__ void reset_state(QueryGroup<QN>& qg) {
+#pragma unroll
+  for (int n = 0; n < QN; ++n) {
+    qg.m[n] = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < 9; ++t) qg.o[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
 }
 
 // S^T = K_b . Q^T for the QN queries.
@@ -121,23 +133,36 @@ __device__ __forceinline__ void scores(QueryGroup<QN>& qg, const lds_char* stage
   for (int n = 0; n < QN; ++n)
 #pragma unroll
     for (int t = 0; t < 8; ++t) qg.s[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // d-step outer, key tile inner: 8*QN independent accumulators between two
+  // dependent MFMAs, and the 8 operand reads of a step are issued together.
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int st = 0; st < 4; ++st) {
+    bf16x8 a[8];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 a = lds_k(stage, t, st, c, qd);
+    for (int t = 0; t < 8; ++t) a[t] = lds_k(stage, t, st, c, qd);
 #pragma unroll
-      for (int n = 0; n < QN; ++n) qg.s[n][t] = mfma16x16x32(a, qg.qop[n][st], qg.s[n][t]);
-    }
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int n = 0; n < QN; ++n) qg.s[n][t] = mfma16x16x32(a[t], qg.qop[n][st], qg.s[n][t]);
   }
 }
 
-// Online-softmax update of (m, l, O) with the block's scores, then
-// O^T += V_b^T . P^T. Keys with index > lim[n] inside the block are masked
-// (causal limit in the query's own block; lim >= 127 means no mask). The
-// logit scale is folded into the exponent: p = 2^(s*c - m*c), m tracked on raw
-// scores. FIRST: the state is fresh (no rescaling of O and l needed).
-template <int QN, bool FIRST>
+// Exponent headroom of the lazily rescaled softmax: P may reach 2^kLazy
+// before the running state is rescaled to a new reference max.
+constexpr float kLazy = 8.0f;
+
+// Softmax update of the running state with the block's scores, then
+// O^T += V_b^T . P^T.
+//  * The logit scale is folded into the exponent: p = 2^(s*c - m*c) (c = scale
+//    * log2 e), with the reference max m kept on raw scores.
+//  * FIRST: fresh state; m is this block's max and the accumulators start at 0.
+//    Otherwise the state is rescaled only when some head's block max exceeds
+//    its reference by more than kLazy/c (the rescale is exact: every term is
+//    multiplied by the same 2^((m_old - m_new) c)).
+//  * MASKED: the queries' own block; keys with index > lim[n] are masked.
+//  * The denominator is accumulated by MFMA as a ninth O^T tile whose A operand
+//    is all ones, so it sums exactly the bf16-rounded P that enters P.V.
+template <int QN, bool FIRST, bool MASKED>
 __device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* stage_in, const int* lim,
                                            float scale_log2) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
@@ -146,40 +171,34 @@ __device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* s
   bf16x8 pop[QN][4];
 #pragma unroll
   for (int n = 0; n < QN; ++n) {
-    if (lim[n] < kBlock - 1) {  // wave-uniform: only the query's own block
+    if (MASKED) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (16 * t + 4 * qd + r > lim[n]) qg.s[n][t][r] = -__builtin_inff();
     }
-    float mx = FIRST ? -__builtin_inff() : qg.m[n];
+    float mx = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       mx = fmaxf(fmaxf(mx, fmaxf(qg.s[n][t][0], qg.s[n][t][1])), fmaxf(qg.s[n][t][2], qg.s[n][t][3]));
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float mc = mx * scale_log2;
-    float sum = 0.f;
+    if (FIRST) {
+      qg.m[n] = mx;
+    } else if (__any((mx - qg.m[n]) * scale_log2 > kLazy)) {
+      const float mnew = fmaxf(qg.m[n], mx);
+      const float alpha = __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
+#pragma unroll
+      for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha;
+      qg.m[n] = mnew;
+    }
+    const float mc = qg.m[n] * scale_log2;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(qg.s[n][t][r], scale_log2, -mc));
-        qg.s[n][t][r] = pv;
-        sum += pv;
-      }
-    sum += shfl_xor_f(sum, 16);
-    sum += shfl_xor_f(sum, 32);
-    if (FIRST) {
-      qg.l[n] = sum;
-    } else {
-      const float alpha = __builtin_amdgcn_exp2f((qg.m[n] - mx) * scale_log2);
-      qg.l[n] = qg.l[n] * alpha + sum;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) qg.o[n][t] *= alpha;
-    }
-    qg.m[n] = mx;
+      for (int r = 0; r < 4; ++r)
+        qg.s[n][t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(qg.s[n][t][r], scale_log2, -mc));
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       u32x4 w;
@@ -190,17 +209,23 @@ __device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* s
       pop[n][st] = as_bf16x8(w);
     }
   }
+  const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
+  const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
+  // key step outer, d tile inner (9*QN independent accumulators)
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
+  for (int st = 0; st < 4; ++st) {
+    bf16x8 a[9];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 a = lds_vt(stage, dt, st, c, qd);
+    for (int dt = 0; dt < 8; ++dt) a[dt] = lds_vt(stage, dt, st, c, qd);
+    a[8] = ones;
+#pragma unroll
+    for (int dt = 0; dt < 9; ++dt) {
 #pragma unroll
       for (int n = 0; n < QN; ++n) {
         if (FIRST && st == 0)
-          qg.o[n][dt] = mfma16x16x32(a, pop[n][st], (f32x4){0.f, 0.f, 0.f, 0.f});
+          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][st], (f32x4){0.f, 0.f, 0.f, 0.f});
         else
-          qg.o[n][dt] = mfma16x16x32(a, pop[n][st], qg.o[n][dt]);
+          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][st], qg.o[n][dt]);
       }
     }
   }
@@ -208,9 +233,10 @@ __device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* s
 
 // Normalised O (bf16, [16 heads][128 d] at dst) and lse2 = m*c + log2(l) of
 // one query (c = scale*log2 e).
-__device__ __forceinline__ void store_normalised(const f32x4 (&o)[8], float m, float l, float scale_log2,
+__device__ __forceinline__ void store_normalised(const f32x4 (&o)[9], float m, float scale_log2,
                                                  uint16_t* dst16x128, float* lse16) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
+  const float l = o[8][0];
   const float inv = 1.0f / l;
   uint16_t* dst = dst16x128 + c * kHeadDim + 4 * qd;
 #pragma unroll
@@ -225,7 +251,8 @@ constexpr int kAttnQN = 2;
 constexpr int kAttnWaves = 8;
 
 // Sparse (KV-outer) part: one persistent workgroup per CU drains the tile
-// queue. The next tile is claimed and its block streamed into the other LDS
+// queue. A query's own block is always shared by its whole 16-row unit, so no
+// KV-outer tile needs causal masking. The next tile is claimed and its block streamed into the other LDS
 // stage while the current tile is computed. Each wave takes QN queries of the
 // tile per pass; the next group's Q is loaded into the Q registers as soon as
 // the current scores are formed.
@@ -287,18 +314,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
       stage_block(lds + ((j + 1) & 1) * kStage, k + (k2 * G + ng) * kHeadDim, v + (k2 * G + ng) * kHeadDim,
                   rstride, (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
     }
-    const int64_t key0 = (int64_t)b * kBlock;
     const lds_char* stage = lds + (j & 1) * kStage;
     have_q = false;
     for (; e0 < len; e0 += kAttnWaves * kAttnQN) {
       scores(qg, stage);
-      int lim[kAttnQN], cur[kAttnQN];
+      int cur[kAttnQN];
 #pragma unroll
-      for (int n = 0; n < kAttnQN; ++n) {
-        cur[n] = ent[n];
-        const int64_t i = row0 + (cur[n] >> 4);
-        lim[n] = ((i >> 7) == b) ? (int)(i - key0) : kBlock;  // causal limit inside the own block
-      }
+      for (int n = 0; n < kAttnQN; ++n) cur[n] = ent[n];
       // prefetch the wave's next group (in this tile, else the first of the next
       // tile) into the Q registers, which the scores no longer need
       const int e1 = e0 + kAttnWaves * kAttnQN;
@@ -308,13 +330,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
         fetch_group(nbegin, ng, nlen, wave * kAttnQN);
         have_q = true;
       }
-      softmax_pv<kAttnQN, true>(qg, stage, lim, scale_log2);
+      softmax_pv<kAttnQN, true, false>(qg, stage, nullptr, scale_log2);
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
         if (e0 + n < len) {
           const int64_t slot = ((int64_t)(cur[n] >> 4) * G + g) * topk + (cur[n] & 15);
-          store_normalised(qg.o[n], qg.m[n], qg.l[n], scale_log2, part_o + slot * kHpg * kHeadDim,
-                           part_lse + slot * kHpg);
+          store_normalised(qg.o[n], qg.m[n], scale_log2, part_o + slot * kHpg * kHeadDim, part_lse + slot * kHpg);
         }
       }
     }
@@ -358,19 +379,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
                 (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
   }
   QueryGroup<kAttnQN> qg;
-  int lim[kAttnQN];
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int64_t i = row0 + min(i_rel0 + n, nrows - 1);
     load_q(qg, n, q + ((i * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
-    qg.m[n] = -__builtin_inff();  // running state: the first block rescales by 2^-inf = 0
-    qg.l[n] = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qg.o[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
+  reset_state(qg);
+  // the list is ascending and always ends with the units' own block b_loc,
+  // the only one that needs the causal mask
   for (int d = 0; d < nd; ++d) {
-    const int b = list[d];
-    const int64_t key0 = (int64_t)b * kBlock;
     wait_loads();
     __syncthreads();  // stage d&1 complete; stage (d+1)&1 free
     if (d + 1 < nd) {
@@ -378,21 +395,25 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
       stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim,
                   rstride, (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
     }
-#pragma unroll
-    for (int n = 0; n < kAttnQN; ++n) {
-      const int64_t i = row0 + min(i_rel0 + n, nrows - 1);
-      lim[n] = (b == b_loc) ? (int)(i - key0) : kBlock;
-    }
     const lds_char* stage = lds + (d & 1) * kStage;
     scores(qg, stage);
-    softmax_pv<kAttnQN, false>(qg, stage, lim, scale_log2);
+    if (d + 1 < nd) {
+      softmax_pv<kAttnQN, false, false>(qg, stage, nullptr, scale_log2);
+    } else {
+      int lim[kAttnQN];
+#pragma unroll
+      for (int n = 0; n < kAttnQN; ++n)
+        lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
+      softmax_pv<kAttnQN, false, true>(qg, stage, lim, scale_log2);
+    }
   }
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int i_rel = i_rel0 + n;
     if (i_rel >= nrows) continue;
     if (final_out) {
-      const float inv = 1.0f / qg.l[n];
+      const float l = qg.o[n][8][0];
+      const float inv = 1.0f / l;
       uint16_t* dst = out + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -402,11 +423,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
       }
       if (lse_out && qd == 0)
         lse_out[(int64_t)i_rel * Hq + g * kHpg + c] =
-            (qg.m[n] * scale_log2 + __builtin_amdgcn_logf(qg.l[n])) * 0.69314718055994530942f;
+            (qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
     } else {
       const int64_t row = (int64_t)i_rel * G + g;
-      store_normalised(qg.o[n], qg.m[n], qg.l[n], scale_log2, dense_o + row * kHpg * kHeadDim,
-                       dense_lse + row * kHpg);
+      store_normalised(qg.o[n], qg.m[n], scale_log2, dense_o + row * kHpg * kHeadDim, dense_lse + row * kHpg);
     }
   }
 }
@@ -439,8 +459,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   if (wave != 0) return;
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
   scores(qg, lds);
-  softmax_pv<1, true>(qg, lds, lim, scale_log2);
-  store_normalised(qg.o[0], qg.m[0], qg.l[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
+  softmax_pv<1, true, true>(qg, lds, lim, scale_log2);
+  store_normalised(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                    part_lse + (int64_t)item * kHpg);
 }
 
