@@ -86,6 +86,55 @@ def decode_bytes(ctx_lens, topk=TOPK):
     return float(tot)
 
 
+def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
+    """Split the selected (query, group, block) pairs of a prefill into the
+    two attention passes, as the library does: a pair is "dense" when every row
+    of its 16-row unit selected the block, else it is computed KV-outer.
+    Returns per-pass pair counts, algorithmic flops (4*d*hpg per attended key)
+    and the number of distinct (group, block) K/V blocks each pass touches.
+    sel: [G, n, k] int32 on the device (-1 = no selection)."""
+    ng, _, k = sel.shape
+    dev = sel.device
+    nb = (n + bk - 1) // bk
+    nunits = (n + 15) // 16
+    rows = torch.arange(n, device=dev)
+    unit_rows = torch.clamp(n - torch.arange(nunits, device=dev) * 16, max=16)
+    st = {"dense_pairs": 0, "sparse_pairs": 0, "F_dense": 0.0, "F_sparse": 0.0, "kv_dense": 0, "kv_sparse": 0}
+    for g in range(ng):
+        s = sel[g].long()
+        valid = s >= 0
+        rr = rows[:, None].expand(n, k)[valid]
+        bb = s[valid]
+        key = (rr // 16) * nb + bb
+        cnt = torch.bincount(key, minlength=nunits * nb).view(nunits, nb)
+        dense = (cnt == unit_rows[:, None]).view(-1)[key]
+        keys = torch.where(bb == rr // bk, rr % bk + 1, torch.full_like(rr, bk)).double()
+        fl = 4.0 * d * hpg * keys
+        st["F_dense"] += float(fl[dense].sum())
+        st["F_sparse"] += float(fl[~dense].sum())
+        st["dense_pairs"] += int(dense.sum())
+        st["sparse_pairs"] += int((~dense).sum())
+        st["kv_dense"] += int(torch.unique(bb[dense]).numel())
+        st["kv_sparse"] += int(torch.unique(bb[~dense]).numel())
+    return st
+
+
+def kernel_roofline(name, ms, flops, nbytes):
+    """Roofline position of one kernel: the bound is whichever of the MFMA
+    time (flops at the bf16 peak) and the HBM time (algorithmic bytes at the
+    HBM peak) is larger; achieved and frac are in that bound's unit."""
+    t = ms * 1e-3
+    mfma_bound = flops / (MFMA_PEAK_TFLOPS * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        ach, peak, unit = flops / t / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        ach, peak, unit = nbytes / t / 1e9, HBM_PEAK_GBS, "GB/s"
+    return {"kernel": name, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(ach, 2), "peak": peak,
+            "unit": unit, "frac": round(ach / peak, 4), "ms": round(ms, 4),
+            "algorithmic_tflop": round(flops / 1e12, 4), "algorithmic_gb": round(nbytes / 1e9, 4),
+            "tflops": round(flops / t / 1e12, 2), "GB/s": round(nbytes / t / 1e9, 1)}
+
+
 # ---- device inputs -----------------------------------------------------------
 
 def make_inputs(torch, dev):
@@ -215,11 +264,25 @@ def main():
     f_idx = index_flops_full(N_PREFILL)
     dbytes = decode_bytes(dec.ctx_lens)
     value = f_main / (pre_ms * 1e-3) / 1e12
-    attn_ms = float(pst[3] + pst[4])
-    attn_tflops = f_main / (attn_ms * 1e-3) / 1e12
-    t_main_ms = float(pst[2] + pst[3] + pst[4] + pst[5])
+    stage = dict(zip(msa.PREFILL_STAGES, (float(x) for x in pst)))
+    t_main_ms = stage["reverse_index"] + stage["kv_outer_attn"] + stage["dense_attn_merge"]
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
     dec_idx_bytes = sum((BK * ((L - 1) // BK) if (L - 1) // BK >= TOPK else 0) * DI * 2 for L in dec.ctx_lens)
+
+    # roofline of the two attention kernels from the actual selection
+    _, sel, _ = msa.prefill(*pre, topk=TOPK, workspace=ws_p, out=out_p, want_sel=True)
+    ps = pair_stats(torch, sel[0], N_PREFILL)
+    del sel
+    assert abs(ps["F_dense"] + ps["F_sparse"] - f_main) <= 1e-9 * f_main, "pair split does not cover F_main"
+    q_bytes = HQ // G * D * 2                     # one (query, group): 16 heads x 128 dims, bf16
+    part_bytes = q_bytes + HQ // G * 4            # normalised bf16 partial + fp32 lse per head
+    kv_block = 2 * BK * D * 2                     # K and V of one block of one group
+    b_kv = ps["sparse_pairs"] * (q_bytes + part_bytes) + ps["kv_sparse"] * kv_block
+    b_dm = (N_PREFILL * G * (2 * q_bytes + TOPK * 4) + ps["kv_dense"] * kv_block
+            + ps["sparse_pairs"] * part_bytes)
+    kernels = [kernel_roofline("k_attn_prefill (KV-outer)", stage["kv_outer_attn"], ps["F_sparse"], b_kv),
+               kernel_roofline("k_attn_dense (dense + merge)", stage["dense_attn_merge"], ps["F_dense"], b_dm)]
+    dom = max(kernels, key=lambda r: r["ms"])
 
     res = {
         "metric": METRIC,
@@ -240,7 +303,7 @@ def main():
         "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
         "prefill": {"ms": round(pre_ms, 4), "F_main_tflop": round(f_main / 1e12, 4),
                     "F_idx_tflop": round(f_idx / 1e12, 4),
-                    "stage_ms": {k: round(float(x), 4) for k, x in zip(msa.PREFILL_STAGES, pst)},
+                    "stage_ms": {k: round(x, 4) for k, x in stage.items()},
                     "main_branch_tflops": round(f_main / (t_main_ms * 1e-3) / 1e12, 2),
                     "end_to_end_tflops": round((f_main + f_idx) / (pre_ms * 1e-3) / 1e12, 2),
                     "index_tflops": round(f_idx / (float(pst[0]) * 1e-3) / 1e12, 2)},
@@ -248,9 +311,10 @@ def main():
                    "pct_of_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
                    "stage_ms": {k: round(float(x), 4) for k, x in zip(msa.DECODE_STAGES, dst)},
                    "index_GB/s": round(dec_idx_bytes / (float(dst[0]) * 1e-3) / 1e9, 1)},
-        "roofline": {"kernel": "k_attn_dense + k_attn_prefill", "bound": "mfma", "achieved": round(attn_tflops, 2),
-                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None},
+        "roofline": {"kernel": dom["kernel"], "bound": dom["bound"], "achieved": dom["achieved"],
+                     "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": None},
+        "kernels": kernels,
+        "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse")},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)

@@ -23,7 +23,7 @@ _STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_UNSUPPORTED",
 EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_decode_workspace_bytes", "msa_decode",
             "msa_prefill_profiled", "msa_decode_profiled", "msa_index_scores", "msa_select_blocks",
             "msa_status_string")
-PREFILL_STAGES = ("index_score", "select", "reverse_index", "dense_attn", "kv_outer_attn", "combine")
+PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
 DECODE_STAGES = ("index_score", "select", "attn", "combine")
 
 

@@ -3,7 +3,8 @@
 //
 // Prefill, per sequence and per window of up to kWindowMax query rows:
 //   index scores -> top-k selection -> reverse index + tile schedule ->
-//   persistent KV-outer attention -> combine.
+//   persistent KV-outer attention -> query-stationary attention over the
+//   unit-shared blocks, which merges the KV-outer partials (combine).
 // Windows bound the workspace (block scores and partials grow with the rows of
 // a window, not with the sequence), which is what makes 1M-token prefill fit.
 // Decode: index scores -> selection -> per-(sequence, group, slot) attention ->
@@ -82,7 +83,7 @@ struct PrefillLayout {
   int64_t nch, Lc, nblk, e_cap, tile_cap, slots;
   int64_t nunits;
   size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, part_o, part_lse, dense_cnt,
-      dense_list, dense_o, dense_lse, total;
+      dense_list, total;
 };
 
 bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
@@ -111,8 +112,6 @@ bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
   L->nunits = cdiv(L->W, 16);
   L->dense_cnt = off;  off += up((size_t)s.G * L->nunits * sizeof(int32_t));
   L->dense_list = off; off += up((size_t)s.G * L->nunits * s.k * sizeof(int32_t));
-  L->dense_o = off;    off += up((size_t)L->W * s.G * kHpg * kHeadDim * sizeof(uint16_t));
-  L->dense_lse = off;  off += up((size_t)L->W * s.G * kHpg * sizeof(float));
   L->total = off;
   return true;
 }
@@ -241,24 +240,19 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
                    at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist, nunits};
       launch_csr_and_tiles(ca, hs);
       clk.mark();
-      // 4. attention: query-stationary over unit-shared blocks, 5. then KV-outer
+      // 4. KV-outer attention over the pairs not shared by a whole unit
       uint16_t* ow = os + w0 * Hq * kHeadDim;
       float* lw = lses ? lses + w0 * Hq : nullptr;
-      LaunchAttnDense da{qs, ks, vs, dcnt, dlist, at<uint16_t>(workspace, L.dense_o),
-                         at<float>(workspace, L.dense_lse), ow, lw, N, w0, (int)Wn, nunits, G, K, s.scale_log2};
-      launch_attn_dense(da, hs);
-      clk.mark();
       LaunchAttnPrefill aa{qs, ks, vs, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
                            at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
                            at<float>(workspace, L.part_lse), N, w0, G, nbw, K, s.scale_log2,
                            (int)std::min<int64_t>(cu_count(), tile_cap)};
       launch_attn_prefill(aa, hs);
       clk.mark();
-      // 6. combine
-      LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse), selw, gstride, dcnt,
-                       dlist, at<uint16_t>(workspace, L.dense_o), at<float>(workspace, L.dense_lse), nunits,
-                       ow, lw, Wn, G, K, w0, nullptr};
-      launch_combine(cb, hs);
+      // 5. query-stationary attention over unit-shared blocks + merge
+      LaunchAttnDense da{qs, ks, vs, dcnt, dlist, selw, gstride, at<uint16_t>(workspace, L.part_o),
+                         at<float>(workspace, L.part_lse), ow, lw, N, w0, (int)Wn, nunits, G, K, s.scale_log2};
+      launch_attn_dense(da, hs);
       clk.mark();
     }
   }
@@ -303,7 +297,7 @@ msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_
   std::vector<hipEvent_t> ev;
   msa_status st = run_prefill(p, batch, seq_len, q, k, v, q_idx, k_idx, out, sel_out, lse_out, workspace,
                               workspace_bytes, stream, &ev);
-  return collect(ev, 6, stage_ms, st);
+  return collect(ev, 5, stage_ms, st);
 }
 
 size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx) {
@@ -351,9 +345,8 @@ msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const
                       at<float>(workspace, L.part_lse), max_ctx, batch, s.G, s.k, s.scale_log2};
   launch_attn_decode(aa, hs);
   clk.mark();
-  LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse), nullptr, 0, nullptr,
-                   nullptr, nullptr, nullptr, 0, static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, 0,
-                   ctx_lens};
+  LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse),
+                   static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, ctx_lens};
   launch_combine(cb, hs);
   clk.mark();
   return finish();

@@ -19,9 +19,9 @@
 // fragments feed the second contraction directly as its B operand (the key
 // order inside a 32-key step is permuted identically in V^T's A operand).
 // KV-outer outputs one softmax partial per (query, head, selected slot), o/l
-// rounded to bf16 plus lse2 = m*c + log2(l); the combine pass merges them
-// without atomics (two-phase combine [pnsm, section 7]). Causal masking is
-// needed only in the query's own block.
+// rounded to bf16 plus lse2 = m*c + log2(l); the dense pass, which runs after
+// it, merges them with its own state without atomics (two-phase combine
+// [pnsm, section 7]). Causal masking is needed only in the query's own block.
 //
 // K_b and V_b travel HBM -> LDS by direct LDS loads (global_load_lds, 16 bytes
 // per lane, no registers), double-buffered so the next block streams in while
@@ -231,18 +231,20 @@ __device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* s
   }
 }
 
-// Normalised O (bf16, [16 heads][128 d] at dst) and lse2 = m*c + log2(l) of
-// one query (c = scale*log2 e).
-__device__ __forceinline__ void store_normalised(const f32x4 (&o)[9], float m, float scale_log2,
-                                                 uint16_t* dst16x128, float* lse16) {
+// Softmax partial of one query, normalised, in fragment order: element (head
+// c, dim 16dt + 4qd + r) sits at dt*256 + (16qd + c)*4 + r of the 2048-element
+// slot, so each of the eight stores of a wave writes 512 contiguous bytes (the
+// reader uses the same lane mapping). lse2 = m*c + log2(l) per head (c = scale
+// * log2 e).
+__device__ __forceinline__ void store_partial(const f32x4 (&o)[9], float m, float scale_log2, uint16_t* dst,
+                                              float* lse16) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
   const float l = o[8][0];
   const float inv = 1.0f / l;
-  uint16_t* dst = dst16x128 + c * kHeadDim + 4 * qd;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
-    *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+    *reinterpret_cast<u32x2*>(dst + dt * 256 + lane * 4) = w;
   }
   if (qd == 0) lse16[c] = m * scale_log2 + __builtin_amdgcn_logf(l);
 }
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
       for (int n = 0; n < kAttnQN; ++n) {
         if (e0 + n < len) {
           const int64_t slot = ((int64_t)(cur[n] >> 4) * G + g) * topk + (cur[n] & 15);
-          store_normalised(qg.o[n], qg.m[n], scale_log2, part_o + slot * kHpg * kHeadDim, part_lse + slot * kHpg);
+          store_partial(qg.o[n], qg.m[n], scale_log2, part_o + slot * kHpg * kHeadDim, part_lse + slot * kHpg);
         }
       }
     }
@@ -348,17 +350,23 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   }
 }
 
-// Dense part: blocks selected by every query of a 16-query unit are computed
-// query-stationary (FlashAttention-style online softmax over the unit's shared
-// blocks; each block is staged once for all 16 queries, the next one streaming
-// into the other stage meanwhile). One workgroup of 8 waves per (unit, group),
-// two queries per wave. A unit whose every selected block is shared writes the
-// final output directly; otherwise its single partial is merged with the
-// KV-outer partials by the combine pass.
+// Dense part and final merge: blocks selected by every query of a 16-query
+// unit are computed query-stationary (FlashAttention-style online softmax over
+// the unit's shared blocks; each block is staged once for all 16 queries, the
+// next one streaming into the other stage meanwhile). One workgroup of 8 waves
+// per (unit, group), two queries per wave. The list always ends with the
+// unit's own block, the only one that needs the causal mask. This pass runs
+// after the KV-outer pass and merges its partials (the slots of the query's
+// selection that are not shared by the unit), so every row's output and lse
+// are written here, once, without atomics: with M = max over the dense state
+// and the partials of lse2 and w = 2^(lse2 - M),
+//   out = sum w o / sum w,   lse = (M + log2 sum w) * ln 2
+// (the second phase of the two-phase combine [pnsm, section 7]).
 __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ dense_cnt, const int32_t* __restrict__ dense_list, uint16_t* __restrict__ dense_o,
-    float* __restrict__ dense_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t n_tokens,
+    const int32_t* __restrict__ dense_cnt, const int32_t* __restrict__ dense_list,
+    const int32_t* __restrict__ sel, int64_t sel_gstride, const uint16_t* __restrict__ part_o,
+    const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t n_tokens,
     int64_t row0, int nrows, int nunits, int G, int topk, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
   lds_char* lds = (lds_char*)lds_raw;
@@ -367,14 +375,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
-  const int nd = dense_cnt[g * nunits + unit];
+  const int nd = dense_cnt[g * nunits + unit];  // >= 1: the unit's own block
   const int32_t* list = dense_list + ((int64_t)g * nunits + unit) * topk;
   const int i_rel0 = unit * 16 + wave * kAttnQN;
   const int b_loc = (int)((row0 + unit * 16) / kBlock);
-  const bool final_out = nd == min(topk, b_loc + 1);
+  const int nsel = min(topk, b_loc + 1);
 
-  if (nd > 0) {
-    const int64_t key0 = (int64_t)list[0] * kBlock;
+  // the list (<= 16 blocks) lives in lane j of every wave; block j is read
+  // back with a uniform readlane, so the loop never waits on a list load
+  const int lane_blk = lane < nd ? list[lane] : 0;
+  {
+    const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(lane_blk) * kBlock;
     stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
                 (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
   }
@@ -385,49 +396,106 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     load_q(qg, n, q + ((i * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
   }
   reset_state(qg);
-  // the list is ascending and always ends with the units' own block b_loc,
-  // the only one that needs the causal mask
-  for (int d = 0; d < nd; ++d) {
+  // shared older blocks (unmasked), then the unit's own block (masked)
+  for (int d = 0; d + 1 < nd; ++d) {
     wait_loads();
     __syncthreads();  // stage d&1 complete; stage (d+1)&1 free
-    if (d + 1 < nd) {
-      const int64_t k2 = (int64_t)list[d + 1] * kBlock;
-      stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim,
-                  rstride, (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
-    }
+    const int64_t k2 = (int64_t)__builtin_amdgcn_readlane(lane_blk, d + 1) * kBlock;
+    stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim, rstride,
+                (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
     const lds_char* stage = lds + (d & 1) * kStage;
     scores(qg, stage);
-    if (d + 1 < nd) {
-      softmax_pv<kAttnQN, false, false>(qg, stage, nullptr, scale_log2);
-    } else {
-      int lim[kAttnQN];
-#pragma unroll
-      for (int n = 0; n < kAttnQN; ++n)
-        lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
-      softmax_pv<kAttnQN, false, true>(qg, stage, lim, scale_log2);
-    }
+    softmax_pv<kAttnQN, false, false>(qg, stage, nullptr, scale_log2);
   }
+  {
+    wait_loads();
+    __syncthreads();
+    const lds_char* stage = lds + ((nd - 1) & 1) * kStage;
+    int lim[kAttnQN];
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
+    scores(qg, stage);
+    softmax_pv<kAttnQN, false, true>(qg, stage, lim, scale_log2);
+  }
+
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int i_rel = i_rel0 + n;
     if (i_rel >= nrows) continue;
-    if (final_out) {
-      const float l = qg.o[n][8][0];
-      const float inv = 1.0f / l;
-      uint16_t* dst = out + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
+    const float l_d = qg.o[n][8][0];
+    const float lse_d = qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l_d);
+    // slots of the selection not covered by the dense list: lane u < nsel
+    // tests its block, one ballot gives the (wave-uniform) mask
+    uint64_t use = 0ull;
+    if (nd < nsel) {
+      bool sparse = false;
+      if (lane < nsel) {
+        const int b = sel[(int64_t)g * sel_gstride + (int64_t)i_rel * topk + lane];
+        sparse = true;
+        for (int j = 0; j < nd; ++j) sparse &= (__builtin_amdgcn_readlane(lane_blk, j) != b);
+      }
+      use = __ballot(sparse);
+    }
+    const int64_t slot0 = ((int64_t)i_rel * G + g) * topk;
+    float lse_u[kMaxTopk];
+    float M = lse_d;
+#pragma unroll
+    for (int u = 0; u < kMaxTopk; ++u) {
+      lse_u[u] = -__builtin_inff();
+      if ((use >> u) & 1ull) lse_u[u] = part_lse[(slot0 + u) * kHpg + c];
+      M = fmaxf(M, lse_u[u]);
+    }
+    const float w_d = __builtin_amdgcn_exp2f(lse_d - M);
+    float wsum = w_d;
+#pragma unroll
+    for (int u = 0; u < kMaxTopk; ++u) {
+      lse_u[u] = __builtin_amdgcn_exp2f(lse_u[u] - M);  // weight; 0 for unused slots
+      wsum += lse_u[u];
+    }
+    f32x4 acc[8];
+    const float sd = w_d / l_d;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = qg.o[n][dt] * sd;
+    // partials two at a time (16 loads in flight per lane); the slot loop is
+    // wave-uniform
+    uint64_t rest = use;
+    while (rest) {
+      const int u0 = __builtin_ctzll(rest);
+      rest &= rest - 1;
+      const bool two = rest != 0ull;
+      const int u1 = two ? __builtin_ctzll(rest) : u0;
+      if (two) rest &= rest - 1;
+      const uint16_t* p0 = part_o + (slot0 + u0) * (kHpg * kHeadDim) + lane * 4;
+      const uint16_t* p1 = part_o + (slot0 + u1) * (kHpg * kHeadDim) + lane * 4;
+      u32x2 x0[8], x1[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        u32x2 w = {pack_bf16x2(qg.o[n][dt][0] * inv, qg.o[n][dt][1] * inv),
-                   pack_bf16x2(qg.o[n][dt][2] * inv, qg.o[n][dt][3] * inv)};
-        *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+        x0[dt] = *reinterpret_cast<const u32x2*>(p0 + dt * 256);
+        x1[dt] = *reinterpret_cast<const u32x2*>(p1 + dt * 256);
       }
-      if (lse_out && qd == 0)
-        lse_out[(int64_t)i_rel * Hq + g * kHpg + c] =
-            (qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
-    } else {
-      const int64_t row = (int64_t)i_rel * G + g;
-      store_normalised(qg.o[n], qg.m[n], scale_log2, dense_o + row * kHpg * kHeadDim, dense_lse + row * kHpg);
+      float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+      for (int u = 0; u < kMaxTopk; ++u) {
+        w0 = (u == u0) ? lse_u[u] : w0;
+        w1 = (two && u == u1) ? lse_u[u] : w1;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        acc[dt][0] += w0 * bf2f(x0[dt][0] & 0xffffu) + w1 * bf2f(x1[dt][0] & 0xffffu);
+        acc[dt][1] += w0 * bf2f(x0[dt][0] >> 16) + w1 * bf2f(x1[dt][0] >> 16);
+        acc[dt][2] += w0 * bf2f(x0[dt][1] & 0xffffu) + w1 * bf2f(x1[dt][1] & 0xffffu);
+        acc[dt][3] += w0 * bf2f(x0[dt][1] >> 16) + w1 * bf2f(x1[dt][1] >> 16);
+      }
     }
+    const float inv = 1.0f / wsum;
+    uint16_t* dst = out + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv), pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+    }
+    if (lse_out && qd == 0)
+      lse_out[(int64_t)i_rel * Hq + g * kHpg + c] = (M + __builtin_amdgcn_logf(wsum)) * 0.69314718055994530942f;
   }
 }
 
@@ -460,8 +528,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
   scores(qg, lds);
   softmax_pv<1, true, true>(qg, lds, lim, scale_log2);
-  store_normalised(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
-                   part_lse + (int64_t)item * kHpg);
+  store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
+                part_lse + (int64_t)item * kHpg);
 }
 
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
@@ -472,8 +540,8 @@ void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {
   if (a.nunits <= 0) return;
   hipLaunchKernelGGL(k_attn_dense, dim3(a.nunits, a.G), dim3(512), 0, st, a.q, a.k, a.v, a.dense_cnt, a.dense_list,
-                     a.dense_o, a.dense_lse, a.out, a.lse_out, a.n_tokens, a.row0, a.nrows, a.nunits, a.G, a.topk,
-                     a.scale_log2);
+                     a.sel, a.sel_gstride, a.part_o, a.part_lse, a.out, a.lse_out, a.n_tokens, a.row0, a.nrows,
+                     a.nunits, a.G, a.topk, a.scale_log2);
 }
 
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st) {

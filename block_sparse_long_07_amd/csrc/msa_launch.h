@@ -80,7 +80,7 @@ struct LaunchAttnPrefill {
   const int32_t* entries;
   const int32_t* tiles;
   int32_t* tile_info;
-  uint16_t* part_o;       // [slot][16][128] bf16, slot = (i_rel*G + g)*topk + u
+  uint16_t* part_o;       // [slot][2048] bf16 in fragment order, slot = (i_rel*G + g)*topk + u
   float* part_lse;        // [slot][16], log2 domain
   int64_t n_tokens, row0;
   int G, nbw, topk;
@@ -95,8 +95,10 @@ struct LaunchAttnDense {
   const uint16_t* v;
   const int32_t* dense_cnt;
   const int32_t* dense_list;
-  uint16_t* dense_o;      // [(i_rel*G + g)][16][128] bf16
-  float* dense_lse;       // [(i_rel*G + g)][16]
+  const int32_t* sel;     // sel[g*sel_gstride + i_rel*topk + u]
+  int64_t sel_gstride;
+  const uint16_t* part_o; // KV-outer partials, merged into the output here
+  const float* part_lse;
   uint16_t* out;          // window's first row
   float* lse_out;         // optional, window's first row
   int64_t n_tokens, row0;
@@ -119,22 +121,13 @@ struct LaunchAttnDecode {
 };
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st);
 
-struct LaunchCombine {
-  const uint16_t* part_o;
+struct LaunchCombine {   // decode
+  const uint16_t* part_o;  // [(s*G + g)*topk + u][2048] bf16, fragment order
   const float* part_lse;
-  // prefill only (null for decode): the unit-shared blocks and their partial
-  const int32_t* sel;     // sel[g*sel_gstride + rr*topk + u]
-  int64_t sel_gstride;
-  const int32_t* dense_cnt;
-  const int32_t* dense_list;
-  const uint16_t* dense_o;
-  const float* dense_lse;
-  int nunits;
-  uint16_t* out;          // row rr at out + rr*Hq*128
-  float* lse_out;         // optional, row rr at lse_out + rr*Hq
+  uint16_t* out;           // row s at out + s*Hq*128
+  float* lse_out;          // optional, row s at lse_out + s*Hq
   int64_t nrows;
   int G, topk;
-  int64_t row0;
   const int32_t* ctx_lens;
 };
 void launch_combine(const LaunchCombine& a, hipStream_t st);

@@ -26,8 +26,10 @@
  *   - All tensors are device pointers to contiguous row-major memory, 16-byte
  *     aligned; bf16 means IEEE bfloat16 stored as uint16.
  *   - The caller owns every buffer (inputs, outputs, workspace). The library
- *     never allocates, frees or synchronises; all work is enqueued on `stream`
- *     (a hipStream_t; NULL = the default stream) and the call returns at once.
+ *     never allocates or frees device memory; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and the call returns at once
+ *     (the *_profiled variants below are the exception: they create HIP
+ *     events and synchronise on them before returning).
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error status nothing has been launched. MSA_ERR_HIP reports a failed
  *     launch (hipGetLastError); asynchronous device faults surface at the
@@ -118,8 +120,9 @@ msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx,
  * on `stream` at every stage boundary. They synchronise on the last event and
  * return in stage_ms the duration of each stage, summed over sequences and
  * windows:
- *   prefill (6): index scores, top-k selection, reverse index + tile schedule,
- *                attention over unit-shared blocks, KV-outer attention, combine
+ *   prefill (5): index scores, top-k selection, reverse index + tile schedule,
+ *                KV-outer attention, attention over unit-shared blocks with
+ *                the merge of the KV-outer partials (combine)
  *   decode  (4): index scores, top-k selection, attention, combine
  * stage_ms must not be NULL (MSA_ERR_INVALID_ARG). */
 msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len,
