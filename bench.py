@@ -135,6 +135,41 @@ def kernel_roofline(name, ms, flops, nbytes):
             "tflops": round(flops / t / 1e12, 2), "GB/s": round(nbytes / t / 1e9, 1)}
 
 
+# ---- rocprofv3 summaries -------------------------------------------------------
+
+def summarize_rocprof(d):
+    """Text summary of rocprofv3 CSV output (kernel stats and per-dispatch
+    counters) for the msa kernels and the calibration kernel."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def keep(name):
+        return "msa::" in name or "neg_kernel" in name
+
+    lines = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        lines.append(f"## kernel stats ({os.path.basename(f)})")
+        lines.append(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>10s}")
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if keep(r["Name"]):
+                    lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                                 f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                                 f"{float(r['TotalDurationNs']) / 1e6:10.3f}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        lines.append(f"## counters per dispatch ({os.path.basename(f)})")
+        agg = defaultdict(list)
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if keep(r["Kernel_Name"]):
+                    agg[(r["Kernel_Name"][:60], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        for (name, ctr), vals in sorted(agg.items()):
+            lines.append(f"{name:60s} {ctr:14s} n={len(vals):3d} mean={np.mean(vals):.6g} "
+                         f"min={min(vals):.6g} max={max(vals):.6g}")
+    return "\n".join(lines)
+
+
 # ---- device inputs -----------------------------------------------------------
 
 def make_inputs(torch, dev):
@@ -197,8 +232,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--profile-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the run, stream 1 GiB through a plain elementwise kernel (torch.neg on int32, "
+                         "1 GiB read + 1 GiB written) to scale rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="no GPU work: condense the rocprofv3 CSV output under DIR to text and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -319,6 +362,13 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)
     print(json.dumps(res), flush=True)
+    if args.calibration_copy:
+        del ws_p, ws_d
+        src = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+        dst = torch.neg(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy done: 1 GiB read, 1 GiB written (neg kernel)")
 
 
 if __name__ == "__main__":

@@ -41,33 +41,40 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
-// LDS byte pointers stay in the local address space (32-bit addressing, no
-// generic-pointer checks)
-typedef __attribute__((address_space(3))) char lds_char;
+// LDS byte pointers (lds_char) stay in the local address space (32-bit
+// addressing, no generic-pointer checks)
 
 constexpr int kStage = 65536;  // bytes per staged block: K then V, 128 rows x 256 B each
 constexpr int kVOff = 32768;
 
-// Issue the direct-to-LDS loads of K_b and V_b (rows key0.., row stride
-// `rstride` elements) into one stage. Slot s (16 B) of the K half holds row
-// s/16, chunk (s%16) ^ (row & 15); of the V half, row s/16, 32-byte chunk
-// ((s%16)/2) ^ (row & 7), half (s%2). Rows at or past `nvalid` repeat the last
-// valid row, so every staged value is finite (those keys are masked).
-__device__ __forceinline__ void stage_block(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
-                                            int64_t rstride, int nvalid, int wave, int nwaves) {
+// Issue the direct-to-LDS loads of ROWS key rows of K and V (rows key0..,
+// row stride `rstride` elements) into one stage: K at the stage start, V at
+// VOFF. Slot s (16 B) of the K part holds row s/16, chunk (s%16) ^ (row & 15);
+// of the V part, row s/16, 32-byte chunk ((s%16)/2) ^ (row & 7), half (s%2).
+// Rows at or past `nvalid` repeat the last valid row, so every staged value is
+// finite (those keys are masked).
+template <int ROWS, int VOFF>
+__device__ __forceinline__ void stage_rows(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
+                                           int64_t rstride, int nvalid, int wave, int nwaves) {
   const int lane = threadIdx.x & 63;
-  for (int s0 = wave * 64; s0 < 2048; s0 += nwaves * 64) {
+  for (int s0 = wave * 64; s0 < ROWS * 16; s0 += nwaves * 64) {
     const int slot = s0 + lane;
     const int r = slot >> 4, p = slot & 15;
     const int64_t row = (int64_t)min(r, nvalid - 1) * rstride;
     const int ck = p ^ (r & 15);
     const int cv = (((p >> 1) ^ (r & 7)) << 1) | (p & 1);
-    __builtin_amdgcn_global_load_lds(kr0 + row + ck * 8, (lds_void*)(stage + s0 * 16), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vr0 + row + cv * 8, (lds_void*)(stage + kVOff + s0 * 16), 16, 0, 0);
+    lds_dma16(kr0 + row + ck * 8, stage + s0 * 16);
+    lds_dma16(vr0 + row + cv * 8, stage + VOFF + s0 * 16);
   }
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A whole block (128 keys) per stage.
+__device__ __forceinline__ void stage_block(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
+                                            int64_t rstride, int nvalid, int wave, int nwaves) {
+  stage_rows<kBlock, kVOff>(stage, kr0, vr0, rstride, nvalid, wave, nwaves);
+}
+
+__device__ __forceinline__ void wait_loads() { wait_vmcnt0(); }
 
 // K A-operand of key tile t, d-step st: lane (c, qd) holds K[16t + c][32st + 8qd .. +7].
 __device__ __forceinline__ bf16x8 lds_k(const lds_char* stage, int t, int st, int c, int qd) {
@@ -81,8 +88,9 @@ __device__ __forceinline__ bf16x8 lds_k(const lds_char* stage, int t, int st, in
 // read gives lane j of a 16-lane group element (4r + j/4, j%4) of the 16 x 4
 // matrix whose row i is the 4 elements addressed by lane i; lane i therefore
 // addresses row 32st + 4qd + i/4 (+16), dims 16dt + 4(i%4) .. +3.
+template <int VOFF>
 __device__ __forceinline__ bf16x8 lds_vt(const lds_char* stage, int dt, int st, int c, int qd) {
-  const lds_char* vb = stage + kVOff;
+  const lds_char* vb = stage + VOFF;
   const int r1 = 32 * st + 4 * qd + (c >> 2), r2 = r1 + 16;
   const int off = 8 * (c & 3);
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + r1 * 256 + ((dt ^ (r1 & 7)) << 5) + off));
@@ -91,39 +99,42 @@ __device__ __forceinline__ bf16x8 lds_vt(const lds_char* stage, int dt, int st, 
                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
 }
 
-// Per-wave state of QN queries (16 heads each) against staged blocks.
+// Per-wave state of QN queries (16 heads each) against staged blocks, which
+// are processed NT key tiles (16 keys each) at a time.
 //   qop: Q^T B-operands (4 steps over d); s: S^T / P^T fragments of the current
-//   block; o[0..7]: O^T accumulators (head = lane & 15, d = 16*dt + 4*(lane/16)
-//   + r); o[8]: every element is the softmax denominator of the lane's head
-//   (see softmax_pv); m: reference max of the raw scores per head.
-template <int QN>
+//   NT tiles; o[0..7]: O^T accumulators (head = lane & 15, d = 16*dt +
+//   4*(lane/16) + r); o[8]: every element is the softmax denominator of the
+//   lane's head (see softmax_pv); m: reference max of the raw scores per head.
+template <int QN, int NT>
 struct QueryGroup {
+  static constexpr int kQN = QN, kNT = NT;
   bf16x8 qop[QN][4];
-  f32x4 s[QN][8];
+  f32x4 s[QN][NT];
   f32x4 o[QN][9];
   float m[QN];
 };
 
-template <int QN>
-__device__ __forceinline__ void load_q(QueryGroup<QN>& qg, int n, const uint16_t* qrow) {
+template <class QG>
+__device__ __forceinline__ void load_q(QG& qg, int n, const uint16_t* qrow) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) qg.qop[n][st] = as_bf16x8(ld16(qrow + 32 * st));
 }
 
 // Running state before the first block: reference max -inf, zero accumulators.
-template <int QN>
-__device__ __forceinline__ void reset_state(QueryGroup<QN>& qg) {
+template <class QG>
+__device__ __forceinline__ void reset_state(QG& qg) {
 #pragma unroll
-  for (int n = 0; n < QN; ++n) {
+  for (int n = 0; n < QG::kQN; ++n) {
     qg.m[n] = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < 9; ++t) qg.o[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// S^T = K_b . Q^T for the QN queries.
-template <int QN>
-__device__ __forceinline__ void scores(QueryGroup<QN>& qg, const lds_char* stage_in) {
+// S^T = K_b . Q^T for key tiles t0 .. t0+NT-1 of the staged block.
+template <class QG>
+__device__ __forceinline__ void scores(QG& qg, const lds_char* stage_in, int t0) {
+  constexpr int QN = QG::kQN, NT = QG::kNT;
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
   // An opaque copy of the stage pointer keeps the K fragment reads inside the
   // query loop (otherwise they are hoisted across queries into many registers).
@@ -132,16 +143,16 @@ __device__ __forceinline__ void scores(QueryGroup<QN>& qg, const lds_char* stage
 #pragma unroll
   for (int n = 0; n < QN; ++n)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) qg.s[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // d-step outer, key tile inner: 8*QN independent accumulators between two
-  // dependent MFMAs, and the 8 operand reads of a step are issued together.
+    for (int t = 0; t < NT; ++t) qg.s[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // d-step outer, key tile inner: NT*QN independent accumulators between two
+  // dependent MFMAs, and the NT operand reads of a step are issued together.
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    bf16x8 a[8];
+    bf16x8 a[NT];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) a[t] = lds_k(stage, t, st, c, qd);
+    for (int t = 0; t < NT; ++t) a[t] = lds_k(stage, t0 + t, st, c, qd);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int n = 0; n < QN; ++n) qg.s[n][t] = mfma16x16x32(a[t], qg.qop[n][st], qg.s[n][t]);
   }
@@ -151,36 +162,41 @@ __device__ __forceinline__ void scores(QueryGroup<QN>& qg, const lds_char* stage
 // before the running state is rescaled to a new reference max.
 constexpr float kLazy = 8.0f;
 
-// Softmax update of the running state with the block's scores, then
-// O^T += V_b^T . P^T.
+// Softmax update of the running state with the scores of key tiles t0 ..
+// t0+NT-1 of the stage (tiles kt0 .. of the block: kt0 places them for the
+// causal mask), then O^T += V^T . P^T over those keys (V at VOFF).
 //  * The logit scale is folded into the exponent: p = 2^(s*c - m*c) (c = scale
 //    * log2 e), with the reference max m kept on raw scores.
-//  * FIRST: fresh state; m is this block's max and the accumulators start at 0.
-//    Otherwise the state is rescaled only when some head's block max exceeds
-//    its reference by more than kLazy/c (the rescale is exact: every term is
+//  * FIRST: fresh state; m is this part's max and the accumulators start at 0.
+//    Otherwise the state is rescaled only when some head's max exceeds its
+//    reference by more than kLazy/c (the rescale is exact: every term is
 //    multiplied by the same 2^((m_old - m_new) c)).
-//  * MASKED: the queries' own block; keys with index > lim[n] are masked.
+//  * MASKED: the queries' own block; keys with index > lim[n] are masked. A
+//    part whose keys are all masked leaves the state unchanged (its max is
+//    -inf), which needs an earlier part with a finite max (key 0 of the own
+//    block is never masked).
 //  * The denominator is accumulated by MFMA as a ninth O^T tile whose A operand
 //    is all ones, so it sums exactly the bf16-rounded P that enters P.V.
-template <int QN, bool FIRST, bool MASKED>
-__device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* stage_in, const int* lim,
-                                           float scale_log2) {
+template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG>
+__device__ __forceinline__ void softmax_pv(QG& qg, const lds_char* stage_in, const int* lim, float scale_log2,
+                                           int t0, int kt0) {
+  constexpr int QN = QG::kQN, NT = QG::kNT, NS = NT / 2;
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
   const lds_char* stage = stage_in;
   asm volatile("" : "+v"(stage));
-  bf16x8 pop[QN][4];
+  bf16x8 pop[QN][NS];
 #pragma unroll
   for (int n = 0; n < QN; ++n) {
     if (MASKED) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (16 * t + 4 * qd + r > lim[n]) qg.s[n][t][r] = -__builtin_inff();
+          if (16 * (kt0 + t) + 4 * qd + r > lim[n]) qg.s[n][t][r] = -__builtin_inff();
     }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < NT; ++t)
       mx = fmaxf(fmaxf(mx, fmaxf(qg.s[n][t][0], qg.s[n][t][1])), fmaxf(qg.s[n][t][2], qg.s[n][t][3]));
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
@@ -195,37 +211,38 @@ __device__ __forceinline__ void softmax_pv(QueryGroup<QN>& qg, const lds_char* s
     }
     const float mc = qg.m[n] * scale_log2;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         qg.s[n][t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(qg.s[n][t][r], scale_log2, -mc));
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int j = 0; j < NS; ++j) {
       u32x4 w;
-      w[0] = pack_bf16x2(qg.s[n][2 * st][0], qg.s[n][2 * st][1]);
-      w[1] = pack_bf16x2(qg.s[n][2 * st][2], qg.s[n][2 * st][3]);
-      w[2] = pack_bf16x2(qg.s[n][2 * st + 1][0], qg.s[n][2 * st + 1][1]);
-      w[3] = pack_bf16x2(qg.s[n][2 * st + 1][2], qg.s[n][2 * st + 1][3]);
-      pop[n][st] = as_bf16x8(w);
+      w[0] = pack_bf16x2(qg.s[n][2 * j][0], qg.s[n][2 * j][1]);
+      w[1] = pack_bf16x2(qg.s[n][2 * j][2], qg.s[n][2 * j][3]);
+      w[2] = pack_bf16x2(qg.s[n][2 * j + 1][0], qg.s[n][2 * j + 1][1]);
+      w[3] = pack_bf16x2(qg.s[n][2 * j + 1][2], qg.s[n][2 * j + 1][3]);
+      pop[n][j] = as_bf16x8(w);
     }
   }
   const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
   const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
   // key step outer, d tile inner (9*QN independent accumulators)
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
+  for (int j = 0; j < NS; ++j) {
+    const int st = t0 / 2 + j;
     bf16x8 a[9];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) a[dt] = lds_vt(stage, dt, st, c, qd);
+    for (int dt = 0; dt < 8; ++dt) a[dt] = lds_vt<VOFF>(stage, dt, st, c, qd);
     a[8] = ones;
 #pragma unroll
     for (int dt = 0; dt < 9; ++dt) {
 #pragma unroll
       for (int n = 0; n < QN; ++n) {
-        if (FIRST && st == 0)
-          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][st], (f32x4){0.f, 0.f, 0.f, 0.f});
+        if (FIRST && j == 0)
+          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][j], (f32x4){0.f, 0.f, 0.f, 0.f});
         else
-          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][st], qg.o[n][dt]);
+          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][j], qg.o[n][dt]);
       }
     }
   }
@@ -251,6 +268,7 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[9], float m, floa
 
 constexpr int kAttnQN = 2;
 constexpr int kAttnWaves = 8;
+constexpr int kAttnNT = 4;  // key tiles per softmax step (half a block)
 
 // Sparse (KV-outer) part: one persistent workgroup per CU drains the tile
 // queue. A query's own block is always shared by its whole 16-row unit, so no
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
                 (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
   }
-  QueryGroup<kAttnQN> qg;
+  QueryGroup<kAttnQN, kAttnNT> qg;
   int ent[kAttnQN];
   int e0 = wave * kAttnQN;
   // Q of the wave's current group; `have_q` says it is already loaded
@@ -319,10 +337,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const lds_char* stage = lds + (j & 1) * kStage;
     have_q = false;
     for (; e0 < len; e0 += kAttnWaves * kAttnQN) {
-      scores(qg, stage);
       int cur[kAttnQN];
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) cur[n] = ent[n];
+#pragma unroll
+      for (int t0 = 0; t0 < 8 - kAttnNT; t0 += kAttnNT) {
+        scores(qg, stage, t0);
+        if (t0 == 0)
+          softmax_pv<true, false>(qg, stage, nullptr, scale_log2, t0, t0);
+        else
+          softmax_pv<false, false>(qg, stage, nullptr, scale_log2, t0, t0);
+      }
+      scores(qg, stage, 8 - kAttnNT);
       // prefetch the wave's next group (in this tile, else the first of the next
       // tile) into the Q registers, which the scores no longer need
       const int e1 = e0 + kAttnWaves * kAttnQN;
@@ -332,7 +358,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
         fetch_group(nbegin, ng, nlen, wave * kAttnQN);
         have_q = true;
       }
-      softmax_pv<kAttnQN, true, false>(qg, stage, nullptr, scale_log2);
+      if (kAttnNT == 8)
+        softmax_pv<true, false>(qg, stage, nullptr, scale_log2, 0, 0);
+      else
+        softmax_pv<false, false>(qg, stage, nullptr, scale_log2, 8 - kAttnNT, 8 - kAttnNT);
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
         if (e0 + n < len) {
@@ -368,134 +397,264 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const int32_t* __restrict__ sel, int64_t sel_gstride, const uint16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t n_tokens,
     int64_t row0, int nrows, int nunits, int G, int topk, float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
+  // two K/V stages, then one 4 KiB partial slot per wave (160 KiB in all)
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage + kAttnWaves * 4096];
   lds_char* lds = (lds_char*)lds_raw;
   const int unit = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
-  const int nd = dense_cnt[g * nunits + unit];  // >= 1: the unit's own block
   const int32_t* list = dense_list + ((int64_t)g * nunits + unit) * topk;
   const int i_rel0 = unit * 16 + wave * kAttnQN;
   const int b_loc = (int)((row0 + unit * 16) / kBlock);
   const int nsel = min(topk, b_loc + 1);
 
-  // the list (<= 16 blocks) lives in lane j of every wave; block j is read
-  // back with a uniform readlane, so the loop never waits on a list load
-  const int lane_blk = lane < nd ? list[lane] : 0;
-  {
-    const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(lane_blk) * kBlock;
-    stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
-  }
-  QueryGroup<kAttnQN> qg;
+  // independent loads first: the unit's list (lane j holds entry j, read back
+  // with a uniform readlane; entries past the count are not used), its count,
+  // and the queries' Q
+  const int lane_blk = lane < topk ? list[lane] : 0;
+  const int nd = dense_cnt[g * nunits + unit];  // >= 1: the unit's own block
+  QueryGroup<kAttnQN, kAttnNT> qg;
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int64_t i = row0 + min(i_rel0 + n, nrows - 1);
     load_q(qg, n, q + ((i * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
   }
-  reset_state(qg);
-  // shared older blocks (unmasked), then the unit's own block (masked)
-  for (int d = 0; d + 1 < nd; ++d) {
-    wait_loads();
-    __syncthreads();  // stage d&1 complete; stage (d+1)&1 free
-    const int64_t k2 = (int64_t)__builtin_amdgcn_readlane(lane_blk, d + 1) * kBlock;
-    stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
-    const lds_char* stage = lds + (d & 1) * kStage;
-    scores(qg, stage);
-    softmax_pv<kAttnQN, false, false>(qg, stage, nullptr, scale_log2);
-  }
   {
-    wait_loads();
-    __syncthreads();
-    const lds_char* stage = lds + ((nd - 1) & 1) * kStage;
-    int lim[kAttnQN];
-#pragma unroll
-    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
-    scores(qg, stage);
-    softmax_pv<kAttnQN, false, true>(qg, stage, lim, scale_log2);
+    const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(lane_blk) * kBlock;
+    stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
+                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
   }
-
+  // slots of each query's selection not covered by the dense list (computed
+  // KV-outer): lane u < nsel tests its block, a ballot gives the wave-uniform
+  // mask
+  uint64_t use[kAttnQN];
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int i_rel = i_rel0 + n;
-    if (i_rel >= nrows) continue;
-    const float l_d = qg.o[n][8][0];
-    const float lse_d = qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l_d);
-    // slots of the selection not covered by the dense list: lane u < nsel
-    // tests its block, one ballot gives the (wave-uniform) mask
-    uint64_t use = 0ull;
-    if (nd < nsel) {
+    use[n] = 0ull;
+    if (i_rel < nrows && nd < nsel) {
       bool sparse = false;
       if (lane < nsel) {
         const int b = sel[(int64_t)g * sel_gstride + (int64_t)i_rel * topk + lane];
         sparse = true;
         for (int j = 0; j < nd; ++j) sparse &= (__builtin_amdgcn_readlane(lane_blk, j) != b);
       }
-      use = __ballot(sparse);
+      use[n] = __ballot(sparse);
     }
-    const int64_t slot0 = ((int64_t)i_rel * G + g) * topk;
-    float lse_u[kMaxTopk];
-    float M = lse_d;
+  }
+  reset_state(qg);
+
+  // KV-outer partials of the wave's queries, in (query, slot) order. One at a
+  // time streams into the wave's slot while a dense block is computed and is
+  // merged into the running state after it; the rest go through the two
+  // larger regions after the last block (below).
+  lds_char* pslot = lds + 2 * kStage + wave * 4096;
+  int cur_n = 0;
+  uint64_t cur_rem = use[0];
+  auto next_pair = [&](int& pn, int64_t& slot) -> bool {
 #pragma unroll
-    for (int u = 0; u < kMaxTopk; ++u) {
-      lse_u[u] = -__builtin_inff();
-      if ((use >> u) & 1ull) lse_u[u] = part_lse[(slot0 + u) * kHpg + c];
-      M = fmaxf(M, lse_u[u]);
-    }
-    const float w_d = __builtin_amdgcn_exp2f(lse_d - M);
-    float wsum = w_d;
+    for (int n = 1; n < kAttnQN; ++n)
+      if (cur_rem == 0ull && cur_n == n - 1) {
+        cur_n = n;
+        cur_rem = use[n];
+      }
+    if (cur_rem == 0ull) return false;
+    const int pu = __builtin_ctzll(cur_rem);
+    cur_rem &= cur_rem - 1;
+    pn = cur_n;
+    slot = ((int64_t)(i_rel0 + cur_n) * G + g) * topk + pu;
+    return true;
+  };
+  int pend_n = -1;       // query of the partial in the slot (-1: none)
+  float pend_lse = 0.f;  // its lse2 for the lane's head
+  auto issue_slot = [&]() {
+    int pn = 0;
+    int64_t slot = 0;
+    pend_n = -1;
+    if (!next_pair(pn, slot)) return;
+    const uint16_t* src = part_o + slot * (kHpg * kHeadDim);
 #pragma unroll
-    for (int u = 0; u < kMaxTopk; ++u) {
-      lse_u[u] = __builtin_amdgcn_exp2f(lse_u[u] - M);  // weight; 0 for unused slots
-      wsum += lse_u[u];
-    }
-    f32x4 acc[8];
-    const float sd = w_d / l_d;
+    for (int j = 0; j < 4; ++j) lds_dma16(src + j * 512 + lane * 8, pslot + j * 1024);
+    pend_lse = part_lse[slot * kHpg + c];
+    pend_n = pn;
+  };
+  // merge of a normalised partial (o_p, lse2 lp) into the running state
+  // (o, l = o[8], reference max m): it adds o_p * w and w, w = 2^(lp - m*c),
+  // after a lazy rescale of the state when lp exceeds m*c by more than kLazy
+  // (a fresh state has m = -inf and takes m*c = lp)
+  auto merge_slot = [&]() {
+    if (pend_n < 0) return;
+    u32x2 x[8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] = qg.o[n][dt] * sd;
-    // partials two at a time (16 loads in flight per lane); the slot loop is
-    // wave-uniform
-    uint64_t rest = use;
-    while (rest) {
-      const int u0 = __builtin_ctzll(rest);
-      rest &= rest - 1;
-      const bool two = rest != 0ull;
-      const int u1 = two ? __builtin_ctzll(rest) : u0;
-      if (two) rest &= rest - 1;
-      const uint16_t* p0 = part_o + (slot0 + u0) * (kHpg * kHeadDim) + lane * 4;
-      const uint16_t* p1 = part_o + (slot0 + u1) * (kHpg * kHeadDim) + lane * 4;
-      u32x2 x0[8], x1[8];
+    for (int dt = 0; dt < 8; ++dt)
+      x[dt] = *(const __attribute__((address_space(3))) u32x2*)(pslot + dt * 512 + lane * 8);
+    const float lp = pend_lse;
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) {
+      if (pend_n != n) continue;  // wave-uniform; every access below has a constant index
+      float mc = qg.m[n] * scale_log2;
+      if (__any(lp - mc > kLazy)) {
+        const float mnew = fmaxf(mc, lp);
+        const float alpha = __builtin_amdgcn_exp2f(mc - mnew);
+#pragma unroll
+        for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha;
+        qg.m[n] = mnew / scale_log2;
+        mc = qg.m[n] * scale_log2;
+      }
+      const float w = __builtin_amdgcn_exp2f(lp - mc);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        x0[dt] = *reinterpret_cast<const u32x2*>(p0 + dt * 256);
-        x1[dt] = *reinterpret_cast<const u32x2*>(p1 + dt * 256);
+        qg.o[n][dt][0] += w * bf2f(x[dt][0] & 0xffffu);
+        qg.o[n][dt][1] += w * bf2f(x[dt][0] >> 16);
+        qg.o[n][dt][2] += w * bf2f(x[dt][1] & 0xffffu);
+        qg.o[n][dt][3] += w * bf2f(x[dt][1] >> 16);
       }
-      float w0 = 0.f, w1 = 0.f;
+      qg.o[n][8] += w;
+    }
+    wait_lgkmcnt0();  // slot read out before it is refilled
+  };
+  issue_slot();
+
+  // shared older blocks (unmasked), then the unit's own block (masked)
+  for (int d = 0; d + 1 < nd; ++d) {
+    wait_loads();
+    __syncthreads();  // stage d&1 and the slot complete; stage (d+1)&1 free
+    const int64_t k2 = (int64_t)__builtin_amdgcn_readlane(lane_blk, d + 1) * kBlock;
+    stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim, rstride,
+                (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
+    const lds_char* stage = lds + (d & 1) * kStage;
 #pragma unroll
-      for (int u = 0; u < kMaxTopk; ++u) {
-        w0 = (u == u0) ? lse_u[u] : w0;
-        w1 = (two && u == u1) ? lse_u[u] : w1;
-      }
+    for (int t0 = 0; t0 < 8; t0 += kAttnNT) {
+      scores(qg, stage, t0);
+      softmax_pv<false, false>(qg, stage, nullptr, scale_log2, t0, t0);
+    }
+    merge_slot();
+    issue_slot();
+  }
+
+  // The remaining partials stream through two 8 KiB LDS regions of the wave
+  // (two partials each, direct-to-LDS loads, their lse into the wave's slot):
+  // region 0 in the stage not holding the last block, filled while the last
+  // block is computed; region 1 in the last block's stage once every wave is
+  // done with it. Completion is tracked with vmcnt (5 loads per partial), so
+  // one region is merged while the other streams in.
+  const int last = (nd - 1) & 1;
+  lds_char* region[2] = {lds + (last ^ 1) * kStage + wave * 8192, lds + last * kStage + wave * 8192};
+  lds_char* lse_side = pslot;  // [region][partial][16 heads] fp32
+  auto issue_round = [&](int reg, int& cnt, int& na, int& nb) {
+    cnt = 0;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        acc[dt][0] += w0 * bf2f(x0[dt][0] & 0xffffu) + w1 * bf2f(x1[dt][0] & 0xffffu);
-        acc[dt][1] += w0 * bf2f(x0[dt][0] >> 16) + w1 * bf2f(x1[dt][0] >> 16);
-        acc[dt][2] += w0 * bf2f(x0[dt][1] & 0xffffu) + w1 * bf2f(x1[dt][1] & 0xffffu);
-        acc[dt][3] += w0 * bf2f(x0[dt][1] >> 16) + w1 * bf2f(x1[dt][1] >> 16);
+    for (int p = 0; p < 2; ++p) {
+      int pn = 0;
+      int64_t slot = 0;
+      if (!next_pair(pn, slot)) break;
+      const uint16_t* src = part_o + slot * (kHpg * kHeadDim);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lds_dma16(src + j * 512 + lane * 8, region[reg] + p * 4096 + j * 1024);
+      if (lane < kHpg) lds_dma4(part_lse + slot * kHpg + lane, lse_side + reg * 128 + p * 64);
+      if (p == 0) na = pn; else nb = pn;
+      cnt = p + 1;
+    }
+  };
+  auto wait_round = [](int cnt_in_flight) {
+    if (cnt_in_flight == 2)
+      wait_vmcnt10();
+    else if (cnt_in_flight == 1)
+      wait_vmcnt5();
+    else
+      wait_vmcnt0();
+  };
+  int cA = 0, nA0 = 0, nA1 = 0, cB = 0, nB0 = 0, nB1 = 0;
+  {
+    wait_loads();
+    __syncthreads();
+    merge_slot();  // frees the slot for the lse of the rounds
+    issue_round(0, cA, nA0, nA1);
+    const lds_char* stage = lds + last * kStage;
+    int lim[kAttnQN];
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
+#pragma unroll
+    for (int t0 = 0; t0 < 8; t0 += kAttnNT) {
+      scores(qg, stage, t0);
+      softmax_pv<false, true>(qg, stage, lim, scale_log2, t0, t0);
+    }
+  }
+  // merge state per query: o = normalised output so far, M its lse2, wsum
+  // the weight sum relative to M (the dense state has weight 1 at its lse2)
+  float M[kAttnQN], wsum[kAttnQN];
+#pragma unroll
+  for (int n = 0; n < kAttnQN; ++n) {
+    const float l_d = qg.o[n][8][0];
+    M[n] = qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l_d);
+    wsum[n] = 1.0f;
+    const float inv = 1.0f / l_d;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) qg.o[n][dt] *= inv;
+  }
+  auto merge_round = [&](int reg, int cnt, int na, int nb) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p >= cnt) break;
+      const int pn = p ? nb : na;
+      u32x2 x[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        x[dt] = *(const __attribute__((address_space(3))) u32x2*)(region[reg] + p * 4096 + dt * 512 + lane * 8);
+      const float lp = *(const __attribute__((address_space(3))) float*)(lse_side + reg * 128 + p * 64 + c * 4);
+      // both queries are updated, the other one with (scale 1, weight 0): a
+      // branch on pn would let the compiler index the accumulators dynamically
+#pragma unroll
+      for (int n = 0; n < kAttnQN; ++n) {
+        const bool mine = pn == n;
+        const float mn = mine ? fmaxf(M[n], lp) : M[n];
+        const float s_old = mine ? __builtin_amdgcn_exp2f(M[n] - mn) : 1.0f;
+        const float w = mine ? __builtin_amdgcn_exp2f(lp - mn) : 0.0f;
+        M[n] = mn;
+        wsum[n] = wsum[n] * s_old + w;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          qg.o[n][dt][0] = qg.o[n][dt][0] * s_old + w * bf2f(x[dt][0] & 0xffffu);
+          qg.o[n][dt][1] = qg.o[n][dt][1] * s_old + w * bf2f(x[dt][0] >> 16);
+          qg.o[n][dt][2] = qg.o[n][dt][2] * s_old + w * bf2f(x[dt][1] & 0xffffu);
+          qg.o[n][dt][3] = qg.o[n][dt][3] * s_old + w * bf2f(x[dt][1] >> 16);
+        }
       }
     }
-    const float inv = 1.0f / wsum;
+    wait_lgkmcnt0();  // region read out before it is refilled
+  };
+  wait_lgkmcnt0();  // the last block's stage is free
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  issue_round(1, cB, nB0, nB1);
+  // rounds alternate regions; pairs are handed out in order, so an empty
+  // round means every later round is empty too
+  while (cA > 0) {
+    wait_round(cB);
+    merge_round(0, cA, nA0, nA1);
+    issue_round(0, cA, nA0, nA1);
+    if (cB == 0) break;
+    wait_round(cA);
+    merge_round(1, cB, nB0, nB1);
+    issue_round(1, cB, nB0, nB1);
+  }
+#pragma unroll
+  for (int n = 0; n < kAttnQN; ++n) {
+    const int i_rel = i_rel0 + n;
+    if (i_rel >= nrows) continue;
+    const float inv = 1.0f / wsum[n];
     uint16_t* dst = out + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv), pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+      u32x2 w = {pack_bf16x2(qg.o[n][dt][0] * inv, qg.o[n][dt][1] * inv),
+                 pack_bf16x2(qg.o[n][dt][2] * inv, qg.o[n][dt][3] * inv)};
       *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
     }
     if (lse_out && qd == 0)
-      lse_out[(int64_t)i_rel * Hq + g * kHpg + c] = (M + __builtin_amdgcn_logf(wsum)) * 0.69314718055994530942f;
+      lse_out[(int64_t)i_rel * Hq + g * kHpg + c] = (M[n] + __builtin_amdgcn_logf(wsum[n])) * 0.69314718055994530942f;
   }
 }
 
@@ -520,14 +679,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   const int Hq = G * kHpg;
   const int64_t base = ((int64_t)sq * max_ctx * G + key0 * G + g) * kHeadDim;
   stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(kBlock, max_ctx - key0), wave, 4);
-  QueryGroup<1> qg;
+  QueryGroup<1, 8> qg;
   if (wave == 0) load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
   wait_loads();
   __syncthreads();
   if (wave != 0) return;
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
-  scores(qg, lds);
-  softmax_pv<1, true, true>(qg, lds, lim, scale_log2);
+  scores(qg, lds, 0);
+  softmax_pv<true, true>(qg, lds, lim, scale_log2, 0, 0);
   store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                 part_lse + (int64_t)item * kHpg);
 }
@@ -539,7 +698,7 @@ void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
 
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {
   if (a.nunits <= 0) return;
-  hipLaunchKernelGGL(k_attn_dense, dim3(a.nunits, a.G), dim3(512), 0, st, a.q, a.k, a.v, a.dense_cnt, a.dense_list,
+  hipLaunchKernelGGL(k_attn_dense, dim3(a.nunits, a.G), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v, a.dense_cnt, a.dense_list,
                      a.sel, a.sel_gstride, a.part_o, a.part_lse, a.out, a.lse_out, a.n_tokens, a.row0, a.nrows,
                      a.nunits, a.G, a.topk, a.scale_log2);
 }

@@ -25,7 +25,6 @@ namespace msa {
 // position x ^ ((r >> 1) & 7), which keeps the operand reads conflict-free.
 constexpr int kKC = 8;
 
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
@@ -37,7 +36,7 @@ __device__ __forceinline__ void stage_kidx(lds_char* dst, const uint16_t* src_ro
     const int slot = s0 + lane;
     const int r = slot >> 3, p = slot & 7;
     const int x = p ^ ((r >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(src_rows + r * kIndexDim + x * 8, (lds_void*)(dst + s0 * 16), 16, 0, 0);
+    lds_dma16(src_rows + r * kIndexDim + x * 8, dst + s0 * 16);
   }
 }
 
@@ -74,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
   }
 
   for (int kb = kb0; kb < kb1; ++kb) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt0();
     __syncthreads();  // block kb staged; the other stage is free
     if (kb + 1 < kb1)
       stage_kidx(lds + ((kb + 1 - kb0) & 1) * 16384, k_idx + (int64_t)(kb + 1) * kBlock * kIndexDim, wave);

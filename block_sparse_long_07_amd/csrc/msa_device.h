@@ -30,6 +30,42 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_b
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Direct global -> LDS loads (no registers): lane L's SIZE bytes from src land
+// at lds + SIZE*L, lds being the same for the whole wave. They are written as
+// inline assembly because the compiler, unable to tell which LDS bytes such a
+// load writes, would otherwise wait for every one of them before any later
+// LDS read, which serialises double buffering. The caller therefore waits
+// itself (s_waitcnt vmcnt, plus a barrier when other waves read the data).
+// Every wait on them must be an s_waitcnt the compiler sees (the builtins
+// below): a wait the compiler cannot see leaves it assuming older loads are
+// still in flight, and its own vmcnt(0) before their first use would then
+// also wait for the LDS loads.
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+// s_waitcnt through the builtin (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8), so that the compiler's own wait tracking knows
+// about it.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmcnt5() { __builtin_amdgcn_s_waitcnt(0x0F75); }
+__device__ __forceinline__ void wait_vmcnt10() { __builtin_amdgcn_s_waitcnt(0x0F7A); }
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ void lds_dma16(const void* src, const lds_char* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, const lds_char* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
