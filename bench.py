@@ -119,6 +119,26 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
     return st
 
 
+# HBM traffic per launch of the attention kernels on this workload, from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB calibration kernel
+# (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
+# were taken on: keyed by the hash that source_hash() computes.
+MEASURED_TRAFFIC = {
+    "source": "d442bfc635342f3d",
+    "k_attn_prefill (KV-outer)": 7.905e9,
+    "k_attn_dense (dense + merge)": 5.684e9,
+}
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn.hip", "msa_device.h", "msa_launch.h"):
+        with open(os.path.join(ROOT, "block_sparse_long_07_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def kernel_roofline(name, ms, flops, nbytes):
     """Roofline position of one kernel: the bound is whichever of the MFMA
     time (flops at the bf16 peak) and the HBM time (algorithmic bytes at the
@@ -129,8 +149,9 @@ def kernel_roofline(name, ms, flops, nbytes):
         ach, peak, unit = flops / t / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s"
     else:
         ach, peak, unit = nbytes / t / 1e9, HBM_PEAK_GBS, "GB/s"
+    traffic = MEASURED_TRAFFIC.get(name) if MEASURED_TRAFFIC["source"] == source_hash() else None
     return {"kernel": name, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(ach, 2), "peak": peak,
-            "unit": unit, "frac": round(ach / peak, 4), "ms": round(ms, 4),
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": traffic, "ms": round(ms, 4),
             "algorithmic_tflop": round(flops / 1e12, 4), "algorithmic_gb": round(nbytes / 1e9, 4),
             "tflops": round(flops / t / 1e12, 2), "GB/s": round(nbytes / t / 1e9, 1)}
 
@@ -355,7 +376,9 @@ def main():
                    "stage_ms": {k: round(float(x), 4) for k, x in zip(msa.DECODE_STAGES, dst)},
                    "index_GB/s": round(dec_idx_bytes / (float(dst[0]) * 1e-3) / 1e9, 1)},
         "roofline": {"kernel": dom["kernel"], "bound": dom["bound"], "achieved": dom["achieved"],
-                     "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": None},
+                     "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": dom["traffic"],
+                     "traffic_unit": "HBM bytes per launch (rocprofv3, calibrated)",
+                     "algorithmic_bytes": round(dom["algorithmic_gb"] * 1e9)},
         "kernels": kernels,
         "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse")},
     }
