@@ -80,6 +80,7 @@ int64_t entries_in(int64_t a, int64_t b, int G, int k) {
 struct PrefillLayout {
   int64_t W;  // window rows
   int nb;     // blocks of the sequence
+  int nbs;    // row stride of the pooled scores (nb rounded up to 4: 16-byte aligned rows)
   int64_t nch, Lc, nblk, e_cap, tile_cap, slots;
   int64_t nunits;
   size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, part_o, part_lse, dense_cnt,
@@ -89,6 +90,7 @@ struct PrefillLayout {
 bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
   if (N <= 0 || N > kMaxSeq) return false;
   L->nb = (int)cdiv(N, kBlock);
+  L->nbs = (L->nb + 3) & ~3;
   L->W = std::min<int64_t>(cdiv(N, kBlock) * kBlock, kWindowMax);
   L->nch = cdiv(L->W, 64);
   L->Lc = (int64_t)s.G * L->nb * L->nch;
@@ -98,7 +100,7 @@ bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
   L->tile_cap = cdiv(L->e_cap, kTileQ) + (int64_t)s.G * L->nb;
   L->slots = L->W * s.G * s.k;
   size_t off = 0;
-  L->sblk = off;       off += up((size_t)L->W * s.G * L->nb * sizeof(float));
+  L->sblk = off;       off += up((size_t)L->W * s.G * L->nbs * sizeof(float));
   L->sel = off;        off += up((size_t)L->W * s.G * s.k * sizeof(int32_t));
   L->chunkcnt = off;   off += up((size_t)L->Lc * sizeof(int32_t));
   L->chunkoff = off;   off += up((size_t)(L->Lc + 1) * sizeof(int32_t));
@@ -218,13 +220,13 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
       clk.mark();
       // 1. index scores for query blocks that have more than k-1 older blocks
       LaunchIndexPrefill ia{qis, kis, at<float>(workspace, L.sblk), N, w0,
-                            (int)std::max<int64_t>(K, w0 / kBlock), nbw, L.nb, G};
+                            (int)std::max<int64_t>(K, w0 / kBlock), nbw, L.nbs, G};
       launch_index_prefill(ia, hs);
       clk.mark();
       // 2. top-k selection
       int32_t* selw = sels ? sels + w0 * K : at<int32_t>(workspace, L.sel);
       const int64_t gstride = sels ? N * K : L.W * K;
-      LaunchSelect sa{at<float>(workspace, L.sblk), L.nb, selw, gstride, K, Wn, G, K, w0, nullptr};
+      LaunchSelect sa{at<float>(workspace, L.sblk), L.nbs, selw, gstride, K, Wn, G, K, w0, nullptr};
       launch_select(sa, hs);
       clk.mark();
       // 3. reverse index and tile schedule

@@ -72,6 +72,15 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
     }
   }
 
+  // pooled scores of the chunk: lane group qd keeps the rows of tiles rt = qd
+  // (mod 4), eight blocks each, and writes them as one 32-byte run per row
+  float res[(RT + 3) / 4][kKC];
+#pragma unroll
+  for (int j = 0; j < (RT + 3) / 4; ++j)
+#pragma unroll
+    for (int x = 0; x < kKC; ++x) res[j][x] = -__builtin_inff();
+
+#pragma unroll 1
   for (int kb = kb0; kb < kb1; ++kb) {
     wait_vmcnt0();
     __syncthreads();  // block kb staged; the other stage is free
@@ -101,11 +110,28 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
       mx[rt] = fmaxf(mx[rt], shfl_xor_f(mx[rt], 16));
       mx[rt] = fmaxf(mx[rt], shfl_xor_f(mx[rt], 32));
     }
-    // all four lane groups now hold the block maxima; group qd stores tiles rt = qd mod 4
+    // all four lane groups now hold the block maxima; group qd keeps tiles rt = qd mod 4
+    const int x = kb - kb0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int64_t row = flat0 + rt * 16 + c;
-      if ((rt & 3) == qd && row < flat_end) sblk[(row - row0 * G) * nb + kb] = mx[rt];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int xx = 0; xx < kKC; ++xx)
+        if ((rt & 3) == qd && xx == x) res[rt >> 2][xx] = mx[rt];
+  }
+  const int nkb = kb1 - kb0;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t row = flat0 + rt * 16 + c;
+    if ((rt & 3) != qd || row >= flat_end) continue;
+    float* dst = sblk + (row - row0 * G) * nb + kb0;
+    const float* rv = res[rt >> 2];
+    if (nkb == kKC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<f32x4*>(dst) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){rv[4], rv[5], rv[6], rv[7]};
+    } else {
+#pragma unroll
+      for (int xx = 0; xx < kKC; ++xx)
+        if (xx < nkb) dst[xx] = rv[xx];
     }
   }
 }

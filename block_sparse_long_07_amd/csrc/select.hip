@@ -7,14 +7,16 @@
 // evaluated; the specialised small-k register top-k follows the pages' kernel
 // choice of a per-thread register list for small k [pnsm, section 7].
 //
-// One lane per row: the candidates b = 0..b_loc-1 are streamed in ascending
-// order through an LDS tile (64 rows x 64 candidates, loaded coalesced), and
-// each lane keeps its row's best k-1 (score, index) pairs in registers, sorted
-// by (score descending, index ascending). A candidate enters only if it is
-// strictly greater than the current (k-1)-th score and is placed after every
-// equal score; since candidates arrive in ascending index order, among equal
-// scores the lowest indices are kept. The chosen indices are sorted ascending at the
-// end and written with b_loc last and -1 padding.
+// Many rows (prefill): 16 lanes per row, 4 rows per wave. Lane s of a row
+// ranks the candidates b = s, s+16, ... < b_loc in ascending order and keeps
+// its best k-1 (score, index) pairs in registers, sorted by (score descending,
+// index ascending): a candidate enters only if it is strictly greater than
+// the current (k-1)-th score and is placed after every equal score, so among
+// equal scores the lowest indices are kept. The 16 lane lists of a row are
+// then merged by k-1 rounds of a row-wide arg-max over the list heads (DPP
+// shifts inside the 16-lane row; ties to the lower index), the winning lane
+// popping its head. The chosen indices are sorted ascending and written with
+// b_loc last and -1 padding.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -22,50 +24,58 @@ namespace msa {
 
 constexpr int64_t kWaveRowsMax = 16384;
 
+__device__ __forceinline__ float dpp_shr_f(float x, int n) {
+  // row_shr:n within 16-lane rows; lanes with no source keep x
+  switch (n) {
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x111, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x112, 0xF, 0xF, false));
+    case 4: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x114, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x118, 0xF, 0xF, false));
+  }
+}
+__device__ __forceinline__ int dpp_shr_i(int x, int n) {
+  switch (n) {
+    case 1: return __builtin_amdgcn_update_dpp(x, x, 0x111, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(x, x, 0x112, 0xF, 0xF, false);
+    case 4: return __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(x, x, 0x118, 0xF, 0xF, false);
+  }
+}
+
 template <int KM1>
-__global__ __launch_bounds__(64) void k_select(const float* __restrict__ sblk, int nb,
-                                               int32_t* __restrict__ sel, int64_t sel_gstride,
-                                               int64_t sel_rstride, int64_t nrows, int G, int64_t row0,
-                                               const int32_t* __restrict__ ctx_lens) {
-  __shared__ float tile[64][65];
-  const int lane = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const int64_t r = r0 + lane;
+__global__ __launch_bounds__(256) void k_select(const float* __restrict__ sblk, int nb,
+                                                int32_t* __restrict__ sel, int64_t sel_gstride,
+                                                int64_t sel_rstride, int64_t nrows, int G, int64_t row0,
+                                                const int32_t* __restrict__ ctx_lens) {
+  const int s = threadIdx.x & 15;
+  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   const bool valid = r < nrows * G;
   const int64_t rr = valid ? r / G : 0;
   const int g = valid ? (int)(r % G) : 0;
   int b_loc = 0;
   if (valid) b_loc = ctx_lens ? (ctx_lens[rr] - 1) / kBlock : (int)((row0 + rr) / kBlock);
-  // candidates this lane must rank (0 when every older block is taken anyway)
+  // candidates this row must rank (0 when every older block is taken anyway)
   const int need = (KM1 > 0 && valid && b_loc > KM1) ? b_loc : 0;
-  int maxneed = need;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) maxneed = max(maxneed, __shfl_xor(maxneed, m, 64));
 
   float v[KM1 > 0 ? KM1 : 1];
   int id[KM1 > 0 ? KM1 : 1];
 #pragma unroll
   for (int t = 0; t < KM1; ++t) {
     v[t] = -__builtin_inff();
-    id[t] = -1;
+    id[t] = 0x7fffffff;
   }
-
-  for (int c0 = 0; c0 < maxneed; c0 += 64) {
-    // cooperative, coalesced staging of 64 rows x 64 candidates
-    for (int q = 0; q < 64; ++q) {
-      const int need_q = __shfl(need, q, 64);
-      const int col = c0 + lane;
-      float x = -__builtin_inff();
-      if (col < need_q) x = sblk[(r0 + q) * (int64_t)nb + col];
-      tile[q][lane] = x;
-    }
-    __syncthreads();
-    const int cnt = min(64, need - c0);
-    for (int j = 0; j < 64; ++j) {
-      if constexpr (KM1 > 0) {
-        float cv = tile[lane][j];
-        if (j < cnt && cv > v[KM1 - 1]) {
-          int ci = c0 + j;
+  if constexpr (KM1 > 0) {
+    const float* row = sblk + r * (int64_t)nb;
+    for (int b0 = s; b0 < need; b0 += 64) {
+      // four candidates per lane per step: the loads are issued together
+      float cvs[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cvs[q] = (b0 + 16 * q < need) ? row[b0 + 16 * q] : -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float cv = cvs[q];
+        if (cv > v[KM1 - 1]) {
+          int ci = b0 + 16 * q;
           // Insert before the first strictly smaller score; from there on every
           // element shifts down one place (the displaced ones keep their order,
           // so equal scores stay in ascending index order).
@@ -83,30 +93,58 @@ __global__ __launch_bounds__(64) void k_select(const float* __restrict__ sblk, i
         }
       }
     }
-    __syncthreads();
   }
-
-  if (!valid) return;
-  int32_t* out = sel + (int64_t)g * sel_gstride + rr * sel_rstride;
-  if (b_loc <= KM1) {
-#pragma unroll
-    for (int u = 0; u <= KM1; ++u) out[u] = (u <= b_loc) ? u : -1;
+  if (!valid) return;  // whole 16-lane rows leave together
+  if (b_loc <= KM1) {  // every block 0..b_loc is selected
+    if (s <= KM1) sel[(int64_t)g * sel_gstride + rr * sel_rstride + s] = (s <= b_loc) ? s : -1;
     return;
   }
-  // ascending block ids (bubble network over the k-1 chosen indices)
+  if constexpr (KM1 == 0) {  // k = 1: the local block alone
+    if (s == 0) sel[(int64_t)g * sel_gstride + rr * sel_rstride] = b_loc;
+  } else {
+    int chosen[KM1];
 #pragma unroll
-  for (int a = 0; a < KM1; ++a) {
+    for (int rd = 0; rd < KM1; ++rd) {
+      // arg-max of the heads over the row: inclusive shifts leave it in lane 15
+      float bv = v[0];
+      int bi = id[0];
 #pragma unroll
-    for (int t = 0; t + 1 < KM1 - a; ++t) {
-      const int lo = min(id[t], id[t + 1]);
-      const int hi = max(id[t], id[t + 1]);
-      id[t] = lo;
-      id[t + 1] = hi;
+      for (int m = 1; m < 16; m <<= 1) {
+        const float ov = dpp_shr_f(bv, m);
+        const int oi = dpp_shr_i(bi, m);
+        const bool take = ov > bv || (ov == bv && oi < bi);
+        bv = take ? ov : bv;
+        bi = take ? oi : bi;
+      }
+      bi = __shfl(bi, (threadIdx.x & 63) | 15, 64);
+      chosen[rd] = bi;
+      if (id[0] == bi) {  // the winning lane pops its head
+#pragma unroll
+        for (int t = 0; t + 1 < KM1; ++t) {
+          v[t] = v[t + 1];
+          id[t] = id[t + 1];
+        }
+        v[KM1 - 1] = -__builtin_inff();
+        id[KM1 - 1] = 0x7fffffff;
+      }
     }
-  }
+    // ascending block ids (bubble network over the k-1 chosen indices)
 #pragma unroll
-  for (int u = 0; u < KM1; ++u) out[u] = id[u];
-  out[KM1] = b_loc;
+    for (int a = 0; a < KM1; ++a) {
+#pragma unroll
+      for (int t = 0; t + 1 < KM1 - a; ++t) {
+        const int lo = min(chosen[t], chosen[t + 1]);
+        const int hi = max(chosen[t], chosen[t + 1]);
+        chosen[t] = lo;
+        chosen[t + 1] = hi;
+      }
+    }
+    // lane s writes slot s (slot k-1 is b_loc)
+    int mine = b_loc;
+#pragma unroll
+    for (int u = 0; u < KM1; ++u) mine = (s == u) ? chosen[u] : mine;
+    if (s <= KM1) sel[(int64_t)g * sel_gstride + rr * sel_rstride + s] = mine;
+  }
 }
 
 // Few rows with many candidates (decode): one wave per row. Lane l ranks the
@@ -202,16 +240,16 @@ __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sb
 void launch_select(const LaunchSelect& a, hipStream_t st) {
   const int64_t rows = a.nrows * a.G;
   if (rows <= 0) return;
-  // thread-per-row needs many rows to fill the GPU; below that, wave-per-row
+  // few rows: a wave per row; many rows: 16 lanes per row (4 rows per wave)
   const bool per_wave = rows <= kWaveRowsMax;
-  dim3 grid((unsigned)(per_wave ? rows : (rows + 63) / 64));
+  dim3 grid((unsigned)(per_wave ? rows : (rows + 15) / 16));
 #define MSA_SEL_CASE(K)                                                                                 \
   case K:                                                                                               \
     if (per_wave)                                                                                       \
       hipLaunchKernelGGL(k_select_wave<K - 1>, grid, dim3(64), 0, st, a.sblk, a.nb, a.sel,              \
                          a.sel_gstride, a.sel_rstride, a.G, a.row0, a.ctx_lens);                        \
     else                                                                                                \
-      hipLaunchKernelGGL(k_select<K - 1>, grid, dim3(64), 0, st, a.sblk, a.nb, a.sel, a.sel_gstride,    \
+      hipLaunchKernelGGL(k_select<K - 1>, grid, dim3(256), 0, st, a.sblk, a.nb, a.sel, a.sel_gstride,   \
                          a.sel_rstride, a.nrows, a.G, a.row0, a.ctx_lens);                              \
     break;
   switch (a.topk) {
