@@ -272,74 +272,102 @@ constexpr int kAttnNT = 4;  // key tiles per softmax step (half a block)
 
 // Sparse (KV-outer) part: one persistent workgroup per CU drains the tile
 // queue. A query's own block is always shared by its whole 16-row unit, so no
-// KV-outer tile needs causal masking. The next tile is claimed and its block streamed into the other LDS
-// stage while the current tile is computed. Each wave takes QN queries of the
-// tile per pass; the next group's Q is loaded into the Q registers as soon as
-// the current scores are formed.
+// KV-outer tile needs causal masking. A tile holds at most 16 queries; wave w
+// takes its entries 2w and 2w+1. Everything a tile needs is fetched one tile
+// ahead, so no latency sits between two tiles: while tile j is computed, the
+// K/V of tile j+1 stream into the other LDS stage, the wave's entries of tile
+// j+1 and then their Q are loaded, and the descriptor of tile j+2 is read.
+// Tiles are claimed from the queue kClaim at a time, one chunk ahead.
 __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ tiles, int32_t* __restrict__ tile_info,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int64_t n_tokens, int64_t row0, int G,
     int nbw, int topk, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
-  __shared__ int s_t[2];
+  __shared__ int s_t[4];
   lds_char* lds = (lds_char*)lds_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, qd = lane >> 4;
   const int T = tile_info[0];
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
+  const int e0 = wave * kAttnQN;  // the wave's entries in every tile
 
-  if (tid == 0) s_t[0] = atomicAdd(&tile_info[1], 1);
-  __syncthreads();
-  int tcur = s_t[0];
-  int begin = 0, len = 0, g = 0, b = 0;
-  if (tcur < T) {
-    const int l = tiles[4 * tcur];
-    begin = tiles[4 * tcur + 1];
-    len = tiles[4 * tcur + 2];
-    g = l / nbw;
-    b = l % nbw;
-    const int64_t key0 = (int64_t)b * kBlock;
-    stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
+  struct Tile {
+    int t, begin, len, g, b;
+  };
+  auto read_tile = [&](int t) -> Tile {
+    Tile d{t, 0, 0, 0, 0};
+    if (t < T) {
+      const int l = tiles[4 * t];
+      d.begin = tiles[4 * t + 1];
+      d.len = tiles[4 * t + 2];
+      d.g = l / nbw;
+      d.b = l % nbw;
+    }
+    return d;
+  };
+  auto stage_tile = [&](const Tile& d, lds_char* dst) {
+    const int64_t key0 = (int64_t)d.b * kBlock;
+    stage_block(dst, k + (key0 * G + d.g) * kHeadDim, v + (key0 * G + d.g) * kHeadDim, rstride,
                 (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
-  }
+  };
   QueryGroup<kAttnQN, kAttnNT> qg;
-  int ent[kAttnQN];
-  int e0 = wave * kAttnQN;
-  // Q of the wave's current group; `have_q` says it is already loaded
-  bool have_q = false;
-  auto fetch_group = [&](int tb, int tg, int tlen, int e) {
+  auto fetch_q = [&](const int (&ent)[kAttnQN], int tg) {
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) {
-      ent[n] = entries[tb + min(e + n, tlen - 1)];
       const int64_t i = row0 + (ent[n] >> 4);
       load_q(qg, n, q + ((i * Hq) + tg * kHpg + c) * kHeadDim + 8 * qd);
     }
   };
-  for (int j = 0; tcur < T; ++j) {
-    if (tid == 0) s_t[(j + 1) & 1] = atomicAdd(&tile_info[1], 1);
-    if (!have_q && e0 < len) fetch_group(begin, g, len, e0);
-    wait_loads();
-    __syncthreads();  // stage j&1 is complete; stage (j+1)&1 is free; s_t visible
-    const int tnext = s_t[(j + 1) & 1];
-    int nbegin = 0, nlen = 0, ng = 0, nb2 = 0;
-    if (tnext < T) {
-      const int l2 = tiles[4 * tnext];
-      nbegin = tiles[4 * tnext + 1];
-      nlen = tiles[4 * tnext + 2];
-      ng = l2 / nbw;
-      nb2 = l2 % nbw;
-      const int64_t k2 = (int64_t)nb2 * kBlock;
-      stage_block(lds + ((j + 1) & 1) * kStage, k + (k2 * G + ng) * kHeadDim, v + (k2 * G + ng) * kHeadDim,
-                  rstride, (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
+  auto read_entries = [&](const Tile& d, int (&ent)[kAttnQN]) {
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) ent[n] = entries[d.begin + min(e0 + n, d.len - 1)];
+  };
+
+  // the queue: chunk c of this workgroup's tiles (tiles kClaim*c ..) starts at
+  // queue position s_t[c & 1]
+  constexpr int kClaim = 4;
+  if (tid == 0) s_t[0] = atomicAdd(&tile_info[1], kClaim);
+  __syncthreads();
+  auto tile_pos = [&](int jj) { return s_t[(jj / kClaim) & 1] + jj % kClaim; };
+  Tile cur = read_tile(tile_pos(0));
+  Tile nxt = read_tile(tile_pos(1));
+  int ent[kAttnQN] = {0, 0};
+  if (cur.t < T) {
+    stage_tile(cur, lds);
+    if (e0 < cur.len) {
+      read_entries(cur, ent);
+      fetch_q(ent, cur.g);
+    }
+  }
+  int after_dma = 0;  // vector memory operations issued after the last stage load
+  for (int j = 0; cur.t < T; ++j) {
+    wait_vmcnt_upto(after_dma);  // the stage of tile j is in
+    wait_lgkmcnt0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // ... for every wave; the other stage is free; s_t visible
+    asm volatile("" ::: "memory");
+    // chunk c+1 is claimed when chunk c starts; it is first read two tiles
+    // later (for tile kClaim*(c+1)), after at least one more barrier
+    if (tid == 0 && j % kClaim == 0) s_t[(j / kClaim + 1) & 1] = atomicAdd(&tile_info[1], kClaim);
+    const int t2 = tile_pos(j + 2);
+    int d2[3] = {0, 0, 0};
+    if (t2 < T) {
+      d2[0] = tiles[4 * t2];
+      d2[1] = tiles[4 * t2 + 1];
+      d2[2] = tiles[4 * t2 + 2];
+    }
+    after_dma = 0;
+    if (nxt.t < T) stage_tile(nxt, lds + ((j + 1) & 1) * kStage);
+    const bool next_work = nxt.t < T && e0 < nxt.len;
+    int nent[kAttnQN] = {0, 0};
+    if (next_work) {
+      read_entries(nxt, nent);
+      after_dma += kAttnQN + 4 * kAttnQN;  // entries, then their Q below
     }
     const lds_char* stage = lds + (j & 1) * kStage;
-    have_q = false;
-    for (; e0 < len; e0 += kAttnWaves * kAttnQN) {
-      int cur[kAttnQN];
-#pragma unroll
-      for (int n = 0; n < kAttnQN; ++n) cur[n] = ent[n];
+    if (e0 < cur.len) {
 #pragma unroll
       for (int t0 = 0; t0 < 8 - kAttnNT; t0 += kAttnNT) {
         scores(qg, stage, t0);
@@ -349,33 +377,31 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
           softmax_pv<false, false>(qg, stage, nullptr, scale_log2, t0, t0);
       }
       scores(qg, stage, 8 - kAttnNT);
-      // prefetch the wave's next group (in this tile, else the first of the next
-      // tile) into the Q registers, which the scores no longer need
-      const int e1 = e0 + kAttnWaves * kAttnQN;
-      if (e1 < len) {
-        fetch_group(begin, g, len, e1);
-      } else if (wave * kAttnQN < nlen) {
-        fetch_group(nbegin, ng, nlen, wave * kAttnQN);
-        have_q = true;
-      }
+      // the scores no longer need Q: load the next tile's
+      if (next_work) fetch_q(nent, nxt.g);
       if (kAttnNT == 8)
         softmax_pv<true, false>(qg, stage, nullptr, scale_log2, 0, 0);
       else
         softmax_pv<false, false>(qg, stage, nullptr, scale_log2, 8 - kAttnNT, 8 - kAttnNT);
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
-        if (e0 + n < len) {
-          const int64_t slot = ((int64_t)(cur[n] >> 4) * G + g) * topk + (cur[n] & 15);
+        if (e0 + n < cur.len) {
+          const int64_t slot = ((int64_t)(ent[n] >> 4) * G + cur.g) * topk + (ent[n] & 15);
           store_partial(qg.o[n], qg.m[n], scale_log2, part_o + slot * kHpg * kHeadDim, part_lse + slot * kHpg);
+          after_dma += 9;  // 8 partial stores + the lse store
         }
       }
+    } else if (next_work) {
+      fetch_q(nent, nxt.g);
     }
-    tcur = tnext;
-    begin = nbegin;
-    len = nlen;
-    g = ng;
-    b = nb2;
-    e0 = wave * kAttnQN;
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) ent[n] = nent[n];
+    cur = nxt;
+    nxt.t = t2;
+    nxt.begin = d2[1];
+    nxt.len = d2[2];
+    nxt.g = d2[0] / nbw;
+    nxt.b = d2[0] % nbw;
   }
 }
 

@@ -52,6 +52,24 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 __device__ __forceinline__ void wait_vmcnt5() { __builtin_amdgcn_s_waitcnt(0x0F75); }
 __device__ __forceinline__ void wait_vmcnt10() { __builtin_amdgcn_s_waitcnt(0x0F7A); }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// vmcnt(min(n, 31)) for a wave-uniform n: at most n vector memory operations
+// (those issued last) may still be in flight; a smaller count only waits more
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n < 31 ? n : 31) {
+#define MSA_VMCNT_CASE(N) \
+  case N:                 \
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N); break;
+    MSA_VMCNT_CASE(0) MSA_VMCNT_CASE(1) MSA_VMCNT_CASE(2) MSA_VMCNT_CASE(3) MSA_VMCNT_CASE(4) MSA_VMCNT_CASE(5)
+    MSA_VMCNT_CASE(6) MSA_VMCNT_CASE(7) MSA_VMCNT_CASE(8) MSA_VMCNT_CASE(9) MSA_VMCNT_CASE(10) MSA_VMCNT_CASE(11)
+    MSA_VMCNT_CASE(12) MSA_VMCNT_CASE(13) MSA_VMCNT_CASE(14) MSA_VMCNT_CASE(15)
+#undef MSA_VMCNT_CASE
+    default:
+      if (n >= 31) __builtin_amdgcn_s_waitcnt(0x4F7F);  // vmcnt(31)
+      else if (n >= 24) __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt(24)
+      else __builtin_amdgcn_s_waitcnt(0x0F7F);  // vmcnt(15)
+      break;
+  }
+}
 
 __device__ __forceinline__ void lds_dma16(const void* src, const lds_char* lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
