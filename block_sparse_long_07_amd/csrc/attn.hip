@@ -198,8 +198,7 @@ __device__ __forceinline__ void softmax_pv(QG& qg, const lds_char* stage_in, con
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       mx = fmaxf(fmaxf(mx, fmaxf(qg.s[n][t][0], qg.s[n][t][1])), fmaxf(qg.s[n][t][2], qg.s[n][t][3]));
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    mx = max_lane_groups(mx);
     if (FIRST) {
       qg.m[n] = mx;
     } else if (__any((mx - qg.m[n]) * scale_log2 > kLazy)) {

@@ -11,7 +11,7 @@
 // Contraction on MFMA: S^T tile (16 keys x 16 rows) = K (16 x 32 dims) * Q^T
 // (32 dims x 16 rows), two steps over d_idx = 64. Each lane then holds four keys
 // of one row, so the pooling max is three in-lane maxima per tile plus two
-// cross-lane steps per block.
+// cross-lane lane-swap steps per block.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -107,8 +107,7 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      mx[rt] = fmaxf(mx[rt], shfl_xor_f(mx[rt], 16));
-      mx[rt] = fmaxf(mx[rt], shfl_xor_f(mx[rt], 32));
+      mx[rt] = max_lane_groups(mx[rt]);
     }
     // all four lane groups now hold the block maxima; group qd keeps tiles rt = qd mod 4
     const int x = kb - kb0;
@@ -192,8 +191,7 @@ __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict
         acc = mfma16x16x32(as_bf16x8(a[h][t][1]), qop[1], acc);
         mx = fmaxf(mx, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
       }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      mx = max_lane_groups(mx);
       const int blk = h ? kb2 : kb;
       if (qd == 0 && c < G && (h == 0 || two)) sblk[((int64_t)sq * G + c) * nb + blk] = mx;
     }

@@ -110,6 +110,17 @@ __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(
 // Cross-lane exchange within a wave (ds_bpermute based).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// max over the four lanes l ^ {0, 16, 32, 48} (the four lane groups of an
+// MFMA 16x16 fragment column): v_permlane32_swap then v_permlane16_swap with
+// both operands x return x of the partner half / row in one of the two
+// results, so each step is one VALU swap and a max, with no LDS traffic.
+__device__ __forceinline__ float max_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Order-preserving map of fp32 onto uint32 (larger float -> larger uint).
 __device__ __forceinline__ uint32_t ord_f32(float f) {
   uint32_t u = __float_as_uint(f);
