@@ -124,9 +124,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "d442bfc635342f3d",
-    "k_attn_prefill (KV-outer)": 7.905e9,
-    "k_attn_dense (dense + merge)": 5.684e9,
+    "source": "778f3394e850d7e2",
+    "k_attn_prefill (KV-outer)": 8.038e9,
+    "k_attn_dense (dense + merge)": 5.670e9,
 }
 
 
