@@ -13,8 +13,8 @@
 // index ascending): a candidate enters only if it is strictly greater than
 // the current (k-1)-th score and is placed after every equal score, so among
 // equal scores the lowest indices are kept. The 16 lane lists of a row are
-// then merged by k-1 rounds of a row-wide arg-max over the list heads (DPP
-// shifts inside the 16-lane row; ties to the lower index), the winning lane
+// then merged by k-1 rounds of a row-wide arg-max over the list heads (a DPP
+// butterfly inside the 16-lane row; ties to the lower index), the winning lane
 // popping its head. The chosen indices are sorted ascending and written with
 // b_loc last and -1 padding.
 #include "msa_device.h"
@@ -24,21 +24,39 @@ namespace msa {
 
 constexpr int64_t kWaveRowsMax = 16384;
 
-__device__ __forceinline__ float dpp_shr_f(float x, int n) {
-  // row_shr:n within 16-lane rows; lanes with no source keep x
-  switch (n) {
-    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x111, 0xF, 0xF, false));
-    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x112, 0xF, 0xF, false));
-    case 4: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x114, 0xF, 0xF, false));
-    default: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x118, 0xF, 0xF, false));
-  }
+// One step of a symmetric arg-max butterfly inside 16-lane rows: lane i meets
+// lane xor 1 (step 0), xor 2 (1), 7-i within its 8-lane half (2), 15-i (3),
+// all DPP moves; after the four steps every lane of the row holds the row's
+// best (score desc, index asc).
+template <int STEP>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), ctrl, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, ctrl, 0xF, 0xF, false);
+  const bool take = ov > bv || (ov == bv && oi < bi);
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
 }
-__device__ __forceinline__ int dpp_shr_i(int x, int n) {
-  switch (n) {
-    case 1: return __builtin_amdgcn_update_dpp(x, x, 0x111, 0xF, 0xF, false);
-    case 2: return __builtin_amdgcn_update_dpp(x, x, 0x112, 0xF, 0xF, false);
-    case 4: return __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false);
-    default: return __builtin_amdgcn_update_dpp(x, x, 0x118, 0xF, 0xF, false);
+__device__ __forceinline__ void argmax_row16(float& bv, int& bi) {
+  argmax_step<0>(bv, bi);
+  argmax_step<1>(bv, bi);
+  argmax_step<2>(bv, bi);
+  argmax_step<3>(bv, bi);
+}
+// across the four rows of a wave: v_permlane16_swap / v_permlane32_swap hand
+// each lane its partner's pair (lane xor 16, then xor 32)
+__device__ __forceinline__ void argmax_rows(float& bv, int& bi) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto sv = h ? __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false)
+                      : __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto si = h ? __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false)
+                      : __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
+    const float v0 = __uint_as_float(sv[0]), v1 = __uint_as_float(sv[1]);
+    const int i0 = (int)si[0], i1 = (int)si[1];
+    const bool take1 = v1 > v0 || (v1 == v0 && i1 < i0);
+    bv = take1 ? v1 : v0;
+    bi = take1 ? i1 : i0;
   }
 }
 
@@ -105,18 +123,10 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ sblk, 
     int chosen[KM1];
 #pragma unroll
     for (int rd = 0; rd < KM1; ++rd) {
-      // arg-max of the heads over the row: inclusive shifts leave it in lane 15
+      // arg-max of the heads over the row
       float bv = v[0];
       int bi = id[0];
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const float ov = dpp_shr_f(bv, m);
-        const int oi = dpp_shr_i(bi, m);
-        const bool take = ov > bv || (ov == bv && oi < bi);
-        bv = take ? ov : bv;
-        bi = take ? oi : bi;
-      }
-      bi = __shfl(bi, (threadIdx.x & 63) | 15, 64);
+      argmax_row16(bv, bi);
       chosen[rd] = bi;
       if (id[0] == bi) {  // the winning lane pops its head
 #pragma unroll
@@ -150,8 +160,9 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ sblk, 
 // Few rows with many candidates (decode): one wave per row. Lane l ranks the
 // candidates b = l, l+64, ... (ascending, so the same register insertion keeps
 // its k-1 best with ties to the lower index); the 64 lane lists are then merged
-// by k-1 rounds of a wave-wide arg-max over the list heads, each round popping
-// the winner's head.
+// by k-1 rounds of a wave-wide arg-max over the list heads (a DPP butterfly
+// within 16-lane rows, then v_permlane16/32 swaps across rows), each round
+// popping the winner's head.
 template <int KM1>
 __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sblk, int nb,
                                                     int32_t* __restrict__ sel, int64_t sel_gstride,
@@ -198,16 +209,12 @@ __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sb
     int chosen[KM1];
 #pragma unroll
     for (int rd = 0; rd < KM1; ++rd) {
+      // wave-wide arg-max: DPP butterfly inside 16-lane rows, then lane swaps
+      // across rows, all without LDS traffic
       float bv = v[0];
       int bi = id[0];
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const int oi = __shfl_xor(bi, m, 64);
-        const bool take = ov > bv || (ov == bv && oi < bi);
-        bv = take ? ov : bv;
-        bi = take ? oi : bi;
-      }
+      argmax_row16(bv, bi);
+      argmax_rows(bv, bi);
       chosen[rd] = bi;
       if (id[0] == bi) {  // the winning lane pops its head
 #pragma unroll
