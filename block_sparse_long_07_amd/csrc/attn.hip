@@ -32,6 +32,8 @@
 //
 // Decode: one workgroup per (sequence, group, selected slot); four waves stage
 // the block, one computes the 16 heads.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -99,17 +101,15 @@ __device__ __forceinline__ bf16x8 lds_vt(const lds_char* stage, int dt, int st, 
                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
 }
 
-// Per-wave state of QN queries (16 heads each) against staged blocks, which
-// are processed NT key tiles (16 keys each) at a time.
-//   qop: Q^T B-operands (4 steps over d); s: S^T / P^T fragments of the current
-//   NT tiles; o[0..7]: O^T accumulators (head = lane & 15, d = 16*dt +
-//   4*(lane/16) + r); o[8]: every element is the softmax denominator of the
-//   lane's head (see softmax_pv); m: reference max of the raw scores per head.
-template <int QN, int NT>
+// Per-wave state of QN queries (16 heads each) against staged blocks.
+//   qop: Q^T B-operands (4 steps over d); o[0..7]: O^T accumulators (head =
+//   lane & 15, d = 16*dt + 4*(lane/16) + r); o[8]: every element is the softmax
+//   denominator of the lane's head (see attend_block); m: reference max of the
+//   raw scores per head.
+template <int QN>
 struct QueryGroup {
-  static constexpr int kQN = QN, kNT = NT;
+  static constexpr int kQN = QN;
   bf16x8 qop[QN][4];
-  f32x4 s[QN][NT];
   f32x4 o[QN][9];
   float m[QN];
 };
@@ -131,127 +131,259 @@ __device__ __forceinline__ void reset_state(QG& qg) {
   }
 }
 
-// S^T = K_b . Q^T for key tiles t0 .. t0+NT-1 of the staged block.
-template <class QG>
-__device__ __forceinline__ void scores(QG& qg, const lds_char* stage_in, int t0) {
-  constexpr int QN = QG::kQN, NT = QG::kNT;
+// Instruction classes of the scheduling hints (sched_group_barrier masks).
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// S^T = K_b . Q^T for key tiles 4h .. 4h+3 of the staged block (half h).
+template <int QN>
+__device__ __forceinline__ void qk_half(f32x4 (&s)[QN][4], const bf16x8 (&qop)[QN][4], const lds_char* stage,
+                                        int h) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
-  // An opaque copy of the stage pointer keeps the K fragment reads inside the
-  // query loop (otherwise they are hoisted across queries into many registers).
-  const lds_char* stage = stage_in;
-  asm volatile("" : "+v"(stage));
 #pragma unroll
   for (int n = 0; n < QN; ++n)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) qg.s[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // d-step outer, key tile inner: NT*QN independent accumulators between two
-  // dependent MFMAs, and the NT operand reads of a step are issued together.
+    for (int t = 0; t < 4; ++t) s[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // d-step outer, key tile inner: 4*QN independent accumulators between two
+  // dependent MFMAs, and the four operand reads of a step are issued together.
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    bf16x8 a[NT];
+    bf16x8 a[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) a[t] = lds_k(stage, t0 + t, st, c, qd);
+    for (int t = 0; t < 4; ++t) a[t] = lds_k(stage, 4 * h + t, st, c, qd);
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int n = 0; n < QN; ++n) qg.s[n][t] = mfma16x16x32(a[t], qg.qop[n][st], qg.s[n][t]);
+      for (int n = 0; n < QN; ++n) s[n][t] = mfma16x16x32(a[t], qop[n][st], s[n][t]);
   }
+}
+
+// Causal mask of half h (MASKED: keys with index > lim[n] get -inf) and the
+// max of each head's raw scores over the half, reduced over the lane groups.
+template <bool MASKED, int QN>
+__device__ __forceinline__ void half_max(f32x4 (&s)[QN][4], const int* lim, int h, float (&mx)[QN]) {
+  const int qd = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int n = 0; n < QN; ++n) {
+    if (MASKED) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * (4 * h + t) + 4 * qd + r > lim[n]) s[n][t][r] = -__builtin_inff();
+    }
+    float x = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      x = fmaxf(fmaxf(x, fmaxf(s[n][t][0], s[n][t][1])), fmaxf(s[n][t][2], s[n][t][3]));
+    mx[n] = max_lane_groups(x);
+  }
+}
+
+// p *= alpha[n] on packed bf16 operands (round to nearest even).
+template <int QN>
+__device__ __forceinline__ void scale_p(bf16x8 (&p)[QN][2], const float (&alpha)[QN]) {
+#pragma unroll
+  for (int n = 0; n < QN; ++n)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 w = __builtin_bit_cast(u32x4, p[n][j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(bf2f(w[i] & 0xffffu) * alpha[n], bf2f(w[i] >> 16) * alpha[n]);
+      p[n][j] = as_bf16x8(w);
+    }
 }
 
 // Exponent headroom of the lazily rescaled softmax: P may reach 2^kLazy
 // before the running state is rescaled to a new reference max.
 constexpr float kLazy = 8.0f;
 
-// Softmax update of the running state with the scores of key tiles t0 ..
-// t0+NT-1 of the stage (tiles kt0 .. of the block: kt0 places them for the
-// causal mask), then O^T += V^T . P^T over those keys (V at VOFF).
-//  * The logit scale is folded into the exponent: p = 2^(s*c - m*c) (c = scale
-//    * log2 e), with the reference max m kept on raw scores.
-//  * FIRST: fresh state; m is this part's max and the accumulators start at 0.
-//    Otherwise the state is rescaled only when some head's max exceeds its
-//    reference by more than kLazy/c (the rescale is exact: every term is
-//    multiplied by the same 2^((m_old - m_new) c)).
+// One exponential unit: P^T operand j of query n from scores s (half layout).
+template <int QN>
+__device__ __forceinline__ void exp_unit(const f32x4 (&s)[QN][4], const float (&mc)[QN], float scale_log2,
+                                         bf16x8 (&p)[QN][2], int n, int j) {
+  float e[8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      e[4 * u + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][2 * j + u][r], scale_log2, -mc[n]));
+  p[n][j] = as_bf16x8((u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                              pack_bf16x2(e[6], e[7])});
+}
+
+// Scheduling pattern of one pipelined region: NM MFMAs, NV VALU and ND LDS
+// reads spread evenly between them; nothing moves across the region's end.
+template <int NM, int NV, int ND, int I = 0>
+__device__ __forceinline__ void sched_region() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    constexpr int vi = (NV * (I + 1)) / NM - (NV * I) / NM;
+    constexpr int di = (ND * (I + 1)) / NM - (ND * I) / NM;
+    if constexpr (vi > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, vi, 0);
+    if constexpr (di > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, di, 0);
+    sched_region<NM, NV, ND, I + 1>();
+  } else {
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Online-softmax update of the running state with one staged block of 8 key
+// tiles (V at VOFF): S^T = K_b . Q^T, p = 2^(s*c - m*c) with the logit scale
+// folded into the exponent (c = scale * log2 e, reference max m kept on raw
+// scores), O^T += V^T . P^T. The block is processed as two halves of four
+// tiles, software-pipelined so that the VALU work of one half runs between
+// the MFMAs of the other:
+//   S0;  mask+max 0;  [S1 | exp 0];  mask+max 1;  [PV0 | exp 1];  PV1.
+// In the pipelined parts every d-step (S1) or key step (PV) is a scheduling
+// region of its own that also issues the operand reads of the next step.
+//  * FIRST: fresh state; m is the first half's max and the accumulators start
+//    at 0. Otherwise the state is rescaled only when some head's max exceeds
+//    its reference by more than kLazy/c; the rescale is exact (every term is
+//    multiplied by the same 2^((m_old - m_new) c)). A rescale decided by half
+//    1 also scales the packed P of half 0, whose PV has not been issued yet.
 //  * MASKED: the queries' own block; keys with index > lim[n] are masked. A
-//    part whose keys are all masked leaves the state unchanged (its max is
-//    -inf), which needs an earlier part with a finite max (key 0 of the own
-//    block is never masked).
-//  * The denominator is accumulated by MFMA as a ninth O^T tile whose A operand
-//    is all ones, so it sums exactly the bf16-rounded P that enters P.V.
-template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG>
-__device__ __forceinline__ void softmax_pv(QG& qg, const lds_char* stage_in, const int* lim, float scale_log2,
-                                           int t0, int kt0) {
-  constexpr int QN = QG::kQN, NT = QG::kNT, NS = NT / 2;
+//    half whose keys are all masked leaves the state unchanged (its max is
+//    -inf); key 0 of the own block is never masked.
+//  * after_qk() runs once the last S^T MFMA is issued (Q is no longer read).
+template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG, class F>
+__device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, const int* lim, float scale_log2,
+                                             F after_qk) {
+  constexpr int QN = QG::kQN;
+  constexpr int kExpValu = 21;  // VALU instructions of one exp_unit
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
+  // An opaque copy of the stage pointer keeps the operand reads next to their
+  // MFMAs (otherwise they are hoisted across queries into many registers).
   const lds_char* stage = stage_in;
   asm volatile("" : "+v"(stage));
-  bf16x8 pop[QN][NS];
+  f32x4 s0[QN][4], s1[QN][4];
+  bf16x8 p0[QN][2], p1[QN][2];
+  float mx[QN], mc[QN];
+
+  qk_half(s0, qg.qop, stage, 0);
+  // operands of the first pipelined step, read before the max and the branch
+  bf16x8 ka[4], va[8];
 #pragma unroll
-  for (int n = 0; n < QN; ++n) {
-    if (MASKED) {
+  for (int t = 0; t < 4; ++t) ka[t] = lds_k(stage, 4 + t, 0, c, qd);
+  half_max<MASKED>(s0, lim, 0, mx);
+  if (FIRST) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+    for (int n = 0; n < QN; ++n) qg.m[n] = mx[n];
+  } else {
+    bool need = false;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * (kt0 + t) + 4 * qd + r > lim[n]) qg.s[n][t][r] = -__builtin_inff();
-    }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      mx = fmaxf(fmaxf(mx, fmaxf(qg.s[n][t][0], qg.s[n][t][1])), fmaxf(qg.s[n][t][2], qg.s[n][t][3]));
-    mx = max_lane_groups(mx);
-    if (FIRST) {
-      qg.m[n] = mx;
-    } else if (__any((mx - qg.m[n]) * scale_log2 > kLazy)) {
-      const float mnew = fmaxf(qg.m[n], mx);
-      const float alpha = __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
-#pragma unroll
-      for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha;
-      qg.m[n] = mnew;
-    }
-    const float mc = qg.m[n] * scale_log2;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        qg.s[n][t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(qg.s[n][t][r], scale_log2, -mc));
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      u32x4 w;
-      w[0] = pack_bf16x2(qg.s[n][2 * j][0], qg.s[n][2 * j][1]);
-      w[1] = pack_bf16x2(qg.s[n][2 * j][2], qg.s[n][2 * j][3]);
-      w[2] = pack_bf16x2(qg.s[n][2 * j + 1][0], qg.s[n][2 * j + 1][1]);
-      w[3] = pack_bf16x2(qg.s[n][2 * j + 1][2], qg.s[n][2 * j + 1][3]);
-      pop[n][j] = as_bf16x8(w);
-    }
-  }
-  const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
-  const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
-  // key step outer, d tile inner (9*QN independent accumulators)
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int st = t0 / 2 + j;
-    bf16x8 a[9];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) a[dt] = lds_vt<VOFF>(stage, dt, st, c, qd);
-    a[8] = ones;
-#pragma unroll
-    for (int dt = 0; dt < 9; ++dt) {
+    for (int n = 0; n < QN; ++n) need |= (mx[n] - qg.m[n]) * scale_log2 > kLazy;
+    if (__any(need)) {
 #pragma unroll
       for (int n = 0; n < QN; ++n) {
-        if (FIRST && j == 0)
-          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][j], (f32x4){0.f, 0.f, 0.f, 0.f});
-        else
-          qg.o[n][dt] = mfma16x16x32(a[dt], pop[n][j], qg.o[n][dt]);
+        const float mnew = fmaxf(qg.m[n], mx[n]);
+        const float alpha = __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
+#pragma unroll
+        for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha;
+        qg.m[n] = mnew;
       }
     }
+  }
+
+  // S1 | exp 0
+  {
+#pragma unroll
+    for (int n = 0; n < QN; ++n) {
+      mc[n] = qg.m[n] * scale_log2;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s1[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    bf16x8 kn[4];
+    static_for<0, 4>([&](auto ist) {
+      constexpr int st = decltype(ist)::value;
+      if constexpr (st < 3) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kn[t] = lds_k(stage, 4 + t, st + 1, c, qd);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int n = 0; n < QN; ++n) s1[n][t] = mfma16x16x32(ka[t], qg.qop[n][st], s1[n][t]);
+      // exp units (n, j) = (u / 2, u % 2) of this step
+      constexpr int u0 = (st * 2 * QN + 3) / 4, u1 = ((st + 1) * 2 * QN + 3) / 4;
+#pragma unroll
+      for (int u = u0; u < u1; ++u) exp_unit(s0, mc, scale_log2, p0, u >> 1, u & 1);
+      sched_region<4 * QN, (u1 - u0) * kExpValu, st < 3 ? 4 : 0>();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ka[t] = kn[t];
+    });
+  }
+  after_qk();
+  half_max<MASKED>(s1, lim, 1, mx);
+  {
+    bool need = false;
+#pragma unroll
+    for (int n = 0; n < QN; ++n) need |= (mx[n] - qg.m[n]) * scale_log2 > kLazy;
+    if (__any(need)) {
+      float alpha[QN];
+#pragma unroll
+      for (int n = 0; n < QN; ++n) {
+        const float mnew = fmaxf(qg.m[n], mx[n]);
+        alpha[n] = __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
+        if (!FIRST) {
+#pragma unroll
+          for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha[n];
+        }
+        qg.m[n] = mnew;
+      }
+      scale_p(p0, alpha);
+    }
+  }
+
+  // PV0 | exp 1, then PV1; each key step reads the next step's V^T operands
+  {
+    const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
+    const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
+#pragma unroll
+    for (int n = 0; n < QN; ++n) mc[n] = qg.m[n] * scale_log2;
+    // region r = 2*st + hh covers d-tiles 4hh .. 4hh+3 (+ the ones tile) of
+    // key step st and reads the next region's V^T operands
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) va[dt] = lds_vt<VOFF>(stage, dt, 0, c, qd);
+    static_for<0, 8>([&](auto ir) {
+      constexpr int r = decltype(ir)::value, st = r >> 1, hh = r & 1;
+      constexpr int nst = hh ? st + 1 : st, nd0 = hh ? 0 : 4;
+      if constexpr (nst < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) va[nd0 + i] = lds_vt<VOFF>(stage, nd0 + i, nst, c, qd);
+      }
+      constexpr int d0 = 4 * hh, d1 = hh ? 9 : 4;
+#pragma unroll
+      for (int dt = d0; dt < d1; ++dt) {
+        const bf16x8 a = dt < 8 ? va[dt] : ones;
+#pragma unroll
+        for (int n = 0; n < QN; ++n) {
+          const bf16x8 b = st < 2 ? p0[n][st & 1] : p1[n][st & 1];
+          qg.o[n][dt] = (FIRST && st == 0) ? mfma16x16x32(a, b, (f32x4){0.f, 0.f, 0.f, 0.f})
+                                           : mfma16x16x32(a, b, qg.o[n][dt]);
+        }
+      }
+      // exp units of half 1 in the first four regions (PV0)
+      constexpr int u0 = r < 4 ? (r * 2 * QN + 3) / 4 : 0, u1 = r < 4 ? ((r + 1) * 2 * QN + 3) / 4 : 0;
+#pragma unroll
+      for (int u = u0; u < u1; ++u) exp_unit(s1, mc, scale_log2, p1, u >> 1, u & 1);
+      sched_region<(d1 - d0) * QN, (u1 - u0) * kExpValu, nst < 4 ? 8 : 0>();
+    });
   }
 }
 
 // Softmax partial of one query, normalised, in fragment order: element (head
 // c, dim 16dt + 4qd + r) sits at dt*256 + (16qd + c)*4 + r of the 2048-element
-// slot, so each of the eight stores of a wave writes 512 contiguous bytes (the
-// reader uses the same lane mapping). lse2 = m*c + log2(l) per head (c = scale
-// * log2 e).
+// slot, so each of the eight stores of a wave writes 512 contiguous bytes.
+// lse2 = m*c + log2(l) per head (c = scale * log2 e).
 __device__ __forceinline__ void store_partial(const f32x4 (&o)[9], float m, float scale_log2, uint16_t* dst,
                                               float* lse16) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
@@ -265,9 +397,79 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[9], float m, floa
   if (qd == 0) lse16[c] = m * scale_log2 + __builtin_amdgcn_logf(l);
 }
 
+// Issue the direct-to-LDS loads of one partial (4 KiB, copied as is) into
+// `dst`: four loads per wave.
+__device__ __forceinline__ void stage_partial(const uint16_t* src, lds_char* dst) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lds_dma16(src + j * 512 + lane * 8, dst + j * 1024);
+}
+
+// A operand of the merge MFMA for d-tile dt of a staged partial X: lane (c,
+// qd) holds X[4qd + (j & 3)][16dt + c] at k = 8qd + j (the four heads of the
+// transposing read, twice). Lane i of a 16-lane group addresses head 4qd +
+// i/4, dims 16dt + 4(i%4) .. +3: the 8-byte piece at dt*512 + (16(i%4) + head)*8
+// of the fragment-order slot.
+__device__ __forceinline__ bf16x8 partial_operand(const lds_char* xs, int dt, int c, int qd) {
+  const int r = 4 * qd + (c >> 2);
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(xs + dt * 512 + (16 * (c & 3) + r) * 8));
+  const u32x2 u = __builtin_bit_cast(u32x2, x);
+  return as_bf16x8((u32x4){u[0], u[1], u[0], u[1]});
+}
+
+// B operand diag(w) paired with partial_operand: row k = 8qd + j of column
+// (head) c is nonzero only for 4qd + (j & 3) == c, where j < 4 carries the
+// bf16 rounding of w and j >= 4 the bf16 rounding of the remainder, so the
+// product carries w to about 16 bits.
+__device__ __forceinline__ bf16x8 diag_operand(float w, int c, int qd) {
+  const uint32_t hi = pack_bf16x2(w, 0.f) & 0xffffu;
+  const uint32_t lo = pack_bf16x2(w - bf2f(hi), 0.f) & 0xffffu;
+  const bool on = qd == (c >> 2);
+  const int sh = (c & 1) * 16;
+  const uint32_t h = on ? hi << sh : 0u, l = on ? lo << sh : 0u;
+  const bool odd = (c & 2) != 0;
+  return as_bf16x8((u32x4){odd ? 0u : h, odd ? h : 0u, odd ? 0u : l, odd ? l : 0u});
+}
+
+// Merge of a normalised partial (staged at xs, lse2 lp for the lane's head)
+// into query n's running state (o, l = o[8], reference max m): o += w X^T and
+// l += w with w = 2^(lp - m*c), as nine MFMAs against diag(w) (the ones tile
+// adds w to l), after a lazy rescale of the state when lp exceeds m*c by more
+// than kLazy (a fresh state, m = -inf, takes m*c = lp).
+template <int N, class QG>
+__device__ __forceinline__ void merge_partial(QG& qg, const lds_char* xs, float lp, float scale_log2) {
+  const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
+  bf16x8 a[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) a[dt] = partial_operand(xs, dt, c, qd);
+  float mc = qg.m[N] * scale_log2;
+  if (__any(lp - mc > kLazy)) {
+    const float mnew = fmaxf(mc, lp);
+    const float alpha = __builtin_amdgcn_exp2f(mc - mnew);
+#pragma unroll
+    for (int t = 0; t < 9; ++t) qg.o[N][t] *= alpha;
+    qg.m[N] = mnew / scale_log2;
+    mc = mnew;
+  }
+  const bf16x8 bw = diag_operand(__builtin_amdgcn_exp2f(lp - mc), c, qd);
+  const uint32_t one2 = 0x3f803f80u;
+  const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) qg.o[N][dt] = mfma16x16x32(a[dt], bw, qg.o[N][dt]);
+  qg.o[N][8] = mfma16x16x32(ones, bw, qg.o[N][8]);
+}
+
+// merge_partial into query pn (wave-uniform) of the group.
+template <class QG>
+__device__ __forceinline__ void merge_partial_into(QG& qg, int pn, const lds_char* xs, float lp, float scale_log2) {
+  static_for<0, QG::kQN>([&](auto in) {
+    constexpr int n = decltype(in)::value;
+    if (pn == n) merge_partial<n>(qg, xs, lp, scale_log2);
+  });
+}
+
 constexpr int kAttnQN = 2;
 constexpr int kAttnWaves = 8;
-constexpr int kAttnNT = 4;  // key tiles per softmax step (half a block)
 
 // Sparse (KV-outer) part: one persistent workgroup per CU drains the tile
 // queue. A query's own block is always shared by its whole 16-row unit, so no
@@ -311,7 +513,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     stage_block(dst, k + (key0 * G + d.g) * kHeadDim, v + (key0 * G + d.g) * kHeadDim, rstride,
                 (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
   };
-  QueryGroup<kAttnQN, kAttnNT> qg;
+  QueryGroup<kAttnQN> qg;
   auto fetch_q = [&](const int (&ent)[kAttnQN], int tg) {
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) {
@@ -367,21 +569,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     }
     const lds_char* stage = lds + (j & 1) * kStage;
     if (e0 < cur.len) {
-#pragma unroll
-      for (int t0 = 0; t0 < 8 - kAttnNT; t0 += kAttnNT) {
-        scores(qg, stage, t0);
-        if (t0 == 0)
-          softmax_pv<true, false>(qg, stage, nullptr, scale_log2, t0, t0);
-        else
-          softmax_pv<false, false>(qg, stage, nullptr, scale_log2, t0, t0);
-      }
-      scores(qg, stage, 8 - kAttnNT);
-      // the scores no longer need Q: load the next tile's
-      if (next_work) fetch_q(nent, nxt.g);
-      if (kAttnNT == 8)
-        softmax_pv<true, false>(qg, stage, nullptr, scale_log2, 0, 0);
-      else
-        softmax_pv<false, false>(qg, stage, nullptr, scale_log2, 8 - kAttnNT, 8 - kAttnNT);
+      // once the scores no longer need Q, the next tile's is loaded
+      attend_block<true, false>(qg, stage, nullptr, scale_log2, [&]() {
+        if (next_work) fetch_q(nent, nxt.g);
+      });
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
         if (e0 + n < cur.len) {
@@ -411,11 +602,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
 // per (unit, group), two queries per wave. The list always ends with the
 // unit's own block, the only one that needs the causal mask. This pass runs
 // after the KV-outer pass and merges its partials (the slots of the query's
-// selection that are not shared by the unit), so every row's output and lse
-// are written here, once, without atomics: with M = max over the dense state
-// and the partials of lse2 and w = 2^(lse2 - M),
-//   out = sum w o / sum w,   lse = (M + log2 sum w) * ln 2
-// (the second phase of the two-phase combine [pnsm, section 7]).
+// selection that are not shared by the unit) into the same online state, so
+// every row's output and lse are written here, once, without atomics (the
+// second phase of the two-phase combine [pnsm, section 7]):
+//   out = o / l,   lse = (m*c + log2 l) * ln 2.
 __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ dense_cnt, const int32_t* __restrict__ dense_list,
@@ -440,7 +630,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   // and the queries' Q
   const int lane_blk = lane < topk ? list[lane] : 0;
   const int nd = dense_cnt[g * nunits + unit];  // >= 1: the unit's own block
-  QueryGroup<kAttnQN, kAttnNT> qg;
+  QueryGroup<kAttnQN> qg;
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int64_t i = row0 + min(i_rel0 + n, nrows - 1);
@@ -473,8 +663,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
 
   // KV-outer partials of the wave's queries, in (query, slot) order. One at a
   // time streams into the wave's slot while a dense block is computed and is
-  // merged into the running state after it; the rest go through the two
-  // larger regions after the last block (below).
+  // merged at the start of the next block; the rest go through the two larger
+  // regions after the last block (below).
   lds_char* pslot = lds + 2 * kStage + wave * 4096;
   int cur_n = 0;
   uint64_t cur_rem = use[0];
@@ -499,46 +689,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     int64_t slot = 0;
     pend_n = -1;
     if (!next_pair(pn, slot)) return;
-    const uint16_t* src = part_o + slot * (kHpg * kHeadDim);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_dma16(src + j * 512 + lane * 8, pslot + j * 1024);
+    stage_partial(part_o + slot * (kHpg * kHeadDim), pslot);
     pend_lse = part_lse[slot * kHpg + c];
     pend_n = pn;
-  };
-  // merge of a normalised partial (o_p, lse2 lp) into the running state
-  // (o, l = o[8], reference max m): it adds o_p * w and w, w = 2^(lp - m*c),
-  // after a lazy rescale of the state when lp exceeds m*c by more than kLazy
-  // (a fresh state has m = -inf and takes m*c = lp)
-  auto merge_slot = [&]() {
-    if (pend_n < 0) return;
-    u32x2 x[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      x[dt] = *(const __attribute__((address_space(3))) u32x2*)(pslot + dt * 512 + lane * 8);
-    const float lp = pend_lse;
-#pragma unroll
-    for (int n = 0; n < kAttnQN; ++n) {
-      if (pend_n != n) continue;  // wave-uniform; every access below has a constant index
-      float mc = qg.m[n] * scale_log2;
-      if (__any(lp - mc > kLazy)) {
-        const float mnew = fmaxf(mc, lp);
-        const float alpha = __builtin_amdgcn_exp2f(mc - mnew);
-#pragma unroll
-        for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha;
-        qg.m[n] = mnew / scale_log2;
-        mc = qg.m[n] * scale_log2;
-      }
-      const float w = __builtin_amdgcn_exp2f(lp - mc);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        qg.o[n][dt][0] += w * bf2f(x[dt][0] & 0xffffu);
-        qg.o[n][dt][1] += w * bf2f(x[dt][0] >> 16);
-        qg.o[n][dt][2] += w * bf2f(x[dt][1] & 0xffffu);
-        qg.o[n][dt][3] += w * bf2f(x[dt][1] >> 16);
-      }
-      qg.o[n][8] += w;
-    }
-    wait_lgkmcnt0();  // slot read out before it is refilled
   };
   issue_slot();
 
@@ -549,13 +702,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const int64_t k2 = (int64_t)__builtin_amdgcn_readlane(lane_blk, d + 1) * kBlock;
     stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim, rstride,
                 (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
-    const lds_char* stage = lds + (d & 1) * kStage;
-#pragma unroll
-    for (int t0 = 0; t0 < 8; t0 += kAttnNT) {
-      scores(qg, stage, t0);
-      softmax_pv<false, false>(qg, stage, nullptr, scale_log2, t0, t0);
-    }
-    merge_slot();
+    if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
+    attend_block<false, false>(qg, lds + (d & 1) * kStage, nullptr, scale_log2, [] {});
+    wait_lgkmcnt0();  // the slot is read out before it is refilled
     issue_slot();
   }
 
@@ -575,9 +724,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
       int pn = 0;
       int64_t slot = 0;
       if (!next_pair(pn, slot)) break;
-      const uint16_t* src = part_o + slot * (kHpg * kHeadDim);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lds_dma16(src + j * 512 + lane * 8, region[reg] + p * 4096 + j * 1024);
+      stage_partial(part_o + slot * (kHpg * kHeadDim), region[reg] + p * 4096);
       if (lane < kHpg) lds_dma4(part_lse + slot * kHpg + lane, lse_side + reg * 128 + p * 64);
       if (p == 0) na = pn; else nb = pn;
       cnt = p + 1;
@@ -591,65 +738,27 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     else
       wait_vmcnt0();
   };
-  int cA = 0, nA0 = 0, nA1 = 0, cB = 0, nB0 = 0, nB1 = 0;
-  {
-    wait_loads();
-    __syncthreads();
-    merge_slot();  // frees the slot for the lse of the rounds
-    issue_round(0, cA, nA0, nA1);
-    const lds_char* stage = lds + last * kStage;
-    int lim[kAttnQN];
-#pragma unroll
-    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
-#pragma unroll
-    for (int t0 = 0; t0 < 8; t0 += kAttnNT) {
-      scores(qg, stage, t0);
-      softmax_pv<false, true>(qg, stage, lim, scale_log2, t0, t0);
-    }
-  }
-  // merge state per query: o = normalised output so far, M its lse2, wsum
-  // the weight sum relative to M (the dense state has weight 1 at its lse2)
-  float M[kAttnQN], wsum[kAttnQN];
-#pragma unroll
-  for (int n = 0; n < kAttnQN; ++n) {
-    const float l_d = qg.o[n][8][0];
-    M[n] = qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l_d);
-    wsum[n] = 1.0f;
-    const float inv = 1.0f / l_d;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) qg.o[n][dt] *= inv;
-  }
   auto merge_round = [&](int reg, int cnt, int na, int nb) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if (p >= cnt) break;
-      const int pn = p ? nb : na;
-      u32x2 x[8];
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        x[dt] = *(const __attribute__((address_space(3))) u32x2*)(region[reg] + p * 4096 + dt * 512 + lane * 8);
       const float lp = *(const __attribute__((address_space(3))) float*)(lse_side + reg * 128 + p * 64 + c * 4);
-      // both queries are updated, the other one with (scale 1, weight 0): a
-      // branch on pn would let the compiler index the accumulators dynamically
-#pragma unroll
-      for (int n = 0; n < kAttnQN; ++n) {
-        const bool mine = pn == n;
-        const float mn = mine ? fmaxf(M[n], lp) : M[n];
-        const float s_old = mine ? __builtin_amdgcn_exp2f(M[n] - mn) : 1.0f;
-        const float w = mine ? __builtin_amdgcn_exp2f(lp - mn) : 0.0f;
-        M[n] = mn;
-        wsum[n] = wsum[n] * s_old + w;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          qg.o[n][dt][0] = qg.o[n][dt][0] * s_old + w * bf2f(x[dt][0] & 0xffffu);
-          qg.o[n][dt][1] = qg.o[n][dt][1] * s_old + w * bf2f(x[dt][0] >> 16);
-          qg.o[n][dt][2] = qg.o[n][dt][2] * s_old + w * bf2f(x[dt][1] & 0xffffu);
-          qg.o[n][dt][3] = qg.o[n][dt][3] * s_old + w * bf2f(x[dt][1] >> 16);
-        }
-      }
+      merge_partial_into(qg, p ? nb : na, region[reg] + p * 4096, lp, scale_log2);
     }
     wait_lgkmcnt0();  // region read out before it is refilled
   };
+  int cA = 0, nA0 = 0, nA1 = 0, cB = 0, nB0 = 0, nB1 = 0;
+  {
+    wait_loads();
+    __syncthreads();
+    if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
+    wait_lgkmcnt0();  // the slot is read out: it holds the lse of the rounds
+    issue_round(0, cA, nA0, nA1);
+    int lim[kAttnQN];
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
+    attend_block<false, true>(qg, lds + last * kStage, lim, scale_log2, [] {});
+  }
   wait_lgkmcnt0();  // the last block's stage is free
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -670,7 +779,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   for (int n = 0; n < kAttnQN; ++n) {
     const int i_rel = i_rel0 + n;
     if (i_rel >= nrows) continue;
-    const float inv = 1.0f / wsum[n];
+    const float l = qg.o[n][8][0];
+    const float inv = 1.0f / l;
     uint16_t* dst = out + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -679,7 +789,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
       *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
     }
     if (lse_out && qd == 0)
-      lse_out[(int64_t)i_rel * Hq + g * kHpg + c] = (M[n] + __builtin_amdgcn_logf(wsum[n])) * 0.69314718055994530942f;
+      lse_out[(int64_t)i_rel * Hq + g * kHpg + c] =
+          (qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
   }
 }
 
@@ -704,14 +815,13 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   const int Hq = G * kHpg;
   const int64_t base = ((int64_t)sq * max_ctx * G + key0 * G + g) * kHeadDim;
   stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(kBlock, max_ctx - key0), wave, 4);
-  QueryGroup<1, 8> qg;
+  QueryGroup<1> qg;
   if (wave == 0) load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
   wait_loads();
   __syncthreads();
   if (wave != 0) return;
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
-  scores(qg, lds, 0);
-  softmax_pv<true, true>(qg, lds, lim, scale_log2, 0, 0);
+  attend_block<true, true>(qg, lds, lim, scale_log2, [] {});
   store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                 part_lse + (int64_t)item * kHpg);
 }
