@@ -86,20 +86,29 @@ def decode_bytes(ctx_lens, topk=TOPK):
     return float(tot)
 
 
+# A 16-row unit's block is computed by the dense pass when at least this many
+# of the unit's rows selected it (all of them, if the unit has fewer); the
+# library's split rule (kDenseMin in its launch header).
+DENSE_MIN = 6
+
+
 def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
     """Split the selected (query, group, block) pairs of a prefill into the
-    two attention passes, as the library does: a pair is "dense" when every row
-    of its 16-row unit selected the block, else it is computed KV-outer.
-    Returns per-pass pair counts, algorithmic flops (4*d*hpg per attended key)
-    and the number of distinct (group, block) K/V blocks each pass touches.
-    sel: [G, n, k] int32 on the device (-1 = no selection)."""
+    two attention passes, as the library does: a pair is "dense" when at least
+    min(DENSE_MIN, rows of the unit) rows of its 16-row unit selected the block,
+    else it is computed KV-outer. Returns per-pass pair counts, algorithmic
+    flops (4*d*hpg per attended key), the number of distinct (group, block) K/V
+    blocks each pass touches, and the dense pass's (unit, block) count (it
+    computes all 16 rows of a unit against each, masking those that did not
+    select it). sel: [G, n, k] int32 on the device (-1 = no selection)."""
     ng, _, k = sel.shape
     dev = sel.device
     nb = (n + bk - 1) // bk
     nunits = (n + 15) // 16
     rows = torch.arange(n, device=dev)
     unit_rows = torch.clamp(n - torch.arange(nunits, device=dev) * 16, max=16)
-    st = {"dense_pairs": 0, "sparse_pairs": 0, "F_dense": 0.0, "F_sparse": 0.0, "kv_dense": 0, "kv_sparse": 0}
+    st = {"dense_pairs": 0, "sparse_pairs": 0, "F_dense": 0.0, "F_sparse": 0.0, "kv_dense": 0, "kv_sparse": 0,
+          "dense_unit_blocks": 0}
     for g in range(ng):
         s = sel[g].long()
         valid = s >= 0
@@ -107,7 +116,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
         bb = s[valid]
         key = (rr // 16) * nb + bb
         cnt = torch.bincount(key, minlength=nunits * nb).view(nunits, nb)
-        dense = (cnt == unit_rows[:, None]).view(-1)[key]
+        dense_ub = cnt >= torch.clamp(unit_rows, max=DENSE_MIN)[:, None]
+        dense = dense_ub.view(-1)[key]
+        st["dense_unit_blocks"] += int((dense_ub & (cnt > 0)).sum())
         keys = torch.where(bb == rr // bk, rr % bk + 1, torch.full_like(rr, bk)).double()
         fl = 4.0 * d * hpg * keys
         st["F_dense"] += float(fl[dense].sum())
@@ -346,6 +357,8 @@ def main():
             + ps["sparse_pairs"] * part_bytes)
     kernels = [kernel_roofline("k_attn_prefill (KV-outer)", stage["kv_outer_attn"], ps["F_sparse"], b_kv),
                kernel_roofline("k_attn_dense (dense + merge)", stage["dense_attn_merge"], ps["F_dense"], b_dm)]
+    # the dense pass's MFMA work including the masked rows of its unit blocks
+    kernels[1]["executed_tflop"] = round(ps["dense_unit_blocks"] * 16 * 4.0 * D * (HQ // G) * BK / 1e12, 4)
     dom = max(kernels, key=lambda r: r["ms"])
 
     res = {
@@ -380,7 +393,7 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3, calibrated)",
                      "algorithmic_bytes": round(dom["algorithmic_gb"] * 1e9)},
         "kernels": kernels,
-        "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse")},
+        "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse", "dense_unit_blocks")},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)

@@ -84,7 +84,7 @@ struct PrefillLayout {
   int64_t nch, Lc, nblk, e_cap, tile_cap, slots;
   int64_t nunits;
   size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, part_o, part_lse, dense_cnt,
-      dense_list, total;
+      dense_list, dense_qmask, dense_slots, total;
 };
 
 bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
@@ -113,7 +113,9 @@ bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
   L->part_lse = off;   off += up((size_t)L->slots * kHpg * sizeof(float));
   L->nunits = cdiv(L->W, 16);
   L->dense_cnt = off;  off += up((size_t)s.G * L->nunits * sizeof(int32_t));
-  L->dense_list = off; off += up((size_t)s.G * L->nunits * s.k * sizeof(int32_t));
+  L->dense_list = off; off += up((size_t)s.G * L->nunits * kDenseMax * sizeof(int32_t));
+  L->dense_qmask = off; off += up((size_t)s.G * L->nunits * kDenseMax * sizeof(int32_t));
+  L->dense_slots = off; off += up((size_t)s.G * L->W * sizeof(int32_t));
   L->total = off;
   return true;
 }
@@ -239,7 +241,8 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
                    at<int32_t>(workspace, L.chunkcnt), at<int32_t>(workspace, L.chunkoff),
                    at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
                    at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
-                   at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist, nunits};
+                   at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist,
+                   at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits};
       launch_csr_and_tiles(ca, hs);
       clk.mark();
       // 4. KV-outer attention over the pairs not shared by a whole unit
@@ -252,7 +255,8 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
       launch_attn_prefill(aa, hs);
       clk.mark();
       // 5. query-stationary attention over unit-shared blocks + merge
-      LaunchAttnDense da{qs, ks, vs, dcnt, dlist, selw, gstride, at<uint16_t>(workspace, L.part_o),
+      LaunchAttnDense da{qs, ks, vs, dcnt, dlist, at<int32_t>(workspace, L.dense_qmask),
+                         at<int32_t>(workspace, L.dense_slots), at<uint16_t>(workspace, L.part_o),
                          at<float>(workspace, L.part_lse), ow, lw, N, w0, (int)Wn, nunits, G, K, s.scale_log2};
       launch_attn_dense(da, hs);
       clk.mark();

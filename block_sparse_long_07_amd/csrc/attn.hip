@@ -2,11 +2,12 @@
 // organised KV-outer ("outer gather Q") [pnsm, section 7; yhxrc, 二;
 // yololab, "KV Outer Gather Q是什麼？"].
 //
-// Prefill has two passes. Blocks selected by every query of a 16-query unit
-// (the query's own block, sink-like or planted blocks) are computed
-// query-stationary: one workgroup per (unit, group) keeps the 16 queries' Q and
-// running softmax state in registers and streams the unit's shared blocks
-// through LDS (k_attn_dense). Every other (query, block) pair goes KV-outer: a
+// Prefill has two passes. Blocks selected by many queries of a 16-query unit
+// (the query's own block, sink-like or planted blocks, blocks a local run of
+// queries agrees on) are computed query-stationary: one workgroup per (unit,
+// group) keeps the 16 queries' Q and running softmax state in registers and
+// streams the unit's listed blocks through LDS, masking the rows that did not
+// select a block (k_attn_dense). Every other (query, block) pair goes KV-outer: a
 // persistent grid drains the tile queue built by the reverse index, a tile being
 // (group g, KV block b, up to 16 queries that selected b); the block is staged
 // once and each wave gathers the 16 query heads of a query (4 KiB, contiguous in
@@ -253,10 +254,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 //  * MASKED: the queries' own block; keys with index > lim[n] are masked. A
 //    half whose keys are all masked leaves the state unchanged (its max is
 //    -inf); key 0 of the own block is never masked.
+//  * skip (bit n): query n did not select the block; all its keys are masked
+//    (p = 0 through a reference of +inf in the exponent, max -inf).
 //  * after_qk() runs once the last S^T MFMA is issued (Q is no longer read).
 template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG, class F>
 __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, const int* lim, float scale_log2,
-                                             F after_qk) {
+                                             unsigned skip, F after_qk) {
   constexpr int QN = QG::kQN;
   constexpr int kExpValu = 21;  // VALU instructions of one exp_unit
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
@@ -274,6 +277,9 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
 #pragma unroll
   for (int t = 0; t < 4; ++t) ka[t] = lds_k(stage, 4 + t, 0, c, qd);
   half_max<MASKED>(s0, lim, 0, mx);
+#pragma unroll
+  for (int n = 0; n < QN; ++n)
+    if ((skip >> n) & 1u) mx[n] = -__builtin_inff();
   if (FIRST) {
 #pragma unroll
     for (int n = 0; n < QN; ++n) qg.m[n] = mx[n];
@@ -284,8 +290,9 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
     if (__any(need)) {
 #pragma unroll
       for (int n = 0; n < QN; ++n) {
+        // alpha = 1 where the reference stays (also for m = mx = -inf)
         const float mnew = fmaxf(qg.m[n], mx[n]);
-        const float alpha = __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
+        const float alpha = mnew == qg.m[n] ? 1.0f : __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
 #pragma unroll
         for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha;
         qg.m[n] = mnew;
@@ -297,7 +304,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
   {
 #pragma unroll
     for (int n = 0; n < QN; ++n) {
-      mc[n] = qg.m[n] * scale_log2;
+      mc[n] = ((skip >> n) & 1u) ? __builtin_inff() : qg.m[n] * scale_log2;
 #pragma unroll
       for (int t = 0; t < 4; ++t) s1[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
@@ -323,6 +330,9 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
   }
   after_qk();
   half_max<MASKED>(s1, lim, 1, mx);
+#pragma unroll
+  for (int n = 0; n < QN; ++n)
+    if ((skip >> n) & 1u) mx[n] = -__builtin_inff();
   {
     bool need = false;
 #pragma unroll
@@ -332,7 +342,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
 #pragma unroll
       for (int n = 0; n < QN; ++n) {
         const float mnew = fmaxf(qg.m[n], mx[n]);
-        alpha[n] = __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
+        alpha[n] = mnew == qg.m[n] ? 1.0f : __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
         if (!FIRST) {
 #pragma unroll
           for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha[n];
@@ -348,7 +358,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
     const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
     const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
 #pragma unroll
-    for (int n = 0; n < QN; ++n) mc[n] = qg.m[n] * scale_log2;
+    for (int n = 0; n < QN; ++n) mc[n] = ((skip >> n) & 1u) ? __builtin_inff() : qg.m[n] * scale_log2;
     // region r = 2*st + hh covers d-tiles 4hh .. 4hh+3 (+ the ones tile) of
     // key step st and reads the next region's V^T operands
 #pragma unroll
@@ -570,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const lds_char* stage = lds + (j & 1) * kStage;
     if (e0 < cur.len) {
       // once the scores no longer need Q, the next tile's is loaded
-      attend_block<true, false>(qg, stage, nullptr, scale_log2, [&]() {
+      attend_block<true, false>(qg, stage, nullptr, scale_log2, 0u, [&]() {
         if (next_work) fetch_q(nent, nxt.g);
       });
 #pragma unroll
@@ -595,21 +605,23 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   }
 }
 
-// Dense part and final merge: blocks selected by every query of a 16-query
-// unit are computed query-stationary (FlashAttention-style online softmax over
-// the unit's shared blocks; each block is staged once for all 16 queries, the
-// next one streaming into the other stage meanwhile). One workgroup of 8 waves
-// per (unit, group), two queries per wave. The list always ends with the
-// unit's own block, the only one that needs the causal mask. This pass runs
-// after the KV-outer pass and merges its partials (the slots of the query's
-// selection that are not shared by the unit) into the same online state, so
+// Dense part and final merge: blocks selected by at least kDenseMin rows of a
+// 16-query unit (by all of them, if the unit has fewer) are computed
+// query-stationary (FlashAttention-style online softmax over the unit's list;
+// each block is staged once for all 16 queries, the next one streaming into
+// the other stage meanwhile). Rows that did not select a listed block are
+// masked for it; a wave whose two rows both did not skips it. One workgroup of
+// 8 waves per (unit, group), two queries per wave. The list always ends with
+// the unit's own block, the only one that needs the causal mask. This pass
+// runs after the KV-outer pass and merges its partials (the slots of the
+// query's selection outside the unit's list) into the same online state, so
 // every row's output and lse are written here, once, without atomics (the
 // second phase of the two-phase combine [pnsm, section 7]):
 //   out = o / l,   lse = (m*c + log2 l) * ln 2.
 __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ dense_cnt, const int32_t* __restrict__ dense_list,
-    const int32_t* __restrict__ sel, int64_t sel_gstride, const uint16_t* __restrict__ part_o,
+    const int32_t* __restrict__ dense_qmask, const int32_t* __restrict__ dense_slots, const uint16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t n_tokens,
     int64_t row0, int nrows, int nunits, int G, int topk, float scale_log2) {
   // two K/V stages, then one 4 KiB partial slot per wave (160 KiB in all)
@@ -620,15 +632,16 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
-  const int32_t* list = dense_list + ((int64_t)g * nunits + unit) * topk;
+  const int64_t list0 = ((int64_t)g * nunits + unit) * kDenseMax;
   const int i_rel0 = unit * 16 + wave * kAttnQN;
   const int b_loc = (int)((row0 + unit * 16) / kBlock);
   const int nsel = min(topk, b_loc + 1);
 
-  // independent loads first: the unit's list (lane j holds entry j, read back
-  // with a uniform readlane; entries past the count are not used), its count,
-  // and the queries' Q
-  const int lane_blk = lane < topk ? list[lane] : 0;
+  // independent loads first: the unit's list and the rows that selected each
+  // entry (lane j holds entry j, read back with a uniform readlane; entries
+  // past the count are not used), its count, and the queries' Q
+  const int lane_blk = dense_list[list0 + lane];
+  const int lane_qm = dense_qmask[list0 + lane];
   const int nd = dense_cnt[g * nunits + unit];  // >= 1: the unit's own block
   QueryGroup<kAttnQN> qg;
 #pragma unroll
@@ -641,23 +654,16 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
                 (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
   }
-  // slots of each query's selection not covered by the dense list (computed
-  // KV-outer): lane u < nsel tests its block, a ballot gives the wave-uniform
-  // mask
+  // slots of each query's selection computed KV-outer: the valid ones the
+  // dense pass does not cover
   uint64_t use[kAttnQN];
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int i_rel = i_rel0 + n;
     use[n] = 0ull;
-    if (i_rel < nrows && nd < nsel) {
-      bool sparse = false;
-      if (lane < nsel) {
-        const int b = sel[(int64_t)g * sel_gstride + (int64_t)i_rel * topk + lane];
-        sparse = true;
-        for (int j = 0; j < nd; ++j) sparse &= (__builtin_amdgcn_readlane(lane_blk, j) != b);
-      }
-      use[n] = __ballot(sparse);
-    }
+    if (i_rel < nrows)
+      use[n] = (uint64_t)(uint32_t)(__builtin_amdgcn_readfirstlane(~dense_slots[(int64_t)g * nrows + i_rel]) &
+                                    ((1 << nsel) - 1));
   }
   reset_state(qg);
 
@@ -703,7 +709,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim, rstride,
                 (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
     if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
-    attend_block<false, false>(qg, lds + (d & 1) * kStage, nullptr, scale_log2, [] {});
+    // queries of the wave that did not select the block are masked; a wave
+    // with none that did skips it
+    const unsigned skip =
+        ~((unsigned)__builtin_amdgcn_readlane(lane_qm, d) >> (wave * kAttnQN)) & ((1u << kAttnQN) - 1u);
+    if (skip != (1u << kAttnQN) - 1u)
+      attend_block<false, false>(qg, lds + (d & 1) * kStage, nullptr, scale_log2, skip, [] {});
     wait_lgkmcnt0();  // the slot is read out before it is refilled
     issue_slot();
   }
@@ -757,7 +768,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     int lim[kAttnQN];
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
-    attend_block<false, true>(qg, lds + last * kStage, lim, scale_log2, [] {});
+    attend_block<false, true>(qg, lds + last * kStage, lim, scale_log2, 0u, [] {});
   }
   wait_lgkmcnt0();  // the last block's stage is free
   asm volatile("" ::: "memory");
@@ -821,7 +832,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   __syncthreads();
   if (wave != 0) return;
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
-  attend_block<true, true>(qg, lds, lim, scale_log2, [] {});
+  attend_block<true, true>(qg, lds, lim, scale_log2, 0u, [] {});
   store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                 part_lse + (int64_t)item * kHpg);
 }
@@ -834,7 +845,7 @@ void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {
   if (a.nunits <= 0) return;
   hipLaunchKernelGGL(k_attn_dense, dim3(a.nunits, a.G), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v, a.dense_cnt, a.dense_list,
-                     a.sel, a.sel_gstride, a.part_o, a.part_lse, a.out, a.lse_out, a.n_tokens, a.row0, a.nrows,
+                     a.dense_qmask, a.dense_slots, a.part_o, a.part_lse, a.out, a.lse_out, a.n_tokens, a.row0, a.nrows,
                      a.nunits, a.G, a.topk, a.scale_log2);
 }
 

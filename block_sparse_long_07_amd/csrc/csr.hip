@@ -12,8 +12,11 @@
 //      (g, b, chunk) its output offset (and every list its start);
 //   3. the chunk pass is repeated and each entry lands at offset + popcount of
 //      the mask bits below its row.
-// Each list is then cut into tiles of at most `tile_q` queries, so a block hit
-// by very many queries (a sink-like block) becomes many independent tiles.
+// Pairs whose 16-row unit selected the block at least kDenseMin times are left
+// out: the dense pass computes them (k_csr_count also writes its per-unit
+// lists). Each list is then cut into tiles of at most `tile_q` queries, so a
+// block hit by very many queries (a sink-like block) becomes many independent
+// tiles.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -22,6 +25,7 @@ namespace msa {
 constexpr int kChunk = 64;       // rows per chunk (one 64-bit mask word)
 constexpr int kScanTile = 4096;  // elements per scan workgroup (256 threads x 16)
 constexpr int kUnit = 16;        // rows per dense unit
+static_assert(kDenseMin >= 4 && kUnit * kMaxTopk / kDenseMin <= kDenseMax, "a dense list fits kDenseMax entries");
 
 __device__ __forceinline__ void chunk_masks(const int32_t* __restrict__ sel, int64_t sel_gstride, int topk,
                                             int g, int i0, int nq, int bmax, unsigned long long* mask) {
@@ -35,8 +39,10 @@ __device__ __forceinline__ void chunk_masks(const int32_t* __restrict__ sel, int
   __syncthreads();
 }
 
-// Bits of `m` that belong to 16-row units of the chunk in which every valid row
-// selected the block: those (unit, block) pairs go to the dense pass.
+// Bits of `m` (rows of the chunk that selected a block) that belong to 16-row
+// units computing the block in the dense pass: at least min(kDenseMin, n) of
+// the unit's n valid rows selected it. All the unit's rows are set, selecting
+// or not (the dense pass masks the others).
 __device__ __forceinline__ unsigned long long dense_bits(unsigned long long m, int nq) {
   unsigned long long d = 0ull;
 #pragma unroll
@@ -44,8 +50,8 @@ __device__ __forceinline__ unsigned long long dense_bits(unsigned long long m, i
     const int r0 = s * kUnit;
     if (r0 >= nq) break;
     const int n = min(kUnit, nq - r0);
-    const unsigned long long full = ((n == 64) ? ~0ull : ((1ull << n) - 1ull)) << r0;
-    if ((m & full) == full) d |= full;
+    const unsigned long long full = ((1ull << n) - 1ull) << r0;
+    if (__popcll(m & full) >= min(kDenseMin, n)) d |= full;
   }
   return d;
 }
@@ -53,8 +59,10 @@ __device__ __forceinline__ unsigned long long dense_bits(unsigned long long m, i
 __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ sel, int64_t sel_gstride,
                                                    int topk, int64_t row0, int nrows, int nbw, int nch,
                                                    int32_t* __restrict__ chunkcnt, int32_t* __restrict__ dense_cnt,
-                                                   int32_t* __restrict__ dense_list, int nunits) {
+                                                   int32_t* __restrict__ dense_list, int32_t* __restrict__ dense_qmask,
+                                                   int32_t* __restrict__ dense_slots, int nunits) {
   extern __shared__ unsigned long long mask[];
+  __shared__ int cand[kChunk / kUnit][kDenseMax];
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int i0 = chunk * kChunk;
   const int nq = min(kChunk, nrows - i0);
@@ -68,20 +76,55 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
     }
     chunkcnt[((int64_t)g * nbw + b) * nch + chunk] = cnt;
   }
-  // dense list of each 16-row unit, in ascending block order: every shared block
-  // is among the first row's selections, which are ascending.
-  const int s = threadIdx.x;
-  if (s < kChunk / kUnit && s * kUnit < nq) {
-    const int unit = (i0 >> 4) + s;
-    const int32_t* row = sel + (int64_t)g * sel_gstride + (int64_t)(i0 + s * kUnit) * topk;
-    const int n = min(kUnit, nq - s * kUnit);
-    const unsigned long long full = ((1ull << n) - 1ull) << (s * kUnit);
-    int nd = 0;
+  const int32_t* srow0 = sel + (int64_t)g * sel_gstride + (int64_t)i0 * topk;
+  // per row: which of its slots the dense pass computes
+  if ((int)threadIdx.x < nq) {
+    const int t = threadIdx.x;
+    int bits = 0;
     for (int u = 0; u < topk; ++u) {
-      const int b = row[u];
-      if (b >= 0 && b <= bmax && (mask[b] & full) == full) dense_list[((int64_t)g * nunits + unit) * topk + nd++] = b;
+      const int b = srow0[t * topk + u];
+      if (b >= 0 && b <= bmax && ((dense_bits(mask[b], nq) >> t) & 1ull)) bits |= 1 << u;
     }
-    dense_cnt[g * nunits + unit] = nd;
+    dense_slots[(int64_t)g * nrows + i0 + t] = bits;
+  }
+  // dense list of each 16-row unit (wave s: unit s of the chunk): the distinct
+  // blocks its rows selected often enough, each taken from the first row that
+  // selected it, then ranked into ascending order
+  const int s = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool active = s * kUnit < nq;
+  const int n = active ? min(kUnit, nq - s * kUnit) : 0;
+  const unsigned long long full = ((1ull << n) - 1ull) << (s * kUnit);
+  int cnt = 0;
+  if (active) {
+    const int r = lane >> 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = 4 * (lane & 3) + j;
+      bool keep = false;
+      int b = -1;
+      if (r < n && u < topk) {
+        b = srow0[(s * kUnit + r) * topk + u];
+        if (b >= 0 && b <= bmax) {
+          const unsigned long long m = mask[b] & full;
+          keep = __popcll(m) >= min(kDenseMin, n) && __builtin_ctzll(m) == s * kUnit + r;
+        }
+      }
+      const unsigned long long bal = __ballot(keep);
+      if (keep) cand[s][cnt + __popcll(bal & ((1ull << lane) - 1ull))] = b;
+      cnt += __popcll(bal);
+    }
+  }
+  __syncthreads();
+  if (active) {
+    const int64_t base = ((int64_t)g * nunits + (i0 >> 4) + s) * kDenseMax;
+    if (lane < cnt) {
+      const int x = cand[s][lane];
+      int rank = 0;
+      for (int j = 0; j < cnt; ++j) rank += cand[s][j] < x;
+      dense_list[base + rank] = x;
+      dense_qmask[base + rank] = (int)((mask[x] & full) >> (s * kUnit));
+    }
+    if (lane == 0) dense_cnt[g * nunits + (i0 >> 4) + s] = cnt;
   }
 }
 
@@ -256,7 +299,7 @@ void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st) {
   const size_t lds = (size_t)a.nbw * sizeof(unsigned long long);
   dim3 grid(nch, a.G);
   hipLaunchKernelGGL(k_csr_count, grid, dim3(256), lds, st, a.sel, a.sel_gstride, a.topk, a.row0, a.nrows,
-                     a.nbw, nch, a.chunkcnt, a.dense_cnt, a.dense_list, a.nunits);
+                     a.nbw, nch, a.chunkcnt, a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.nunits);
   const int64_t n = (int64_t)a.G * a.nbw * nch;
   const int nblk = (int)((n + kScanTile - 1) / kScanTile);
   hipLaunchKernelGGL(k_scan_reduce, dim3(nblk), dim3(256), 0, st, a.chunkcnt, n, a.bsum);

@@ -11,6 +11,12 @@ constexpr int kIndexDim = 64;  // d_idx
 constexpr int kBlock = 128;    // B_k
 constexpr int kHpg = 16;       // query heads per GQA group
 constexpr int kMaxTopk = 16;
+// A 16-row unit's block goes to the query-stationary (dense) pass when at
+// least kDenseMin of the unit's rows selected it (all rows, if the unit has
+// fewer): the rows that did not are masked there, which costs less than
+// their KV-outer partials would. At most 16*16/kDenseMin blocks qualify.
+constexpr int kDenseMin = 6;
+constexpr int kDenseMax = 64;
 
 struct LaunchIndexPrefill {
   const uint16_t* q_idx;  // [n_tokens, G, 64] of one sequence
@@ -67,8 +73,10 @@ struct LaunchCsr {
   int32_t* tile_info;     // [0] tiles, [1] queue counter
   int tile_q;             // queries per tile
   int64_t tile_cap;
-  int32_t* dense_cnt;     // [G][nunits]: blocks shared by all queries of a 16-row unit
-  int32_t* dense_list;    // [G][nunits][topk], ascending
+  int32_t* dense_cnt;     // [G][nunits]: blocks a 16-row unit computes in the dense pass
+  int32_t* dense_list;    // [G][nunits][kDenseMax], ascending
+  int32_t* dense_qmask;   // [G][nunits][kDenseMax]: bit r = row r of the unit selected the block
+  int32_t* dense_slots;   // [G][nrows]: bit u = slot u of the row is computed in the dense pass
   int nunits;             // ceil(nrows / 16)
 };
 void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st);
@@ -95,8 +103,8 @@ struct LaunchAttnDense {
   const uint16_t* v;
   const int32_t* dense_cnt;
   const int32_t* dense_list;
-  const int32_t* sel;     // sel[g*sel_gstride + i_rel*topk + u]
-  int64_t sel_gstride;
+  const int32_t* dense_qmask;
+  const int32_t* dense_slots;
   const uint16_t* part_o; // KV-outer partials, merged into the output here
   const float* part_lse;
   uint16_t* out;          // window's first row
