@@ -71,10 +71,38 @@ __device__ __forceinline__ void stage_rows(lds_char* stage, const uint16_t* kr0,
   }
 }
 
-// A whole block (128 keys) per stage.
+// Per-lane byte offsets of a wave's staging loads, the same for every block:
+// slot s = 64*wave + lane of the layout above. A wave's next slots (64*nwaves
+// further) are 4*nwaves rows further with the same swizzle when nwaves is a
+// multiple of 4, so only the (uniform) base moves.
+struct StageOffsets {
+  uint32_t k, v;
+};
+
+__device__ __forceinline__ StageOffsets stage_offsets(int64_t rstride, int wave) {
+  const int s = wave * 64 + (threadIdx.x & 63);
+  const int r = s >> 4, p = s & 15;
+  const int ck = p ^ (r & 15);
+  const int cv = (((p >> 1) ^ (r & 7)) << 1) | (p & 1);
+  return {(uint32_t)(((int64_t)r * rstride + ck * 8) * 2), (uint32_t)(((int64_t)r * rstride + cv * 8) * 2)};
+}
+
+// A whole block (128 keys) per stage. A full block is loaded from uniform
+// bases and the precomputed offsets (nwaves a multiple of 4); a partial one
+// (the sequence's last) clamps its rows.
 __device__ __forceinline__ void stage_block(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
-                                            int64_t rstride, int nvalid, int wave, int nwaves) {
-  stage_rows<kBlock, kVOff>(stage, kr0, vr0, rstride, nvalid, wave, nwaves);
+                                            int64_t rstride, int nvalid, int wave, int nwaves,
+                                            const StageOffsets& off) {
+  if (nvalid < kBlock) {
+    stage_rows<kBlock, kVOff>(stage, kr0, vr0, rstride, nvalid, wave, nwaves);
+    return;
+  }
+  const int64_t rows_it = (int64_t)4 * nwaves * rstride;  // elements per iteration
+  for (int it = 0; it * 4 * nwaves < kBlock; ++it) {
+    const int s0 = wave * 64 + it * nwaves * 64;
+    lds_dma16_s(kr0 + it * rows_it, off.k, stage + s0 * 16);
+    lds_dma16_s(vr0 + it * rows_it, off.v, stage + kVOff + s0 * 16);
+  }
 }
 
 __device__ __forceinline__ void wait_loads() { wait_vmcnt0(); }
@@ -135,27 +163,46 @@ __device__ __forceinline__ void reset_state(QG& qg) {
 // Instruction classes of the scheduling hints (sched_group_barrier masks).
 constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
-// S^T = K_b . Q^T for key tiles 4h .. 4h+3 of the staged block (half h).
-template <int QN>
-__device__ __forceinline__ void qk_half(f32x4 (&s)[QN][4], const bf16x8 (&qop)[QN][4], const lds_char* stage,
-                                        int h) {
+// K operands of the first two d-steps of the first half of a staged block
+// (key tiles 0..3): read as one batch, as early as the caller can, so their
+// latency overlaps other work. The last two d-steps are read when the
+// contraction starts.
+constexpr int kPreSteps = 2;
+struct KHalf {
+  bf16x8 a[kPreSteps][4];  // [d-step][key tile]
+};
+
+__device__ __forceinline__ void load_k_half(KHalf& kh, const lds_char* stage) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
+#pragma unroll
+  for (int st = 0; st < kPreSteps; ++st)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kh.a[st][t] = lds_k(stage, t, st, c, qd);
+}
+
+// S^T = K_b . Q^T for key tiles 0..3, the first d-steps from preloaded operands.
+template <int QN>
+__device__ __forceinline__ void qk_half0(f32x4 (&s)[QN][4], const bf16x8 (&qop)[QN][4], const KHalf& kh,
+                                         const lds_char* stage) {
+  const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
+  bf16x8 a[4 - kPreSteps][4];
+#pragma unroll
+  for (int st = kPreSteps; st < 4; ++st)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[st - kPreSteps][t] = lds_k(stage, t, st, c, qd);
 #pragma unroll
   for (int n = 0; n < QN; ++n)
 #pragma unroll
     for (int t = 0; t < 4; ++t) s[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   // d-step outer, key tile inner: 4*QN independent accumulators between two
-  // dependent MFMAs, and the four operand reads of a step are issued together.
+  // dependent MFMAs
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    bf16x8 a[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) a[t] = lds_k(stage, 4 * h + t, st, c, qd);
+  for (int st = 0; st < 4; ++st)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int n = 0; n < QN; ++n) s[n][t] = mfma16x16x32(a[t], qop[n][st], s[n][t]);
-  }
+      for (int n = 0; n < QN; ++n)
+        s[n][t] = mfma16x16x32(st < kPreSteps ? kh.a[st][t] : a[st - kPreSteps][t], qop[n][st], s[n][t]);
 }
 
 // Causal mask of half h (MASKED: keys with index > lim[n] get -inf) and the
@@ -172,10 +219,13 @@ __device__ __forceinline__ void half_max(f32x4 (&s)[QN][4], const int* lim, int 
         for (int r = 0; r < 4; ++r)
           if (16 * (4 * h + t) + 4 * qd + r > lim[n]) s[n][t][r] = -__builtin_inff();
     }
-    float x = -__builtin_inff();
+    float x = fmaxf(s[n][0][0], s[n][0][1]);
+    x = fmaxf(fmaxf(x, s[n][0][2]), s[n][0][3]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      x = fmaxf(fmaxf(x, fmaxf(s[n][t][0], s[n][t][1])), fmaxf(s[n][t][2], s[n][t][3]));
+    for (int t = 1; t < 4; ++t) {
+      x = fmaxf(fmaxf(x, s[n][t][0]), s[n][t][1]);
+      x = fmaxf(fmaxf(x, s[n][t][2]), s[n][t][3]);
+    }
     mx[n] = max_lane_groups(x);
   }
 }
@@ -256,10 +306,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 //    -inf); key 0 of the own block is never masked.
 //  * skip (bit n): query n did not select the block; all its keys are masked
 //    (p = 0 through a reference of +inf in the exponent, max -inf).
+//  * k0: the first half's K operands, from load_k_half on the same stage.
 //  * after_qk() runs once the last S^T MFMA is issued (Q is no longer read).
 template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG, class F>
-__device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, const int* lim, float scale_log2,
-                                             unsigned skip, F after_qk) {
+__device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, const KHalf& k0, const int* lim,
+                                             float scale_log2, unsigned skip, F after_qk) {
   constexpr int QN = QG::kQN;
   constexpr int kExpValu = 21;  // VALU instructions of one exp_unit
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
@@ -271,7 +322,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
   bf16x8 p0[QN][2], p1[QN][2];
   float mx[QN], mc[QN];
 
-  qk_half(s0, qg.qop, stage, 0);
+  qk_half0(s0, qg.qop, k0, stage);
   // operands of the first pipelined step, read before the max and the branch
   bf16x8 ka[4], va[8];
 #pragma unroll
@@ -410,46 +461,44 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[9], float m, floa
 // Issue the direct-to-LDS loads of one partial (4 KiB, copied as is) into
 // `dst`: four loads per wave.
 __device__ __forceinline__ void stage_partial(const uint16_t* src, lds_char* dst) {
-  const int lane = threadIdx.x & 63;
+  const uint32_t voff = (threadIdx.x & 63) * 16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) lds_dma16(src + j * 512 + lane * 8, dst + j * 1024);
+  for (int j = 0; j < 4; ++j) lds_dma16_s(src + j * 512, voff, dst + j * 1024);
+}
+
+// MFMA 16x16x16 bf16: lane (i, g) holds A[i][4g + j] and B[4g + j][i] (j < 4);
+// the result layout is that of the 16x16x32 product.
+__device__ __forceinline__ f32x4 mfma16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // A operand of the merge MFMA for d-tile dt of a staged partial X: lane (c,
-// qd) holds X[4qd + (j & 3)][16dt + c] at k = 8qd + j (the four heads of the
-// transposing read, twice). Lane i of a 16-lane group addresses head 4qd +
-// i/4, dims 16dt + 4(i%4) .. +3: the 8-byte piece at dt*512 + (16(i%4) + head)*8
-// of the fragment-order slot.
-__device__ __forceinline__ bf16x8 partial_operand(const lds_char* xs, int dt, int c, int qd) {
+// qd) holds X[4qd + j][16dt + c] at k = 4qd + j, read transposed: lane i of a
+// 16-lane group addresses head 4qd + i/4, dims 16dt + 4(i%4) .. +3, the 8-byte
+// piece at dt*512 + (16(i%4) + head)*8 of the fragment-order slot.
+__device__ __forceinline__ i16x4 partial_operand(const lds_char* xs, int dt, int c, int qd) {
   const int r = 4 * qd + (c >> 2);
-  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(xs + dt * 512 + (16 * (c & 3) + r) * 8));
-  const u32x2 u = __builtin_bit_cast(u32x2, x);
-  return as_bf16x8((u32x4){u[0], u[1], u[0], u[1]});
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(xs + dt * 512 + (16 * (c & 3) + r) * 8));
 }
 
-// B operand diag(w) paired with partial_operand: row k = 8qd + j of column
-// (head) c is nonzero only for 4qd + (j & 3) == c, where j < 4 carries the
-// bf16 rounding of w and j >= 4 the bf16 rounding of the remainder, so the
-// product carries w to about 16 bits.
-__device__ __forceinline__ bf16x8 diag_operand(float w, int c, int qd) {
-  const uint32_t hi = pack_bf16x2(w, 0.f) & 0xffffu;
-  const uint32_t lo = pack_bf16x2(w - bf2f(hi), 0.f) & 0xffffu;
-  const bool on = qd == (c >> 2);
-  const int sh = (c & 1) * 16;
-  const uint32_t h = on ? hi << sh : 0u, l = on ? lo << sh : 0u;
+// B operand diag(x) paired with partial_operand: row k = 4qd + j of column
+// (head) c is x at k == c, else 0; `bits` is x as bf16.
+__device__ __forceinline__ i16x4 diag_operand(uint32_t bits, int c, int qd) {
+  const uint32_t h = qd == (c >> 2) ? bits << ((c & 1) * 16) : 0u;
   const bool odd = (c & 2) != 0;
-  return as_bf16x8((u32x4){odd ? 0u : h, odd ? h : 0u, odd ? 0u : l, odd ? l : 0u});
+  return __builtin_bit_cast(i16x4, (u32x2){odd ? 0u : h, odd ? h : 0u});
 }
 
 // Merge of a normalised partial (staged at xs, lse2 lp for the lane's head)
 // into query n's running state (o, l = o[8], reference max m): o += w X^T and
-// l += w with w = 2^(lp - m*c), as nine MFMAs against diag(w) (the ones tile
-// adds w to l), after a lazy rescale of the state when lp exceeds m*c by more
-// than kLazy (a fresh state, m = -inf, takes m*c = lp).
+// l += w with w = 2^(lp - m*c), as MFMAs against diag(w_hi) and diag(w_lo),
+// the bf16 rounding of w and of its remainder (w to about 16 bits; the ones
+// tile adds w to l), after a lazy rescale of the state when lp exceeds m*c by
+// more than kLazy (a fresh state, m = -inf, takes m*c = lp).
 template <int N, class QG>
 __device__ __forceinline__ void merge_partial(QG& qg, const lds_char* xs, float lp, float scale_log2) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
-  bf16x8 a[8];
+  i16x4 a[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) a[dt] = partial_operand(xs, dt, c, qd);
   float mc = qg.m[N] * scale_log2;
@@ -461,12 +510,18 @@ __device__ __forceinline__ void merge_partial(QG& qg, const lds_char* xs, float 
     qg.m[N] = mnew / scale_log2;
     mc = mnew;
   }
-  const bf16x8 bw = diag_operand(__builtin_amdgcn_exp2f(lp - mc), c, qd);
+  const float w = __builtin_amdgcn_exp2f(lp - mc);
+  const uint32_t hi = pack_bf16x2(w, 0.f) & 0xffffu;
+  const uint32_t lo = pack_bf16x2(w - bf2f(hi), 0.f) & 0xffffu;
+  const i16x4 bh = diag_operand(hi, c, qd), bl = diag_operand(lo, c, qd);
   const uint32_t one2 = 0x3f803f80u;
-  const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
+  const i16x4 ones = __builtin_bit_cast(i16x4, (u32x2){one2, one2});
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) qg.o[N][dt] = mfma16x16x32(a[dt], bw, qg.o[N][dt]);
-  qg.o[N][8] = mfma16x16x32(ones, bw, qg.o[N][8]);
+  for (int dt = 0; dt < 8; ++dt) qg.o[N][dt] = mfma16x16x16(a[dt], bh, qg.o[N][dt]);
+  qg.o[N][8] = mfma16x16x16(ones, bh, qg.o[N][8]);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) qg.o[N][dt] = mfma16x16x16(a[dt], bl, qg.o[N][dt]);
+  qg.o[N][8] = mfma16x16x16(ones, bl, qg.o[N][8]);
 }
 
 // merge_partial into query pn (wave-uniform) of the group.
@@ -497,13 +552,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
   __shared__ int s_t[4];
   lds_char* lds = (lds_char*)lds_raw;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, qd = lane >> 4;
   const int T = tile_info[0];
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
   const int e0 = wave * kAttnQN;  // the wave's entries in every tile
 
+  const StageOffsets soff = stage_offsets(rstride, wave);
   struct Tile {
     int t, begin, len, g, b;
   };
@@ -521,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   auto stage_tile = [&](const Tile& d, lds_char* dst) {
     const int64_t key0 = (int64_t)d.b * kBlock;
     stage_block(dst, k + (key0 * G + d.g) * kHeadDim, v + (key0 * G + d.g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
+                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves, soff);
   };
   QueryGroup<kAttnQN> qg;
   auto fetch_q = [&](const int (&ent)[kAttnQN], int tg) {
@@ -559,6 +615,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();  // ... for every wave; the other stage is free; s_t visible
     asm volatile("" ::: "memory");
+    const lds_char* stage = lds + (j & 1) * kStage;
+    KHalf k0;
+    if (e0 < cur.len) load_k_half(k0, stage);
     // chunk c+1 is claimed when chunk c starts; it is first read two tiles
     // later (for tile kClaim*(c+1)), after at least one more barrier
     if (tid == 0 && j % kClaim == 0) s_t[(j / kClaim + 1) & 1] = atomicAdd(&tile_info[1], kClaim);
@@ -577,10 +636,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
       read_entries(nxt, nent);
       after_dma += kAttnQN + 4 * kAttnQN;  // entries, then their Q below
     }
-    const lds_char* stage = lds + (j & 1) * kStage;
     if (e0 < cur.len) {
       // once the scores no longer need Q, the next tile's is loaded
-      attend_block<true, false>(qg, stage, nullptr, scale_log2, 0u, [&]() {
+      attend_block<true, false>(qg, stage, k0, nullptr, scale_log2, 0u, [&]() {
         if (next_work) fetch_q(nent, nxt.g);
       });
 #pragma unroll
@@ -628,10 +686,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage + kAttnWaves * 4096];
   lds_char* lds = (lds_char*)lds_raw;
   const int unit = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
+  const StageOffsets soff = stage_offsets(rstride, wave);
   const int64_t list0 = ((int64_t)g * nunits + unit) * kDenseMax;
   const int i_rel0 = unit * 16 + wave * kAttnQN;
   const int b_loc = (int)((row0 + unit * 16) / kBlock);
@@ -652,7 +711,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   {
     const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(lane_blk) * kBlock;
     stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves);
+                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves, soff);
   }
   // slots of each query's selection computed KV-outer: the valid ones the
   // dense pass does not cover
@@ -705,16 +764,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   for (int d = 0; d + 1 < nd; ++d) {
     wait_loads();
     __syncthreads();  // stage d&1 and the slot complete; stage (d+1)&1 free
+    KHalf k0;
+    load_k_half(k0, lds + (d & 1) * kStage);
     const int64_t k2 = (int64_t)__builtin_amdgcn_readlane(lane_blk, d + 1) * kBlock;
     stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves);
+                (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves, soff);
     if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
     // queries of the wave that did not select the block are masked; a wave
     // with none that did skips it
     const unsigned skip =
         ~((unsigned)__builtin_amdgcn_readlane(lane_qm, d) >> (wave * kAttnQN)) & ((1u << kAttnQN) - 1u);
     if (skip != (1u << kAttnQN) - 1u)
-      attend_block<false, false>(qg, lds + (d & 1) * kStage, nullptr, scale_log2, skip, [] {});
+      attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [] {});
     wait_lgkmcnt0();  // the slot is read out before it is refilled
     issue_slot();
   }
@@ -762,13 +823,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   {
     wait_loads();
     __syncthreads();
+    KHalf k0;
+    load_k_half(k0, lds + last * kStage);
     if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
     wait_lgkmcnt0();  // the slot is read out: it holds the lse of the rounds
     issue_round(0, cA, nA0, nA1);
     int lim[kAttnQN];
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
-    attend_block<false, true>(qg, lds + last * kStage, lim, scale_log2, 0u, [] {});
+    attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [] {});
   }
   wait_lgkmcnt0();  // the last block's stage is free
   asm volatile("" ::: "memory");
@@ -820,19 +883,22 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   const int sq = item / (G * topk), g = (item / topk) % G;
   const int b = sel[item];
   if (b < 0) return;
-  const int tid = threadIdx.x, wave = tid >> 6, c = tid & 15, qd = (tid >> 4) & 3;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 15, qd = (tid >> 4) & 3;
   const int64_t i = ctx_lens[sq] - 1;
   const int64_t key0 = (int64_t)b * kBlock;
   const int Hq = G * kHpg;
   const int64_t base = ((int64_t)sq * max_ctx * G + key0 * G + g) * kHeadDim;
-  stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(kBlock, max_ctx - key0), wave, 4);
+  stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(kBlock, max_ctx - key0), wave, 4,
+              stage_offsets((int64_t)G * kHeadDim, wave));
   QueryGroup<1> qg;
   if (wave == 0) load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
   wait_loads();
   __syncthreads();
   if (wave != 0) return;
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
-  attend_block<true, true>(qg, lds, lim, scale_log2, 0u, [] {});
+  KHalf k0;
+  load_k_half(k0, lds);
+  attend_block<true, true>(qg, lds, k0, lim, scale_log2, 0u, [] {});
   store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                 part_lse + (int64_t)item * kHpg);
 }

@@ -77,6 +77,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, const lds_char* lds) 
                : "v"(src), "s"(lds_addr(lds))
                : "memory", "m0");
 }
+// The same load addressed as an SGPR base (wave-uniform; taken from the first
+// lane) plus a 32-bit per-lane byte offset: no per-lane 64-bit address
+// arithmetic.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t voff, const lds_char* lds) {
+  // readfirstlane returns int: both halves are widened from uint32_t (a sign
+  // extension of the low half would corrupt the high half)
+  const uint64_t u = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint64_t b = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(b), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4(const void* src, const lds_char* lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
