@@ -87,6 +87,25 @@ __device__ __forceinline__ StageOffsets stage_offsets(int64_t rstride, int wave)
   return {(uint32_t)(((int64_t)r * rstride + ck * 8) * 2), (uint32_t)(((int64_t)r * rstride + cv * 8) * 2)};
 }
 
+// Element offset of key block b, group g in a [tokens][G][128] K or V array,
+// from 32-bit uniform ints (blocks * 128 * G stays below 2^31).
+__device__ __forceinline__ uint64_t block_elems(int b, int G, int g) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(b * kBlock * G + g) * kHeadDim;
+}
+
+// Load i (0 .. 8*nwaves/4 - 1) of the fast path below: K (even i) or V (odd
+// i) of row group i/2; for spreading a full block's loads over compute.
+__device__ __forceinline__ void stage_piece(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
+                                            int64_t rstride, int wave, int nwaves, const StageOffsets& off, int i) {
+  const int it = i >> 1;
+  const int s0 = wave * 64 + it * nwaves * 64;
+  const int64_t e = (int64_t)it * 4 * nwaves * rstride;
+  if (i & 1)
+    lds_dma16_s(vr0 + e, off.v, stage + kVOff + s0 * 16);
+  else
+    lds_dma16_s(kr0 + e, off.k, stage + s0 * 16);
+}
+
 // A whole block (128 keys) per stage. A full block is loaded from uniform
 // bases and the precomputed offsets (nwaves a multiple of 4); a partial one
 // (the sequence's last) clamps its rows.
@@ -307,10 +326,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 //  * skip (bit n): query n did not select the block; all its keys are masked
 //    (p = 0 through a reference of +inf in the exponent, max -inf).
 //  * k0: the first half's K operands, from load_k_half on the same stage.
-//  * after_qk() runs once the last S^T MFMA is issued (Q is no longer read).
-template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG, class F>
+//  * hook(i) lets the caller place its own memory traffic in the block:
+//    i = 0..3 at the start of the d-steps of S1, i = 4 right after them (Q is
+//    no longer read from there on), i = 5..12 at the start of the PV regions.
+template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG, class H>
 __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, const KHalf& k0, const int* lim,
-                                             float scale_log2, unsigned skip, F after_qk) {
+                                             float scale_log2, unsigned skip, H hook) {
   constexpr int QN = QG::kQN;
   constexpr int kExpValu = 21;  // VALU instructions of one exp_unit
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
@@ -362,6 +383,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
     bf16x8 kn[4];
     static_for<0, 4>([&](auto ist) {
       constexpr int st = decltype(ist)::value;
+      hook(st);
       if constexpr (st < 3) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) kn[t] = lds_k(stage, 4 + t, st + 1, c, qd);
@@ -379,7 +401,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
       for (int t = 0; t < 4; ++t) ka[t] = kn[t];
     });
   }
-  after_qk();
+  hook(4);
   half_max<MASKED>(s1, lim, 1, mx);
 #pragma unroll
   for (int n = 0; n < QN; ++n)
@@ -417,6 +439,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
     static_for<0, 8>([&](auto ir) {
       constexpr int r = decltype(ir)::value, st = r >> 1, hh = r & 1;
       constexpr int nst = hh ? st + 1 : st, nd0 = hh ? 0 : 4;
+      hook(5 + r);
       if constexpr (nst < 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) va[nd0 + i] = lds_vt<VOFF>(stage, nd0 + i, nst, c, qd);
@@ -566,18 +589,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   auto read_tile = [&](int t) -> Tile {
     Tile d{t, 0, 0, 0, 0};
     if (t < T) {
-      const int l = tiles[4 * t];
+      d.g = tiles[4 * t];
       d.begin = tiles[4 * t + 1];
       d.len = tiles[4 * t + 2];
-      d.g = l / nbw;
-      d.b = l % nbw;
+      d.b = tiles[4 * t + 3];
     }
     return d;
   };
   auto stage_tile = [&](const Tile& d, lds_char* dst) {
-    const int64_t key0 = (int64_t)d.b * kBlock;
-    stage_block(dst, k + (key0 * G + d.g) * kHeadDim, v + (key0 * G + d.g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves, soff);
+    const uint64_t e = block_elems(d.b, G, d.g);
+    stage_block(dst, k + e, v + e, rstride, (int)min<int64_t>(kBlock, n_tokens - (int64_t)d.b * kBlock), wave,
+                kAttnWaves, soff);
   };
   QueryGroup<kAttnQN> qg;
   auto fetch_q = [&](const int (&ent)[kAttnQN], int tg) {
@@ -597,7 +619,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   constexpr int kClaim = 4;
   if (tid == 0) s_t[0] = atomicAdd(&tile_info[1], kClaim);
   __syncthreads();
-  auto tile_pos = [&](int jj) { return s_t[(jj / kClaim) & 1] + jj % kClaim; };
+  auto tile_pos = [&](int jj) { return __builtin_amdgcn_readfirstlane(s_t[(jj / kClaim) & 1] + jj % kClaim); };
   Tile cur = read_tile(tile_pos(0));
   Tile nxt = read_tile(tile_pos(1));
   int ent[kAttnQN] = {0, 0};
@@ -622,11 +644,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     // later (for tile kClaim*(c+1)), after at least one more barrier
     if (tid == 0 && j % kClaim == 0) s_t[(j / kClaim + 1) & 1] = atomicAdd(&tile_info[1], kClaim);
     const int t2 = tile_pos(j + 2);
-    int d2[3] = {0, 0, 0};
+    int d2[4] = {0, 0, 0, 0};
     if (t2 < T) {
       d2[0] = tiles[4 * t2];
       d2[1] = tiles[4 * t2 + 1];
       d2[2] = tiles[4 * t2 + 2];
+      d2[3] = tiles[4 * t2 + 3];
     }
     after_dma = 0;
     if (nxt.t < T) stage_tile(nxt, lds + ((j + 1) & 1) * kStage);
@@ -638,8 +661,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     }
     if (e0 < cur.len) {
       // once the scores no longer need Q, the next tile's is loaded
-      attend_block<true, false>(qg, stage, k0, nullptr, scale_log2, 0u, [&]() {
-        if (next_work) fetch_q(nent, nxt.g);
+      attend_block<true, false>(qg, stage, k0, nullptr, scale_log2, 0u, [&](int i) {
+        if (i == 4 && next_work) fetch_q(nent, nxt.g);
       });
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
@@ -658,8 +681,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     nxt.t = t2;
     nxt.begin = d2[1];
     nxt.len = d2[2];
-    nxt.g = d2[0] / nbw;
-    nxt.b = d2[0] % nbw;
+    nxt.g = d2[0];
+    nxt.b = d2[3];
   }
 }
 
@@ -709,56 +732,65 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     load_q(qg, n, q + ((i * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
   }
   {
-    const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(lane_blk) * kBlock;
-    stage_block(lds, k + (key0 * G + g) * kHeadDim, v + (key0 * G + g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - key0), wave, kAttnWaves, soff);
+    const int b0 = __builtin_amdgcn_readfirstlane(lane_blk);
+    const uint64_t e0 = block_elems(b0, G, g);
+    stage_block(lds, k + e0, v + e0, rstride, (int)min<int64_t>(kBlock, n_tokens - (int64_t)b0 * kBlock), wave,
+                kAttnWaves, soff);
   }
   // slots of each query's selection computed KV-outer: the valid ones the
   // dense pass does not cover
-  uint64_t use[kAttnQN];
+  uint32_t use[kAttnQN];
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
     const int i_rel = i_rel0 + n;
-    use[n] = 0ull;
+    use[n] = 0u;
     if (i_rel < nrows)
-      use[n] = (uint64_t)(uint32_t)(__builtin_amdgcn_readfirstlane(~dense_slots[(int64_t)g * nrows + i_rel]) &
-                                    ((1 << nsel) - 1));
+      use[n] = (uint32_t)__builtin_amdgcn_readfirstlane(~dense_slots[(int64_t)g * nrows + i_rel]) &
+               ((1u << nsel) - 1u);
   }
   reset_state(qg);
 
   // KV-outer partials of the wave's queries, in (query, slot) order. One at a
-  // time streams into the wave's slot while a dense block is computed and is
-  // merged at the start of the next block; the rest go through the two larger
+  // time streams into the wave's slot while a dense block is computed (issued
+  // once the previous one is merged, at the start of the block) and is merged
+  // at the start of the next block; the rest go through the two larger
   // regions after the last block (below).
   lds_char* pslot = lds + 2 * kStage + wave * 4096;
+  // (wave-uniform bookkeeping, kept in scalar registers; slot indices fit 32
+  // bits: rows * G * topk of a window)
   int cur_n = 0;
-  uint64_t cur_rem = use[0];
+  uint32_t cur_rem = use[0];
   auto next_pair = [&](int& pn, int64_t& slot) -> bool {
 #pragma unroll
     for (int n = 1; n < kAttnQN; ++n)
-      if (cur_rem == 0ull && cur_n == n - 1) {
+      if (cur_rem == 0u && cur_n == n - 1) {
         cur_n = n;
         cur_rem = use[n];
       }
-    if (cur_rem == 0ull) return false;
-    const int pu = __builtin_ctzll(cur_rem);
-    cur_rem &= cur_rem - 1;
+    if (cur_rem == 0u) return false;
+    const int pu = __builtin_ctz(cur_rem);
+    cur_rem &= cur_rem - 1u;
     pn = cur_n;
-    slot = ((int64_t)(i_rel0 + cur_n) * G + g) * topk + pu;
+    slot = (uint32_t)__builtin_amdgcn_readfirstlane(((i_rel0 + cur_n) * G + g) * topk + pu);
     return true;
   };
   int pend_n = -1;       // query of the partial in the slot (-1: none)
   float pend_lse = 0.f;  // its lse2 for the lane's head
-  auto issue_slot = [&]() {
+  int64_t pend_slot = 0;
+  // picks the next partial for the slot (pend_n, pend_slot); its loads are
+  // issued by slot_piece(0..3) and its lse with piece 0
+  auto take_slot = [&]() {
     int pn = 0;
-    int64_t slot = 0;
-    pend_n = -1;
-    if (!next_pair(pn, slot)) return;
-    stage_partial(part_o + slot * (kHpg * kHeadDim), pslot);
-    pend_lse = part_lse[slot * kHpg + c];
-    pend_n = pn;
+    pend_n = next_pair(pn, pend_slot) ? pn : -1;
   };
-  issue_slot();
+  auto slot_piece = [&](int j) {
+    if (pend_n < 0) return;
+    lds_dma16_s(part_o + pend_slot * (kHpg * kHeadDim) + j * 512, (uint32_t)lane * 16, pslot + j * 1024);
+    if (j == 0) pend_lse = part_lse[pend_slot * kHpg + c];
+  };
+  take_slot();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) slot_piece(j);
 
   // shared older blocks (unmasked), then the unit's own block (masked)
   for (int d = 0; d + 1 < nd; ++d) {
@@ -766,18 +798,29 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     __syncthreads();  // stage d&1 and the slot complete; stage (d+1)&1 free
     KHalf k0;
     load_k_half(k0, lds + (d & 1) * kStage);
-    const int64_t k2 = (int64_t)__builtin_amdgcn_readlane(lane_blk, d + 1) * kBlock;
-    stage_block(lds + ((d + 1) & 1) * kStage, k + (k2 * G + g) * kHeadDim, v + (k2 * G + g) * kHeadDim, rstride,
-                (int)min<int64_t>(kBlock, n_tokens - k2), wave, kAttnWaves, soff);
-    if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
+    // block d+1 streams into the other stage, loaded by waves 0-3 only (one
+    // per SIMD): their partners start computing while they wait for room in
+    // the memory queue
+    const int b2 = __builtin_amdgcn_readlane(lane_blk, d + 1);
+    const uint64_t e2 = block_elems(b2, G, g);
+    if (wave < 4)
+      stage_block(lds + ((d + 1) & 1) * kStage, k + e2, v + e2, rstride,
+                  (int)min<int64_t>(kBlock, n_tokens - (int64_t)b2 * kBlock), wave, 4, soff);
+    // merge the slot's partial, then refill the slot right away: the load has
+    // the whole block's compute to arrive
+    if (pend_n >= 0) {
+      merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
+      wait_lgkmcnt0();  // the slot is read out before it is refilled
+    }
+    take_slot();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) slot_piece(j);
     // queries of the wave that did not select the block are masked; a wave
     // with none that did skips it
     const unsigned skip =
         ~((unsigned)__builtin_amdgcn_readlane(lane_qm, d) >> (wave * kAttnQN)) & ((1u << kAttnQN) - 1u);
     if (skip != (1u << kAttnQN) - 1u)
-      attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [] {});
-    wait_lgkmcnt0();  // the slot is read out before it is refilled
-    issue_slot();
+      attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [](int) {});
   }
 
   // The remaining partials stream through two 8 KiB LDS regions of the wave
@@ -831,7 +874,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     int lim[kAttnQN];
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
-    attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [] {});
+    attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [](int) {});
   }
   wait_lgkmcnt0();  // the last block's stage is free
   asm volatile("" ::: "memory");
@@ -898,7 +941,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
   KHalf k0;
   load_k_half(k0, lds);
-  attend_block<true, true>(qg, lds, k0, lim, scale_log2, 0u, [] {});
+  attend_block<true, true>(qg, lds, k0, lim, scale_log2, 0u, [](int) {});
   store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                 part_lse + (int64_t)item * kHpg);
 }

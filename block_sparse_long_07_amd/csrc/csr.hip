@@ -269,7 +269,7 @@ __global__ __launch_bounds__(1024) void k_tiles_count(const int32_t* __restrict_
 }
 
 __global__ __launch_bounds__(256) void k_tiles_fill(const int32_t* __restrict__ tile_start,
-                                                    const int32_t* __restrict__ chunkoff, int nch, int L,
+                                                    const int32_t* __restrict__ chunkoff, int nch, int L, int nbw,
                                                     int tile_q, const int32_t* __restrict__ tile_info,
                                                     int64_t tile_cap, int32_t* __restrict__ tiles) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -288,10 +288,10 @@ __global__ __launch_bounds__(256) void k_tiles_fill(const int32_t* __restrict__ 
   const int begin = start + j * tile_q;
   const int len = min(tile_q, cnt - j * tile_q);
   int32_t* o = tiles + t * 4;
-  o[0] = l;
+  o[0] = l / nbw;  // group
   o[1] = begin;
   o[2] = len;
-  o[3] = 0;
+  o[3] = l % nbw;  // block
 }
 
 void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st) {
@@ -311,7 +311,7 @@ void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st) {
   hipLaunchKernelGGL(k_tiles_count, dim3(1), dim3(1024), 0, st, a.chunkoff, nch, L, a.tile_q, a.tile_start,
                      a.tile_info);
   const int fill_blocks = (int)((a.tile_cap + 255) / 256);
-  hipLaunchKernelGGL(k_tiles_fill, dim3(fill_blocks), dim3(256), 0, st, a.tile_start, a.chunkoff, nch, L,
+  hipLaunchKernelGGL(k_tiles_fill, dim3(fill_blocks), dim3(256), 0, st, a.tile_start, a.chunkoff, nch, L, a.nbw,
                      a.tile_q, a.tile_info, a.tile_cap, a.tiles);
 }
 

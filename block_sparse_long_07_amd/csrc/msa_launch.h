@@ -69,7 +69,7 @@ struct LaunchCsr {
   int32_t* bsum;          // scan scratch
   int32_t* entries;
   int32_t* tile_start;    // [G*nbw + 1]
-  int32_t* tiles;         // [T_cap][4] = (list, begin, len, 0)
+  int32_t* tiles;         // [T_cap][4] = (group, begin, len, block)
   int32_t* tile_info;     // [0] tiles, [1] queue counter
   int tile_q;             // queries per tile
   int64_t tile_cap;
