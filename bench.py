@@ -135,9 +135,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "778f3394e850d7e2",
-    "k_attn_prefill (KV-outer)": 8.038e9,
-    "k_attn_dense (dense + merge)": 5.670e9,
+    "source": "1b544b9566419ad8",
+    "k_attn_prefill (KV-outer)": 4.792e9,
+    "k_attn_dense (dense + merge)": 4.127e9,
 }
 
 

@@ -4,7 +4,8 @@
 // Prefill, per sequence and per window of up to kWindowMax query rows:
 //   index scores -> top-k selection -> reverse index + tile schedule ->
 //   persistent KV-outer attention -> query-stationary attention over the
-//   unit-shared blocks, which merges the KV-outer partials (combine).
+//   blocks each 16-row unit shares, which merges the KV-outer partials
+//   (combine).
 // Windows bound the workspace (block scores and partials grow with the rows of
 // a window, not with the sequence), which is what makes 1M-token prefill fit.
 // Decode: index scores -> selection -> per-(sequence, group, slot) attention ->
@@ -254,7 +255,7 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
                            (int)std::min<int64_t>(cu_count(), tile_cap)};
       launch_attn_prefill(aa, hs);
       clk.mark();
-      // 5. query-stationary attention over unit-shared blocks + merge
+      // 5. query-stationary attention over the units' shared blocks + merge
       LaunchAttnDense da{qs, ks, vs, dcnt, dlist, at<int32_t>(workspace, L.dense_qmask),
                          at<int32_t>(workspace, L.dense_slots), at<uint16_t>(workspace, L.part_o),
                          at<float>(workspace, L.part_lse), ow, lw, N, w0, (int)Wn, nunits, G, K, s.scale_log2};

@@ -121,8 +121,8 @@ msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx,
  * return in stage_ms the duration of each stage, summed over sequences and
  * windows:
  *   prefill (5): index scores, top-k selection, reverse index + tile schedule,
- *                KV-outer attention, attention over unit-shared blocks with
- *                the merge of the KV-outer partials (combine)
+ *                KV-outer attention, attention over the blocks each 16-row
+ *                unit shares with the merge of the KV-outer partials (combine)
  *   decode  (4): index scores, top-k selection, attention, combine
  * stage_ms must not be NULL (MSA_ERR_INVALID_ARG). */
 msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len,
