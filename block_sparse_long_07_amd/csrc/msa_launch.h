@@ -15,7 +15,7 @@ constexpr int kMaxTopk = 16;
 // least kDenseMin of the unit's rows selected it (all rows, if the unit has
 // fewer): the rows that did not are masked there, which costs less than
 // their KV-outer partials would. At most 16*16/kDenseMin blocks qualify.
-constexpr int kDenseMin = 6;
+constexpr int kDenseMin = 7;
 constexpr int kDenseMax = 64;
 
 struct LaunchIndexPrefill {
