@@ -80,16 +80,18 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
 #pragma unroll
     for (int x = 0; x < kKC; ++x) res[j][x] = -__builtin_inff();
 
-#pragma unroll 1
-  for (int kb = kb0; kb < kb1; ++kb) {
+  // fully unrolled over the chunk's blocks, so every pooled maximum lands in
+  // a fixed register (the block position x is a constant)
+#pragma unroll
+  for (int x = 0; x < kKC; ++x) {
+    const int kb = kb0 + x;
+    if (kb >= kb1) break;
     wait_vmcnt0();
     __syncthreads();  // block kb staged; the other stage is free
     if (kb + 1 < kb1)
-      stage_kidx(lds + ((kb + 1 - kb0) & 1) * 16384, k_idx + (int64_t)(kb + 1) * kBlock * kIndexDim, wave);
-    const lds_char* st = lds + ((kb - kb0) & 1) * 16384;
+      stage_kidx(lds + ((x + 1) & 1) * 16384, k_idx + (int64_t)(kb + 1) * kBlock * kIndexDim, wave);
+    const lds_char* st = lds + (x & 1) * 16384;
     float mx[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) mx[rt] = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int r = 16 * t + c;
@@ -102,20 +104,21 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mfma16x16x32(a0, qop[rt][0], acc);
         acc = mfma16x16x32(a1, qop[rt][1], acc);
-        mx[rt] = fmaxf(fmaxf(mx[rt], fmaxf(acc[0], acc[1])), fmaxf(acc[2], acc[3]));
+        float m = t == 0 ? fmaxf(acc[0], acc[1]) : fmaxf(fmaxf(mx[rt], acc[0]), acc[1]);
+        mx[rt] = fmaxf(fmaxf(m, acc[2]), acc[3]);
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      mx[rt] = max_lane_groups(mx[rt]);
-    }
+    for (int rt = 0; rt < RT; ++rt) mx[rt] = max_lane_groups(mx[rt]);
     // all four lane groups now hold the block maxima; group qd keeps tiles rt = qd mod 4
-    const int x = kb - kb0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int j = 0; j < (RT + 3) / 4; ++j) {
+      float v = mx[4 * j];
 #pragma unroll
-      for (int xx = 0; xx < kKC; ++xx)
-        if ((rt & 3) == qd && xx == x) res[rt >> 2][xx] = mx[rt];
+      for (int u = 1; u < 4; ++u)
+        if (4 * j + u < RT) v = qd == u ? mx[4 * j + u] : v;
+      res[j][x] = v;
+    }
   }
   const int nkb = kb1 - kb0;
 #pragma unroll
