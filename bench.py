@@ -135,9 +135,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "1b544b9566419ad8",
-    "k_attn_prefill (KV-outer)": 4.792e9,
-    "k_attn_dense (dense + merge)": 4.127e9,
+    "source": "7706e5b2ee1fbe89",
+    "k_attn_prefill (KV-outer)": 5.341e9,
+    "k_attn_dense (dense + merge)": 4.373e9,
 }
 
 
