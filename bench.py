@@ -255,6 +255,62 @@ def cpu_baseline(pin, budget_s=15.0):
                       f"float64 numpy), {spent:.1f}s of oracle time"}
 
 
+# ---- serving shapes (msa_prefill_varlen) --------------------------------------
+
+def _time_calls(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def serving_shapes(torch, msa, pre, topk, reps, n_chunks=4, varlen_lens=(8192, 6144, 4096, 2048)):
+    """The 32K sequence prefilled as n_chunks chunks, each against the cache
+    the previous ones filled, and a batch of prompts of mixed lengths (rows of
+    the same tensors, one cache per prompt). Throughput = attended-token flops
+    (the same F_main definition) / wall time of the calls."""
+    q, k, v, qi, ki = (t[0] for t in pre)
+    n = q.shape[0]
+    step = n // n_chunks
+    bounds = [(a, min(n, a + step)) for a in range(0, n, step)]
+    p = msa.params(HQ, G, D, DI, BK, topk)
+    ws = torch.empty(msa.prefill_varlen_workspace_bytes(p, step, n), dtype=torch.uint8, device=q.device)
+    outs = [torch.empty((b - a, HQ, D), dtype=torch.bfloat16, device=q.device) for a, b in bounds]
+    qs = [q[a:b].contiguous() for a, b in bounds]
+    qis = [qi[a:b].contiguous() for a, b in bounds]
+
+    def chunks():
+        for (a, b), qc, qic, o in zip(bounds, qs, qis, outs):
+            msa.prefill_varlen(qc, qic, k[None], v[None], ki[None], [a], [b - a], topk=topk, workspace=ws, out=o)
+
+    ms_c = _time_calls(torch, chunks, reps)
+    f_c = prefill_flops_full(n, topk=topk)
+    chunked = {"chunks": len(bounds), "chunk_rows": step, "ms": round(ms_c, 4),
+               "tflops": round(f_c / (ms_c * 1e-3) / 1e12, 2)}
+
+    seg = max(varlen_lens)
+    B = len(varlen_lens)
+    assert B * seg <= n
+    kc, vc, kic = (t[:B * seg].reshape((B, seg) + tuple(t.shape[1:])) for t in (k, v, ki))
+    vq = torch.cat([q[b * seg:b * seg + L] for b, L in enumerate(varlen_lens)]).contiguous()
+    vqi = torch.cat([qi[b * seg:b * seg + L] for b, L in enumerate(varlen_lens)]).contiguous()
+    ws2 = torch.empty(msa.prefill_varlen_workspace_bytes(p, seg, seg), dtype=torch.uint8, device=q.device)
+    vout = torch.empty_like(vq)
+
+    def batch():
+        msa.prefill_varlen(vq, vqi, kc, vc, kic, [0] * B, list(varlen_lens), topk=topk, workspace=ws2, out=vout)
+
+    ms_v = _time_calls(torch, batch, reps)
+    f_v = sum(prefill_flops_full(L, topk=topk) for L in varlen_lens)
+    varlen = {"q_lens": list(varlen_lens), "ms": round(ms_v, 4), "tflops": round(f_v / (ms_v * 1e-3) / 1e12, 2)}
+    return chunked, varlen
+
+
 # ---- main ---------------------------------------------------------------------
 
 def main():
@@ -361,6 +417,8 @@ def main():
     kernels[1]["executed_tflop"] = round(ps["dense_unit_blocks"] * 16 * 4.0 * D * (HQ // G) * BK / 1e12, 4)
     dom = max(kernels, key=lambda r: r["ms"])
 
+    chunked, varlen = serving_shapes(torch, msa, pre, TOPK, args.steps)
+
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -394,6 +452,8 @@ def main():
                      "algorithmic_bytes": round(dom["algorithmic_gb"] * 1e9)},
         "kernels": kernels,
         "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse", "dense_unit_blocks")},
+        "chunked_prefill": chunked,
+        "varlen_prefill": varlen,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)

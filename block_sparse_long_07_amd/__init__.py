@@ -20,9 +20,9 @@ MSA_OK = 0
 _STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_UNSUPPORTED",
            -3: "MSA_ERR_WORKSPACE_TOO_SMALL", -4: "MSA_ERR_HIP"}
 
-EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_decode_workspace_bytes", "msa_decode",
-            "msa_prefill_profiled", "msa_decode_profiled", "msa_index_scores", "msa_select_blocks",
-            "msa_status_string")
+EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_prefill_varlen_workspace_bytes",
+            "msa_prefill_varlen", "msa_decode_workspace_bytes", "msa_decode", "msa_prefill_profiled",
+            "msa_decode_profiled", "msa_index_scores", "msa_select_blocks", "msa_status_string")
 PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
 DECODE_STAGES = ("index_score", "select", "attn", "combine")
 
@@ -58,6 +58,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_prefill_workspace_bytes.restype = sz
     lib.msa_prefill.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_prefill.restype = ctypes.c_int
+    lib.msa_prefill_varlen_workspace_bytes.argtypes = [P, i64, i64]
+    lib.msa_prefill_varlen_workspace_bytes.restype = sz
+    lib.msa_prefill_varlen.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_prefill_varlen.restype = ctypes.c_int
     lib.msa_decode_workspace_bytes.argtypes = [P, i32, i64]
     lib.msa_decode_workspace_bytes.restype = sz
     lib.msa_decode.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -141,6 +145,53 @@ def prefill(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale=Non
         ms = (ctypes.c_float * len(PREFILL_STAGES))()
         _check(lib.msa_prefill_profiled(*args, ms), "msa_prefill_profiled")
         stage_ms.extend(float(x) for x in ms)
+    return out, sel, lse
+
+
+def prefill_varlen_workspace_bytes(p: MsaParams, max_q_len: int, max_ctx: int) -> int:
+    return int(load().msa_prefill_varlen_workspace_bytes(ctypes.byref(p), max_q_len, max_ctx))
+
+
+def prefill_varlen(q, q_idx, k_cache, v_cache, k_idx_cache, q_start, q_len, *, topk=16,
+                   block_size=128, softmax_scale=None, want_sel=False, want_lse=False,
+                   workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Variable-length / chunked prefill against per-sequence caches.
+    q [T,Hq,d] and q_idx [T,G,d_idx] hold the sequences' query rows packed in
+    order; sequence b's rows are positions q_start[b] .. q_start[b]+q_len[b]-1
+    (q_start, q_len: host sequences of ints). k_cache/v_cache [B,max_ctx,G,d],
+    k_idx_cache [B,max_ctx,d_idx] already hold those positions. Returns
+    (out [T,Hq,d], sel [G,T,topk] or None, lse [T,Hq] or None)."""
+    lib = load()
+    T, Hq, d = q.shape
+    B, max_ctx, G = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for t, name in ((q, "q"), (q_idx, "q_idx"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                    (k_idx_cache, "k_idx_cache")):
+        _need(t, torch.bfloat16, name)
+    starts = [int(x) for x in q_start]
+    lens = [int(x) for x in q_len]
+    if len(starts) != B or len(lens) != B:
+        raise ValueError("q_start and q_len need one entry per cache sequence")
+    if sum(lens) != T:
+        raise ValueError(f"q has {T} rows but q_len sums to {sum(lens)}")
+    p = params(Hq, G, d, q_idx.shape[-1], block_size, topk, softmax_scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    sel = torch.empty((G, T, topk), dtype=torch.int32, device=dev) if want_sel else None
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    if T == 0:
+        return out, sel, lse
+    nbytes = int(lib.msa_prefill_varlen_workspace_bytes(ctypes.byref(p), max(lens), max_ctx))
+    if nbytes == 0:
+        raise MsaError(-2, "msa_prefill_varlen_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    c_start = (ctypes.c_int64 * B)(*starts)
+    c_len = (ctypes.c_int64 * B)(*lens)
+    _check(lib.msa_prefill_varlen(ctypes.byref(p), B, max_ctx, c_start, c_len, _ptr(q), _ptr(q_idx),
+                                  _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(out),
+                                  _ptr(sel), _ptr(lse), _ptr(workspace), nbytes, _stream(dev)),
+           "msa_prefill_varlen")
     return out, sel, lse
 
 

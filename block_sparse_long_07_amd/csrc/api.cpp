@@ -88,11 +88,13 @@ struct PrefillLayout {
       dense_list, dense_qmask, dense_slots, total;
 };
 
-bool prefill_layout(const Shape& s, int64_t N, PrefillLayout* L) {
-  if (N <= 0 || N > kMaxSeq) return false;
-  L->nb = (int)cdiv(N, kBlock);
+// n_ctx: positions of the longest context; max_rows: most query rows of one
+// sequence in the call.
+bool prefill_layout(const Shape& s, int64_t n_ctx, int64_t max_rows, PrefillLayout* L) {
+  if (n_ctx <= 0 || n_ctx > kMaxSeq || max_rows <= 0 || max_rows > n_ctx) return false;
+  L->nb = (int)cdiv(n_ctx, kBlock);
   L->nbs = (L->nb + 3) & ~3;
-  L->W = std::min<int64_t>(cdiv(N, kBlock) * kBlock, kWindowMax);
+  L->W = std::min<int64_t>(cdiv(max_rows, kBlock) * kBlock, kWindowMax);
   L->nch = cdiv(L->W, 64);
   L->Lc = (int64_t)s.G * L->nb * L->nch;
   L->nblk = cdiv(L->Lc, 4096);
@@ -164,7 +166,7 @@ const char* msa_status_string(msa_status s) {
 size_t msa_prefill_workspace_bytes(const msa_params* p, int32_t batch, int64_t seq_len) {
   Shape s;
   PrefillLayout L;
-  if (batch <= 0 || check_params(p, &s) != MSA_OK || !prefill_layout(s, seq_len, &L)) return 0;
+  if (batch <= 0 || check_params(p, &s) != MSA_OK || !prefill_layout(s, seq_len, seq_len, &L)) return 0;
   return L.total;
 }
 
@@ -186,6 +188,83 @@ struct StageClock {
   }
 };
 
+// One sequence's query rows [q_start, q_start + q_len); they attend to the
+// positions < q_start + q_len of k, v and k_idx. The query-side pointers hold
+// the q_len rows only; sel (optional) is sel[g*sel_gstride + (i - q_start)*k + u].
+struct SeqIO {
+  const uint16_t *q, *q_idx, *k, *v, *k_idx;
+  uint16_t* out;
+  int32_t* sel;
+  int64_t sel_gstride;
+  float* lse;
+  int64_t q_start, q_len;
+};
+
+// The five stages on the window of rows [w0, w0 + Wn) of a sequence.
+void prefill_window(const Shape& s, const PrefillLayout& L, const SeqIO& io, int64_t w0, int64_t Wn,
+                    void* workspace, hipStream_t hs, StageClock& clk) {
+  const int G = s.G, Hq = s.Hq, K = s.k;
+  const int64_t n_ctx = io.q_start + io.q_len;
+  const int64_t r0 = w0 - io.q_start;  // the window's first row among the call's rows
+  const int nbw = (int)((w0 + Wn - 1) / kBlock + 1);
+  const uint16_t* qw = io.q + r0 * Hq * kHeadDim;
+  clk.mark();
+  // 1. index scores for query blocks that have more than k-1 older blocks
+  LaunchIndexPrefill ia{io.q_idx + r0 * G * kIndexDim, io.k_idx, at<float>(workspace, L.sblk), w0, w0 + Wn,
+                        (int)std::max<int64_t>(K, w0 / kBlock), nbw, L.nbs, G};
+  launch_index_prefill(ia, hs);
+  clk.mark();
+  // 2. top-k selection
+  int32_t* selw = io.sel ? io.sel + r0 * K : at<int32_t>(workspace, L.sel);
+  const int64_t gstride = io.sel ? io.sel_gstride : L.W * K;
+  LaunchSelect sa{at<float>(workspace, L.sblk), L.nbs, selw, gstride, K, Wn, G, K, w0, nullptr};
+  launch_select(sa, hs);
+  clk.mark();
+  // 3. reverse index and tile schedule
+  const int64_t e_w = entries_in(w0, w0 + Wn, G, K);
+  const int64_t tile_cap = cdiv(e_w, kTileQ) + (int64_t)G * nbw;
+  const int nunits = (int)cdiv(Wn, 16);
+  int32_t* dcnt = at<int32_t>(workspace, L.dense_cnt);
+  int32_t* dlist = at<int32_t>(workspace, L.dense_list);
+  LaunchCsr ca{selw, gstride, K, w0, (int)Wn, nbw, G,
+               at<int32_t>(workspace, L.chunkcnt), at<int32_t>(workspace, L.chunkoff),
+               at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
+               at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
+               at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist,
+               at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits};
+  launch_csr_and_tiles(ca, hs);
+  clk.mark();
+  // 4. KV-outer attention over the pairs not shared by a whole unit
+  LaunchAttnPrefill aa{qw, io.k, io.v, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
+                       at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
+                       at<float>(workspace, L.part_lse), n_ctx, G, nbw, K, s.scale_log2,
+                       (int)std::min<int64_t>(cu_count(), tile_cap)};
+  launch_attn_prefill(aa, hs);
+  clk.mark();
+  // 5. query-stationary attention over the units' shared blocks + merge
+  LaunchAttnDense da{qw, io.k, io.v, dcnt, dlist, at<int32_t>(workspace, L.dense_qmask),
+                     at<int32_t>(workspace, L.dense_slots), at<uint16_t>(workspace, L.part_o),
+                     at<float>(workspace, L.part_lse), io.out + r0 * Hq * kHeadDim,
+                     io.lse ? io.lse + r0 * Hq : nullptr, n_ctx, w0, (int)Wn, nunits, G, K, s.scale_log2};
+  launch_attn_dense(da, hs);
+  clk.mark();
+}
+
+// Windows of one sequence. The 16-row units of the dense pass must not
+// straddle a key block (their rows share the local block), so a start that is
+// not a multiple of 16 first gets a window of its own up to the next multiple
+// of 16; the rest goes in windows of at most L.W rows.
+void prefill_seq(const Shape& s, const PrefillLayout& L, const SeqIO& io, void* workspace, hipStream_t hs,
+                 StageClock& clk) {
+  const int64_t end = io.q_start + io.q_len;
+  for (int64_t w0 = io.q_start; w0 < end;) {
+    const int64_t head_end = (w0 + 15) / 16 * 16;
+    const int64_t Wn = head_end != w0 ? std::min(head_end, end) - w0 : std::min(L.W, end - w0);
+    prefill_window(s, L, io, w0, Wn, workspace, hs, clk);
+    w0 += Wn;
+  }
+}
+
 msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, const void* q, const void* k,
                        const void* v, const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
                        float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
@@ -200,7 +279,7 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
   if ((sel_out && !aligned(sel_out, 4)) || (lse_out && !aligned(lse_out, 4))) return MSA_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
   PrefillLayout L;
-  if (!prefill_layout(s, seq_len, &L)) return MSA_ERR_UNSUPPORTED;
+  if (!prefill_layout(s, seq_len, seq_len, &L)) return MSA_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total) return MSA_ERR_WORKSPACE_TOO_SMALL;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -209,59 +288,80 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
   const int64_t N = seq_len;
   const int G = s.G, Hq = s.Hq, K = s.k;
   for (int32_t bi = 0; bi < batch; ++bi) {
-    const uint16_t* qs = static_cast<const uint16_t*>(q) + (int64_t)bi * N * Hq * kHeadDim;
-    const uint16_t* ks = static_cast<const uint16_t*>(k) + (int64_t)bi * N * G * kHeadDim;
-    const uint16_t* vs = static_cast<const uint16_t*>(v) + (int64_t)bi * N * G * kHeadDim;
-    const uint16_t* qis = static_cast<const uint16_t*>(q_idx) + (int64_t)bi * N * G * kIndexDim;
-    const uint16_t* kis = static_cast<const uint16_t*>(k_idx) + (int64_t)bi * N * kIndexDim;
-    uint16_t* os = static_cast<uint16_t*>(out) + (int64_t)bi * N * Hq * kHeadDim;
-    int32_t* sels = sel_out ? sel_out + (int64_t)bi * G * N * K : nullptr;
-    float* lses = lse_out ? lse_out + (int64_t)bi * N * Hq : nullptr;
-    for (int64_t w0 = 0; w0 < N; w0 += L.W) {
-      const int64_t Wn = std::min(L.W, N - w0);
-      const int nbw = (int)((w0 + Wn - 1) / kBlock + 1);
-      clk.mark();
-      // 1. index scores for query blocks that have more than k-1 older blocks
-      LaunchIndexPrefill ia{qis, kis, at<float>(workspace, L.sblk), N, w0,
-                            (int)std::max<int64_t>(K, w0 / kBlock), nbw, L.nbs, G};
-      launch_index_prefill(ia, hs);
-      clk.mark();
-      // 2. top-k selection
-      int32_t* selw = sels ? sels + w0 * K : at<int32_t>(workspace, L.sel);
-      const int64_t gstride = sels ? N * K : L.W * K;
-      LaunchSelect sa{at<float>(workspace, L.sblk), L.nbs, selw, gstride, K, Wn, G, K, w0, nullptr};
-      launch_select(sa, hs);
-      clk.mark();
-      // 3. reverse index and tile schedule
-      const int64_t e_w = entries_in(w0, w0 + Wn, G, K);
-      const int64_t tile_cap = cdiv(e_w, kTileQ) + (int64_t)G * nbw;
-      const int nunits = (int)cdiv(Wn, 16);
-      int32_t* dcnt = at<int32_t>(workspace, L.dense_cnt);
-      int32_t* dlist = at<int32_t>(workspace, L.dense_list);
-      LaunchCsr ca{selw, gstride, K, w0, (int)Wn, nbw, G,
-                   at<int32_t>(workspace, L.chunkcnt), at<int32_t>(workspace, L.chunkoff),
-                   at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
-                   at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
-                   at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist,
-                   at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits};
-      launch_csr_and_tiles(ca, hs);
-      clk.mark();
-      // 4. KV-outer attention over the pairs not shared by a whole unit
-      uint16_t* ow = os + w0 * Hq * kHeadDim;
-      float* lw = lses ? lses + w0 * Hq : nullptr;
-      LaunchAttnPrefill aa{qs, ks, vs, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
-                           at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
-                           at<float>(workspace, L.part_lse), N, w0, G, nbw, K, s.scale_log2,
-                           (int)std::min<int64_t>(cu_count(), tile_cap)};
-      launch_attn_prefill(aa, hs);
-      clk.mark();
-      // 5. query-stationary attention over the units' shared blocks + merge
-      LaunchAttnDense da{qs, ks, vs, dcnt, dlist, at<int32_t>(workspace, L.dense_qmask),
-                         at<int32_t>(workspace, L.dense_slots), at<uint16_t>(workspace, L.part_o),
-                         at<float>(workspace, L.part_lse), ow, lw, N, w0, (int)Wn, nunits, G, K, s.scale_log2};
-      launch_attn_dense(da, hs);
-      clk.mark();
+    SeqIO io;
+    io.q = static_cast<const uint16_t*>(q) + (int64_t)bi * N * Hq * kHeadDim;
+    io.k = static_cast<const uint16_t*>(k) + (int64_t)bi * N * G * kHeadDim;
+    io.v = static_cast<const uint16_t*>(v) + (int64_t)bi * N * G * kHeadDim;
+    io.q_idx = static_cast<const uint16_t*>(q_idx) + (int64_t)bi * N * G * kIndexDim;
+    io.k_idx = static_cast<const uint16_t*>(k_idx) + (int64_t)bi * N * kIndexDim;
+    io.out = static_cast<uint16_t*>(out) + (int64_t)bi * N * Hq * kHeadDim;
+    io.sel = sel_out ? sel_out + (int64_t)bi * G * N * K : nullptr;
+    io.sel_gstride = N * K;
+    io.lse = lse_out ? lse_out + (int64_t)bi * N * Hq : nullptr;
+    io.q_start = 0;
+    io.q_len = N;
+    prefill_seq(s, L, io, workspace, hs, clk);
+  }
+  return finish();
+}
+
+// Host-side checks of a variable-length call; *max_rows and *total get the
+// longest q_len and the sum of q_len.
+msa_status check_varlen(int32_t batch, int64_t max_ctx, const int64_t* q_start, const int64_t* q_len,
+                        int64_t* max_rows, int64_t* total) {
+  if (batch <= 0 || max_ctx <= 0 || !q_start || !q_len) return MSA_ERR_INVALID_ARG;
+  if (max_ctx > kMaxSeq) return MSA_ERR_UNSUPPORTED;
+  *max_rows = 0;
+  *total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (q_start[b] < 0 || q_len[b] < 0 || q_len[b] > max_ctx - q_start[b]) return MSA_ERR_INVALID_ARG;
+    *max_rows = std::max(*max_rows, q_len[b]);
+    *total += q_len[b];
+  }
+  return MSA_OK;
+}
+
+msa_status run_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ctx, const int64_t* q_start,
+                              const int64_t* q_len, const void* q, const void* q_idx, const void* k_cache,
+                              const void* v_cache, const void* k_idx_cache, void* out, int32_t* sel_out,
+                              float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  int64_t max_rows = 0, total = 0;
+  st = check_varlen(batch, max_ctx, q_start, q_len, &max_rows, &total);
+  if (st != MSA_OK) return st;
+  for (const void* ptr : {q, q_idx, k_cache, v_cache, k_idx_cache, (const void*)out})
+    if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
+  if ((sel_out && !aligned(sel_out, 4)) || (lse_out && !aligned(lse_out, 4))) return MSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  if (total == 0) return MSA_OK;
+  PrefillLayout L;
+  if (!prefill_layout(s, max_ctx, max_rows, &L)) return MSA_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.total) return MSA_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  StageClock clk{nullptr, hs};
+  const int G = s.G, Hq = s.Hq, K = s.k;
+  int64_t r = 0;  // first packed row of sequence b
+  for (int32_t b = 0; b < batch; ++b) {
+    if (q_len[b] > 0) {
+      SeqIO io;
+      io.q = static_cast<const uint16_t*>(q) + r * Hq * kHeadDim;
+      io.q_idx = static_cast<const uint16_t*>(q_idx) + r * G * kIndexDim;
+      io.k = static_cast<const uint16_t*>(k_cache) + (int64_t)b * max_ctx * G * kHeadDim;
+      io.v = static_cast<const uint16_t*>(v_cache) + (int64_t)b * max_ctx * G * kHeadDim;
+      io.k_idx = static_cast<const uint16_t*>(k_idx_cache) + (int64_t)b * max_ctx * kIndexDim;
+      io.out = static_cast<uint16_t*>(out) + r * Hq * kHeadDim;
+      io.sel = sel_out ? sel_out + r * K : nullptr;
+      io.sel_gstride = total * K;
+      io.lse = lse_out ? lse_out + r * Hq : nullptr;
+      io.q_start = q_start[b];
+      io.q_len = q_len[b];
+      prefill_seq(s, L, io, workspace, hs, clk);
     }
+    r += q_len[b];
   }
   return finish();
 }
@@ -305,6 +405,21 @@ msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_
   msa_status st = run_prefill(p, batch, seq_len, q, k, v, q_idx, k_idx, out, sel_out, lse_out, workspace,
                               workspace_bytes, stream, &ev);
   return collect(ev, 5, stage_ms, st);
+}
+
+size_t msa_prefill_varlen_workspace_bytes(const msa_params* p, int64_t max_q_len, int64_t max_ctx) {
+  Shape s;
+  PrefillLayout L;
+  if (check_params(p, &s) != MSA_OK || !prefill_layout(s, max_ctx, std::min(max_q_len, max_ctx), &L)) return 0;
+  return L.total;
+}
+
+msa_status msa_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ctx, const int64_t* q_start,
+                              const int64_t* q_len, const void* q, const void* q_idx, const void* k_cache,
+                              const void* v_cache, const void* k_idx_cache, void* out, int32_t* sel_out,
+                              float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_prefill_varlen(p, batch, max_ctx, q_start, q_len, q, q_idx, k_cache, v_cache, k_idx_cache, out,
+                            sel_out, lse_out, workspace, workspace_bytes, stream);
 }
 
 size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx) {
@@ -394,8 +509,8 @@ msa_status msa_index_scores(const msa_params* p, int64_t seq_len, const void* q_
     return MSA_ERR_INVALID_ARG;
   (void)hipGetLastError();
   const int nb = (int)cdiv(seq_len, kBlock);
-  LaunchIndexPrefill ia{static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), scores, seq_len,
-                        0, s.k, nb, nb, s.G};
+  LaunchIndexPrefill ia{static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), scores, 0,
+                        seq_len, s.k, nb, nb, s.G};
   launch_index_prefill(ia, static_cast<hipStream_t>(stream));
   return finish();
 }

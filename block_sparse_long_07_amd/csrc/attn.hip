@@ -570,7 +570,7 @@ constexpr int kAttnWaves = 8;
 __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ tiles, int32_t* __restrict__ tile_info,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int64_t n_tokens, int64_t row0, int G,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int64_t n_tokens, int G,
     int nbw, int topk, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
   __shared__ int s_t[4];
@@ -605,8 +605,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   auto fetch_q = [&](const int (&ent)[kAttnQN], int tg) {
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) {
-      const int64_t i = row0 + (ent[n] >> 4);
-      load_q(qg, n, q + ((i * Hq) + tg * kHpg + c) * kHeadDim + 8 * qd);
+      const int64_t i_rel = ent[n] >> 4;
+      load_q(qg, n, q + ((i_rel * Hq) + tg * kHpg + c) * kHeadDim + 8 * qd);
     }
   };
   auto read_entries = [&](const Tile& d, int (&ent)[kAttnQN]) {
@@ -728,8 +728,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   QueryGroup<kAttnQN> qg;
 #pragma unroll
   for (int n = 0; n < kAttnQN; ++n) {
-    const int64_t i = row0 + min(i_rel0 + n, nrows - 1);
-    load_q(qg, n, q + ((i * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
+    const int64_t i_rel = min(i_rel0 + n, nrows - 1);
+    load_q(qg, n, q + ((i_rel * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
   }
   {
     const int b0 = __builtin_amdgcn_readfirstlane(lane_blk);
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
 
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
   hipLaunchKernelGGL(k_attn_prefill, dim3(a.grid), dim3(512), 0, st, a.q, a.k, a.v, a.entries, a.tiles,
-                     a.tile_info, a.part_o, a.part_lse, a.n_tokens, a.row0, a.G, a.nbw, a.topk, a.scale_log2);
+                     a.tile_info, a.part_o, a.part_lse, a.n_tokens, a.G, a.nbw, a.topk, a.scale_log2);
 }
 
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {

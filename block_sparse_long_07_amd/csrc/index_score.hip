@@ -43,8 +43,8 @@ __device__ __forceinline__ void stage_kidx(lds_char* dst, const uint16_t* src_ro
 template <int G>
 __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __restrict__ q_idx,
                                                           const uint16_t* __restrict__ k_idx,
-                                                          float* __restrict__ sblk, int64_t n_tokens,
-                                                          int64_t row0, int qb_begin, int nb) {
+                                                          float* __restrict__ sblk, int64_t row0,
+                                                          int64_t row_end, int qb_begin, int nb) {
   constexpr int RT = 2 * G;  // 16-row tiles per wave
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * 16384];
   lds_char* lds = (lds_char*)lds_raw;
@@ -57,9 +57,10 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
 
   stage_kidx(lds, k_idx + (int64_t)kb0 * kBlock * kIndexDim, wave);
 
-  // flat index row (i*G + g) of this wave's first row
+  // flat index row (i*G + g) of this wave's first row; the window's rows are
+  // [row0, row_end) (a query block can start before or end after them)
   const int64_t flat0 = (int64_t)qb * kBlock * G + (int64_t)wave * 32 * G;
-  const int64_t flat_end = n_tokens * G;
+  const int64_t flat_lo = row0 * G, flat_end = row_end * G;
   bf16x8 qop[RT][2];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < flat_end) v = ld16(q_idx + row * kIndexDim + 32 * s + 8 * qd);
+      if (row >= flat_lo && row < flat_end) v = ld16(q_idx + (row - flat_lo) * kIndexDim + 32 * s + 8 * qd);
       qop[rt][s] = as_bf16x8(v);
     }
   }
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t row = flat0 + rt * 16 + c;
-    if ((rt & 3) != qd || row >= flat_end) continue;
-    float* dst = sblk + (row - row0 * G) * nb + kb0;
+    if ((rt & 3) != qd || row < flat_lo || row >= flat_end) continue;
+    float* dst = sblk + (row - flat_lo) * nb + kb0;
     const float* rv = res[rt >> 2];
     if (nkb == kKC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
       *reinterpret_cast<f32x4*>(dst) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
@@ -207,8 +208,8 @@ static void launch_prefill_g(const LaunchIndexPrefill& a, hipStream_t st) {
   if (n_qb <= 0) return;
   const int chunks = (a.qb_end - 1 + kKC - 1) / kKC;
   dim3 grid(chunks, n_qb);
-  hipLaunchKernelGGL(k_index_prefill<G>, grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.sblk, a.n_tokens,
-                     a.row0, a.qb_begin, a.nb);
+  hipLaunchKernelGGL(k_index_prefill<G>, grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.sblk, a.row0, a.row_end,
+                     a.qb_begin, a.nb);
 }
 
 void launch_index_prefill(const LaunchIndexPrefill& a, hipStream_t st) {

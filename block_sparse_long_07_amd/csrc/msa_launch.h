@@ -18,12 +18,13 @@ constexpr int kMaxTopk = 16;
 constexpr int kDenseMin = 7;
 constexpr int kDenseMax = 64;
 
+// Per-query arrays of a prefill window (q, q_idx, out, lse, selection) start
+// at the window's first row row0; key-side arrays (k, v, k_idx) at position 0.
 struct LaunchIndexPrefill {
-  const uint16_t* q_idx;  // [n_tokens, G, 64] of one sequence
-  const uint16_t* k_idx;  // [n_tokens, 64]
+  const uint16_t* q_idx;  // [(i - row0)*G + g][64]: the window's rows
+  const uint16_t* k_idx;  // [position][64]
   float* sblk;            // rows (i - row0)*G + g, row stride nb
-  int64_t n_tokens;
-  int64_t row0;           // first row of the window (multiple of 128)
+  int64_t row0, row_end;  // the window's rows [row0, row_end)
   int qb_begin, qb_end;   // query blocks scored: [qb_begin, qb_end)
   int nb;                 // row stride of sblk
   int G;
@@ -82,15 +83,15 @@ struct LaunchCsr {
 void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st);
 
 struct LaunchAttnPrefill {
-  const uint16_t* q;      // [n_tokens, Hq, 128]
-  const uint16_t* k;      // [n_tokens, G, 128]
+  const uint16_t* q;      // [i - row0][Hq][128]
+  const uint16_t* k;      // [position][G][128]
   const uint16_t* v;
   const int32_t* entries;
   const int32_t* tiles;
   int32_t* tile_info;
   uint16_t* part_o;       // [slot][2048] bf16 in fragment order, slot = (i_rel*G + g)*topk + u
   float* part_lse;        // [slot][16], log2 domain
-  int64_t n_tokens, row0;
+  int64_t n_tokens;       // keys that exist (positions < n_tokens)
   int G, nbw, topk;
   float scale_log2;
   int grid;               // persistent workgroups
@@ -98,7 +99,7 @@ struct LaunchAttnPrefill {
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st);
 
 struct LaunchAttnDense {
-  const uint16_t* q;
+  const uint16_t* q;      // [i - row0][Hq][128]
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* dense_cnt;

@@ -92,6 +92,39 @@ msa_status msa_prefill(const msa_params* p, int32_t batch, int64_t seq_len,
                        void* out, int32_t* sel_out, float* lse_out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace msa_prefill_varlen needs when no sequence has more
+ * than max_q_len query rows and caches hold max_ctx positions. Returns 0 for
+ * invalid or unsupported arguments. */
+size_t msa_prefill_varlen_workspace_bytes(const msa_params* p, int64_t max_q_len, int64_t max_ctx);
+
+/* Prefill of `batch` sequences of different lengths, each a chunk of query
+ * rows that continues an existing cache: sequence b's rows are the positions
+ * [q_start[b], q_start[b] + q_len[b]), and each attends causally to the cache
+ * positions 0 .. its own position. q_start[b] = 0 is a fresh prompt; a chunk
+ * split into pieces gives every row the same result as one call over the
+ * whole (up to fp32 rounding order in the attention; the selection is the
+ * same), since row i depends only on positions <= i [yifor, 設計核心;
+ * pnsm, section 2]. As in decode, the chunk's K, V and k_idx must already be
+ * in the caches at its positions.
+ *   q_start, q_len  HOST int64 [batch]: q_start >= 0, q_len >= 0 (0: nothing for
+ *                   that sequence), q_start + q_len <= max_ctx
+ *   q      bf16 [T, Hq, d] with T = sum of q_len: the sequences' rows packed in
+ *          order (sequence b starts at row sum_{b'<b} q_len[b'])
+ *   q_idx  bf16 [T, G, d_idx]
+ *   k_cache, v_cache  bf16 [batch, max_ctx, G, d]
+ *   k_idx_cache       bf16 [batch, max_ctx, d_idx]
+ *   out      bf16 [T, Hq, d]
+ *   sel_out  optional int32 [G, T, topk] (ascending, -1 padded)
+ *   lse_out  optional fp32 [T, Hq]
+ *   workspace  >= msa_prefill_varlen_workspace_bytes(p, max q_len, max_ctx) bytes
+ * T = 0 returns MSA_OK at once. max_ctx above 2^20 is MSA_ERR_UNSUPPORTED. */
+msa_status msa_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ctx,
+                              const int64_t* q_start, const int64_t* q_len,
+                              const void* q, const void* q_idx,
+                              const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                              void* out, int32_t* sel_out, float* lse_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace msa_decode needs. Returns 0 on invalid arguments. */
 size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx);
 

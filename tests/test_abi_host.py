@@ -99,3 +99,31 @@ def test_stage_entry_points_reject_bad_args(lib):
     assert lib.msa_select_blocks(ctypes.byref(p), 256, ok, None, None) == -1
     p.block_size = 64
     assert lib.msa_select_blocks(ctypes.byref(p), 256, ok, ok, None) == -2
+
+
+def test_varlen_workspace_and_rejects_bad_args(lib):
+    p = msa.params()
+    need = msa.prefill_varlen_workspace_bytes(p, 3000, 8192)
+    assert need > 0
+    # one call over the whole sequence needs what msa_prefill needs for it
+    assert msa.prefill_varlen_workspace_bytes(p, 8192, 8192) == msa.prefill_workspace_bytes(p, 1, 8192)
+    assert msa.prefill_varlen_workspace_bytes(p, 0, 8192) == 0
+    assert msa.prefill_varlen_workspace_bytes(p, 16, (1 << 20) + 1) == 0
+    ok = ctypes.c_void_p(1 << 20)
+    I64 = ctypes.c_int64 * 2
+
+    def call(starts, lens, max_ctx=8192, ws=need, ptrs=None, batch=2):
+        a = ptrs if ptrs is not None else [ok] * 6
+        return lib.msa_prefill_varlen(ctypes.byref(p), batch, max_ctx, starts, lens, *a, None, None,
+                                      ok, ws, None)
+
+    assert call(I64(0, 100), I64(3000, -1)) == -1          # negative length
+    assert call(I64(-1, 0), I64(10, 10)) == -1             # negative start
+    assert call(I64(0, 8000), I64(10, 193)) == -1          # runs past the cache
+    assert call(None, I64(10, 10)) == -1                   # host arrays required
+    assert call(I64(0, 0), I64(10, 10), batch=0) == -1
+    assert call(I64(0, 0), I64(10, 10), max_ctx=(1 << 20) + 1) == -2
+    assert call(I64(0, 5000), I64(3000, 3000), ws=need - 1) == -3
+    assert call(I64(0, 0), I64(10, 10), ptrs=[None] + [ok] * 5) == -1
+    # nothing to do: returns before anything is launched
+    assert call(I64(0, 17), I64(0, 0)) == 0

@@ -139,3 +139,43 @@ def test_decode_1m_eight_sequences():
             assert np.array_equal(sel[b].cpu().numpy(), ref["sel"]), f"seq {b}"
             compare_out(out[b], ref["out"], f"decode 1M seq{b}")
             compare_lse(lse[b], ref["lse"], f"decode 1M seq{b}")
+
+
+@pytest.mark.timeout(1200)
+def test_chunk_across_windows_sampled():
+    """A 69995-row chunk continuing a 5-token cache: an unaligned 11-row head
+    window, a full 65536-row window and a ragged tail window."""
+    n, a, topk, max_ctx = 70000, 5, 16, 70400
+    inp = syn.PrefillInputs(n, syn.Dims(), 6, "planted", n_planted=8)
+    dev = "cuda"
+    log(f"case chunk [{a},{n}) of a {max_ctx}-position cache")
+    with timed("inputs"):
+        chunk = np.arange(a, n)
+        q = inp.q(chunk, device=dev)
+        qi = inp.q_idx(chunk, device=dev)
+        caches = []
+        for t in (inp.k(device=dev), inp.v(device=dev), inp.k_idx(device=dev)):
+            c = torch.empty((1, max_ctx) + tuple(t.shape[1:]), dtype=torch.bfloat16, device=dev)
+            c.view(torch.int16).fill_(0x7FC0)  # NaN past the chunk's end
+            c[0, :n] = t
+            caches.append(c)
+            del t
+        torch.cuda.synchronize()
+    with timed("gpu"):
+        out, sel, lse = msa.prefill_varlen(q, qi, *caches, [a], [n - a], topk=topk, want_sel=True, want_lse=True)
+        torch.cuda.synchronize()
+    extra = sorted({b for g in inp.planted.values() for b in g})
+    edges = [5, 6, 15, 16, 17, 127, 128, 65551, 65552, 65553, 69999]
+    rows = np.union1d(syn.stratified_rows(n, 1536, 128, 6, topk, extra=extra), edges)
+    rows = rows[rows >= a]
+    rt = torch.as_tensor(rows - a, device=dev)
+    got_sel = sel[:, rt].permute(1, 0, 2).cpu().numpy()
+    got_out, got_lse = out[rt].cpu(), lse[rt].cpu()
+    k0, v0, ki0 = caches
+    with timed("oracle"):
+        ref = oracle_rows_threaded(rows, mo.to_f64(inp.q(rows)), mo.to_f64(inp.q_idx(rows)),
+                                   mo.to_f64(ki0[0, :n]), RowsF64(k0[0]), RowsF64(v0[0]), topk)
+    mism = np.argwhere(got_sel != ref["sel"])
+    assert mism.size == 0, f"selection mismatch at {mism[:5].tolist()}"
+    compare_out(got_out, ref["out"], "chunk out")
+    compare_lse(got_lse, ref["lse"], "chunk")
