@@ -14,7 +14,11 @@ from oracle import msa_oracle as mo
 
 OUT_MAX_ABS = 2e-2      # bf16 in/out, fp32 accumulation
 OUT_REL_L2 = 5e-3
-LSE_MAX_ABS = 2e-3
+# lse: the attention weights P enter both P.V and the denominator rounded to
+# bf16 (unit roundoff u = 2^-8), so the denominator can be off by a relative u
+# when one key dominates a row: |d lse| <= ln(1 + 2^-8) = 3.9e-3, plus fp32
+# accumulation (~1e-6).
+LSE_MAX_ABS = 4e-3
 
 
 def log(msg: str):

@@ -3,7 +3,7 @@ oracle on the same seeded inputs.
 
 Bar: block selection bit-exact (integer-valued index projections make every
 score exact in fp32); pooled scores exactly equal; outputs within max-abs 2e-2
-and relative L2 5e-3 (bf16 in/out, fp32 accumulation); lse within 2e-3.
+and relative L2 5e-3 (bf16 in/out, fp32 accumulation); lse within 4e-3 (bf16 rounding of P, see tests/_parity.py).
 """
 import numpy as np
 import pytest

@@ -9,7 +9,7 @@ the 16-row units are those of a one-call prefill, so the outputs must be
 identical bit for bit to that call's.
 
 Bar as in the other parity tests: selection bit-exact, outputs max-abs 2e-2 and
-relative L2 5e-3, lse 2e-3.
+relative L2 5e-3, lse 4e-3.
 """
 import numpy as np
 import pytest
