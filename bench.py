@@ -135,9 +135,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "7706e5b2ee1fbe89",
-    "k_attn_prefill (KV-outer)": 5.341e9,
-    "k_attn_dense (dense + merge)": 4.373e9,
+    "source": "1d947a604c68ad88",
+    "k_attn_prefill (KV-outer)": 5.330e9,
+    "k_attn_dense (dense + merge)": 4.377e9,
 }
 
 
@@ -326,6 +326,9 @@ def main():
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="no GPU work: condense the rocprofv3 CSV output under DIR to text and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the chunked / variable-length prefill measurement (profiling runs use this so that "
+                         "per-kernel averages cover the headline workload only)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
@@ -417,7 +420,7 @@ def main():
     kernels[1]["executed_tflop"] = round(ps["dense_unit_blocks"] * 16 * 4.0 * D * (HQ // G) * BK / 1e12, 4)
     dom = max(kernels, key=lambda r: r["ms"])
 
-    chunked, varlen = serving_shapes(torch, msa, pre, TOPK, args.steps)
+    chunked, varlen = (None, None) if args.no_serving else serving_shapes(torch, msa, pre, TOPK, args.steps)
 
     res = {
         "metric": METRIC,
