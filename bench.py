@@ -311,6 +311,34 @@ def serving_shapes(torch, msa, pre, topk, reps, n_chunks=4, varlen_lens=(8192, 6
     return chunked, varlen
 
 
+# ---- Index Branch KL-alignment backward ------------------------------------------
+
+def kl_backward_measure(torch, msa, pre, topk, reps):
+    """KL alignment of the Index Branch (loss, dq_idx, dk_idx) on the bench
+    prefill, with the forward's selection and lse. Algorithmic HBM bytes per
+    selected (row, group, block) pair: the query's 16 heads (4 KiB, pass 2),
+    its index query twice (2 x 128 B), its 16 lse values (64 B), and the slot
+    partials written and read back (2 x 268 B); per (group, block) its K block
+    (32 KiB) and its k_idx block twice (2 x 16 KiB); per row and group the
+    outputs (dq_idx 256 B, loss 4 B); per key dk_idx (256 B)."""
+    q, k, v, qi, ki = pre
+    _, sel, lse = msa.prefill(q, k, v, qi, ki, topk=topk, want_sel=True, want_lse=True)
+    sel, lse = sel[0].contiguous(), lse[0].contiguous()
+    q0, k0, qi0, ki0 = q[0], k[0], qi[0], ki[0]
+    p = msa.params(HQ, G, D, DI, BK, topk)
+    n = q0.shape[0]
+    ws = torch.empty(msa.index_kl_workspace_bytes(p, n), dtype=torch.uint8, device=q0.device)
+    ms = _time_calls(torch, lambda: msa.index_kl_backward(q0, k0, qi0, ki0, sel, lse, topk=topk, workspace=ws), reps)
+    nb = (n + BK - 1) // BK
+    pairs = G * sum(min(BK, n - blk * BK) * min(topk, blk + 1) for blk in range(nb))
+    nbytes = (pairs * (4096 + 2 * 128 + 64 + 2 * 268) + G * nb * (32768 + 2 * 16384)
+              + n * G * (256 + 4) + n * 256)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "pairs": int(pairs), "Mpairs/s": round(pairs / (ms * 1e-3) / 1e6, 1),
+            "algorithmic_gb": round(nbytes / 1e9, 4), "GB/s": round(gbs, 1), "bound": "hbm",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 # ---- main ---------------------------------------------------------------------
 
 def main():
@@ -327,8 +355,8 @@ def main():
                     help="no GPU work: condense the rocprofv3 CSV output under DIR to text and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-serving", action="store_true",
-                    help="skip the chunked / variable-length prefill measurement (profiling runs use this so that "
-                         "per-kernel averages cover the headline workload only)")
+                    help="skip the chunked / variable-length prefill and KL-backward measurements (profiling runs "
+                         "use this so that per-kernel averages cover the headline workload only)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
@@ -421,6 +449,7 @@ def main():
     dom = max(kernels, key=lambda r: r["ms"])
 
     chunked, varlen = (None, None) if args.no_serving else serving_shapes(torch, msa, pre, TOPK, args.steps)
+    kl = None if args.no_serving else kl_backward_measure(torch, msa, pre, TOPK, args.steps)
 
     res = {
         "metric": METRIC,
@@ -457,6 +486,7 @@ def main():
         "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse", "dense_unit_blocks")},
         "chunked_prefill": chunked,
         "varlen_prefill": varlen,
+        "index_kl_backward": kl,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)

@@ -22,7 +22,8 @@ _STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_UNSUPPORTED",
 
 EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_prefill_varlen_workspace_bytes",
             "msa_prefill_varlen", "msa_decode_workspace_bytes", "msa_decode", "msa_prefill_profiled",
-            "msa_decode_profiled", "msa_index_scores", "msa_select_blocks", "msa_status_string")
+            "msa_decode_profiled", "msa_index_kl_workspace_bytes", "msa_index_kl_backward", "msa_index_scores",
+            "msa_select_blocks", "msa_status_string")
 PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
 DECODE_STAGES = ("index_score", "select", "attn", "combine")
 
@@ -71,6 +72,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_prefill_profiled.restype = ctypes.c_int
     lib.msa_decode_profiled.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, fp]
     lib.msa_decode_profiled.restype = ctypes.c_int
+    lib.msa_index_kl_workspace_bytes.argtypes = [P, i64]
+    lib.msa_index_kl_workspace_bytes.restype = sz
+    lib.msa_index_kl_backward.argtypes = [P, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_index_kl_backward.restype = ctypes.c_int
     lib.msa_index_scores.argtypes = [P, i64, vp, vp, vp, vp]
     lib.msa_index_scores.restype = ctypes.c_int
     lib.msa_select_blocks.argtypes = [P, i64, vp, vp, vp]
@@ -234,6 +239,40 @@ def decode(q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, *, topk=16, block_
         _check(lib.msa_decode_profiled(*args, ms), "msa_decode_profiled")
         stage_ms.extend(float(x) for x in ms)
     return out, sel, lse
+
+
+def index_kl_workspace_bytes(p: MsaParams, seq_len: int) -> int:
+    return int(load().msa_index_kl_workspace_bytes(ctypes.byref(p), seq_len))
+
+
+def index_kl_backward(q, k, q_idx, k_idx, sel, lse, *, topk=16, block_size=128, softmax_scale=None,
+                      workspace: Optional[torch.Tensor] = None):
+    """KL alignment of the Index Branch to the Main Branch for one sequence:
+    q [N,Hq,d], k [N,G,d], q_idx [N,G,d_idx], k_idx [N,d_idx] (bf16), sel
+    int32 [G,N,topk] and lse fp32 [N,Hq] as returned by prefill (batch entry).
+    Returns (loss fp32 [G,N], dq_idx fp32 [N,G,d_idx], dk_idx fp32 [N,d_idx]):
+    the per-(group, row) divergences and the gradients of their sum."""
+    lib = load()
+    N, Hq, d = q.shape
+    G = k.shape[1]
+    for t, name in ((q, "q"), (k, "k"), (q_idx, "q_idx"), (k_idx, "k_idx")):
+        _need(t, torch.bfloat16, name)
+    _need(sel, torch.int32, "sel")
+    _need(lse, torch.float32, "lse")
+    p = params(Hq, G, d, q_idx.shape[-1], block_size, topk, softmax_scale)
+    dev = q.device
+    loss = torch.empty((G, N), dtype=torch.float32, device=dev)
+    dq = torch.empty((N, G, q_idx.shape[-1]), dtype=torch.float32, device=dev)
+    dk = torch.empty((N, k_idx.shape[-1]), dtype=torch.float32, device=dev)
+    nbytes = int(lib.msa_index_kl_workspace_bytes(ctypes.byref(p), N))
+    if nbytes == 0:
+        raise MsaError(-2, "msa_index_kl_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib.msa_index_kl_backward(ctypes.byref(p), N, _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(sel),
+                                     _ptr(lse), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(workspace), nbytes,
+                                     _stream(dev)), "msa_index_kl_backward")
+    return loss, dq, dk
 
 
 def index_scores(q_idx, k_idx, *, num_q_heads=None, topk=16, block_size=128, scores=None):

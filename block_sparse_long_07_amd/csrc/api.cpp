@@ -123,6 +123,45 @@ bool prefill_layout(const Shape& s, int64_t n_ctx, int64_t max_rows, PrefillLayo
   return true;
 }
 
+// Workspace of the KL-alignment backward, per window of W rows.
+constexpr int kKlChunk = 1024;  // reverse-index entries per KL work item
+
+struct KlLayout {
+  int64_t W;
+  int nb, nch;
+  int64_t Lc, nblk, e_cap, chunk_cap, slots;
+  size_t chunkcnt, chunkoff, bsum, entries, tile_start, chunks, chunk_info, part_m, part_l, loss_part, dq_part,
+      lse_idx, total;
+};
+
+bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
+  if (N <= 0 || N > kMaxSeq) return false;
+  L->nb = (int)cdiv(N, kBlock);
+  L->W = std::min<int64_t>(cdiv(N, kBlock) * kBlock, kWindowMax);
+  L->nch = (int)cdiv(L->W, 64);
+  L->Lc = (int64_t)s.G * L->nb * L->nch;
+  L->nblk = cdiv(L->Lc, 4096);
+  if (L->nblk > 16384) return false;
+  L->e_cap = L->W * s.G * s.k;
+  L->chunk_cap = cdiv(L->e_cap, kKlChunk) + (int64_t)s.G * L->nb;
+  L->slots = L->W * s.G * s.k;
+  size_t off = 0;
+  L->chunkcnt = off;   off += up((size_t)L->Lc * sizeof(int32_t));
+  L->chunkoff = off;   off += up((size_t)(L->Lc + 1) * sizeof(int32_t));
+  L->bsum = off;       off += up((size_t)(L->nblk + 1) * sizeof(int32_t));
+  L->entries = off;    off += up((size_t)L->e_cap * sizeof(int32_t));
+  L->tile_start = off; off += up((size_t)((int64_t)s.G * L->nb + 1) * sizeof(int32_t));
+  L->chunks = off;     off += up((size_t)L->chunk_cap * 4 * sizeof(int32_t));
+  L->chunk_info = off; off += up(4 * sizeof(int32_t));
+  L->part_m = off;     off += up((size_t)L->slots * sizeof(float));
+  L->part_l = off;     off += up((size_t)L->slots * sizeof(float));
+  L->loss_part = off;  off += up((size_t)L->slots * sizeof(float));
+  L->dq_part = off;    off += up((size_t)L->slots * kIndexDim * sizeof(float));
+  L->lse_idx = off;    off += up((size_t)L->W * s.G * sizeof(float));
+  L->total = off;
+  return true;
+}
+
 struct DecodeLayout {
   int nb;
   size_t sblk, sel, part_o, part_lse, total;
@@ -231,7 +270,7 @@ void prefill_window(const Shape& s, const PrefillLayout& L, const SeqIO& io, int
                at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
                at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
                at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist,
-               at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits};
+               at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits, true};
   launch_csr_and_tiles(ca, hs);
   clk.mark();
   // 4. KV-outer attention over the pairs not shared by a whole unit
@@ -496,6 +535,61 @@ msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_c
   msa_status st = run_decode(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out,
                              lse_out, workspace, workspace_bytes, stream, &ev);
   return collect(ev, 4, stage_ms, st);
+}
+
+size_t msa_index_kl_workspace_bytes(const msa_params* p, int64_t seq_len) {
+  Shape s;
+  KlLayout L;
+  if (check_params(p, &s) != MSA_OK || !kl_layout(s, seq_len, &L)) return 0;
+  return L.total;
+}
+
+msa_status msa_index_kl_backward(const msa_params* p, int64_t seq_len, const void* q, const void* k,
+                                 const void* q_idx, const void* k_idx, const int32_t* sel, const float* lse,
+                                 float* loss, float* dq_idx, float* dk_idx, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  if (seq_len <= 0) return MSA_ERR_INVALID_ARG;
+  if (seq_len > kMaxSeq) return MSA_ERR_UNSUPPORTED;
+  for (const void* ptr : {q, k, q_idx, k_idx, (const void*)lse, (const void*)dq_idx, (const void*)dk_idx})
+    if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
+  if (!sel || !aligned(sel, 4) || !loss || !aligned(loss, 4)) return MSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  KlLayout L;
+  if (!kl_layout(s, seq_len, &L)) return MSA_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.total) return MSA_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t N = seq_len;
+  const int G = s.G, Hq = s.Hq, K = s.k;
+  launch_zero_f32(dk_idx, N * kIndexDim, hs);
+  for (int64_t w0 = 0; w0 < N; w0 += L.W) {
+    const int64_t Wn = std::min(L.W, N - w0);
+    const int nbw = (int)((w0 + Wn - 1) / kBlock + 1);
+    const int32_t* selw = sel + w0 * K;
+    const int64_t e_w = entries_in(w0, w0 + Wn, G, K);
+    const int64_t chunk_cap = cdiv(e_w, kKlChunk) + (int64_t)G * nbw;
+    // every selected pair, in chunks of up to kKlChunk queries per (group, block)
+    LaunchCsr ca{selw, N * K, K, w0, (int)Wn, nbw, G,
+                 at<int32_t>(workspace, L.chunkcnt), at<int32_t>(workspace, L.chunkoff),
+                 at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
+                 at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.chunks),
+                 at<int32_t>(workspace, L.chunk_info), kKlChunk, chunk_cap, nullptr, nullptr, nullptr, nullptr,
+                 (int)cdiv(Wn, 16), false};
+    launch_csr_and_tiles(ca, hs);
+    LaunchKl ka{static_cast<const uint16_t*>(q) + w0 * Hq * kHeadDim, static_cast<const uint16_t*>(k),
+                static_cast<const uint16_t*>(q_idx) + w0 * G * kIndexDim, static_cast<const uint16_t*>(k_idx),
+                lse + w0 * Hq, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.chunks),
+                at<int32_t>(workspace, L.chunk_info), chunk_cap, at<float>(workspace, L.part_m),
+                at<float>(workspace, L.part_l), at<float>(workspace, L.loss_part), at<float>(workspace, L.dq_part),
+                at<float>(workspace, L.lse_idx), loss, dq_idx + w0 * G * kIndexDim, dk_idx, N, w0, (int)Wn, G, K,
+                s.scale_log2};
+    launch_kl_window(ka, hs);
+  }
+  return finish();
 }
 
 msa_status msa_index_scores(const msa_params* p, int64_t seq_len, const void* q_idx, const void* k_idx,

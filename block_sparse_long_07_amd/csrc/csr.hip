@@ -12,11 +12,11 @@
 //      (g, b, chunk) its output offset (and every list its start);
 //   3. the chunk pass is repeated and each entry lands at offset + popcount of
 //      the mask bits below its row.
-// Pairs whose 16-row unit selected the block at least kDenseMin times are left
-// out: the dense pass computes them (k_csr_count also writes its per-unit
-// lists). Each list is then cut into tiles of at most `tile_q` queries, so a
-// block hit by very many queries (a sink-like block) becomes many independent
-// tiles.
+// With the dense pass on, pairs whose 16-row unit selected the block at least
+// kDenseMin times are left out: the dense pass computes them (k_csr_count also
+// writes its per-unit lists); with it off, every pair is listed. Each list is
+// then cut into tiles of at most `tile_q` queries, so a block hit by very many
+// queries (a sink-like block) becomes many independent tiles.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -43,8 +43,9 @@ __device__ __forceinline__ void chunk_masks(const int32_t* __restrict__ sel, int
 // units computing the block in the dense pass: at least min(kDenseMin, n) of
 // the unit's n valid rows selected it. All the unit's rows are set, selecting
 // or not (the dense pass masks the others).
-__device__ __forceinline__ unsigned long long dense_bits(unsigned long long m, int nq) {
+__device__ __forceinline__ unsigned long long dense_bits(unsigned long long m, int nq, bool dense) {
   unsigned long long d = 0ull;
+  if (!dense) return d;
 #pragma unroll
   for (int s = 0; s < kChunk / kUnit; ++s) {
     const int r0 = s * kUnit;
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
                                                    int topk, int64_t row0, int nrows, int nbw, int nch,
                                                    int32_t* __restrict__ chunkcnt, int32_t* __restrict__ dense_cnt,
                                                    int32_t* __restrict__ dense_list, int32_t* __restrict__ dense_qmask,
-                                                   int32_t* __restrict__ dense_slots, int nunits) {
+                                                   int32_t* __restrict__ dense_slots, int nunits, bool dense) {
   extern __shared__ unsigned long long mask[];
   __shared__ int cand[kChunk / kUnit][kDenseMax];
   const int chunk = blockIdx.x, g = blockIdx.y;
@@ -72,10 +73,11 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
     int cnt = 0;
     if (b <= bmax) {
       const unsigned long long m = mask[b];
-      cnt = __popcll(m & ~dense_bits(m, nq));
+      cnt = __popcll(m & ~dense_bits(m, nq, dense));
     }
     chunkcnt[((int64_t)g * nbw + b) * nch + chunk] = cnt;
   }
+  if (!dense) return;
   const int32_t* srow0 = sel + (int64_t)g * sel_gstride + (int64_t)i0 * topk;
   // per row: which of its slots the dense pass computes
   if ((int)threadIdx.x < nq) {
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
     int bits = 0;
     for (int u = 0; u < topk; ++u) {
       const int b = srow0[t * topk + u];
-      if (b >= 0 && b <= bmax && ((dense_bits(mask[b], nq) >> t) & 1ull)) bits |= 1 << u;
+      if (b >= 0 && b <= bmax && ((dense_bits(mask[b], nq, true) >> t) & 1ull)) bits |= 1 << u;
     }
     dense_slots[(int64_t)g * nrows + i0 + t] = bits;
   }
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
 __global__ __launch_bounds__(256) void k_csr_scatter(const int32_t* __restrict__ sel, int64_t sel_gstride,
                                                      int topk, int64_t row0, int nrows, int nbw, int nch,
                                                      const int32_t* __restrict__ chunkoff,
-                                                     int32_t* __restrict__ entries) {
+                                                     int32_t* __restrict__ entries, bool dense) {
   extern __shared__ unsigned long long mask[];
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int i0 = chunk * kChunk;
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(256) void k_csr_scatter(const int32_t* __restrict__
     const int b = s[e];
     if (b < 0 || b > bmax) continue;
     const int ql = e / topk, u = e % topk;
-    const unsigned long long m = mask[b] & ~dense_bits(mask[b], nq);
+    const unsigned long long m = mask[b] & ~dense_bits(mask[b], nq, dense);
     if (!((m >> ql) & 1ull)) continue;  // handled by the dense pass
     const unsigned long long below = m & ((1ull << ql) - 1ull);
     const int64_t pos = chunkoff[((int64_t)g * nbw + b) * nch + chunk] + __popcll(below);
@@ -299,14 +301,14 @@ void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st) {
   const size_t lds = (size_t)a.nbw * sizeof(unsigned long long);
   dim3 grid(nch, a.G);
   hipLaunchKernelGGL(k_csr_count, grid, dim3(256), lds, st, a.sel, a.sel_gstride, a.topk, a.row0, a.nrows,
-                     a.nbw, nch, a.chunkcnt, a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.nunits);
+                     a.nbw, nch, a.chunkcnt, a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.nunits, a.dense);
   const int64_t n = (int64_t)a.G * a.nbw * nch;
   const int nblk = (int)((n + kScanTile - 1) / kScanTile);
   hipLaunchKernelGGL(k_scan_reduce, dim3(nblk), dim3(256), 0, st, a.chunkcnt, n, a.bsum);
   hipLaunchKernelGGL(k_scan_bsums, dim3(1), dim3(1024), 0, st, a.bsum, nblk);
   hipLaunchKernelGGL(k_scan_final, dim3(nblk), dim3(256), 0, st, a.chunkcnt, n, a.bsum, a.chunkoff);
   hipLaunchKernelGGL(k_csr_scatter, grid, dim3(256), lds, st, a.sel, a.sel_gstride, a.topk, a.row0, a.nrows,
-                     a.nbw, nch, a.chunkoff, a.entries);
+                     a.nbw, nch, a.chunkoff, a.entries, a.dense);
   const int L = a.G * a.nbw;
   hipLaunchKernelGGL(k_tiles_count, dim3(1), dim3(1024), 0, st, a.chunkoff, nch, L, a.tile_q, a.tile_start,
                      a.tile_info);

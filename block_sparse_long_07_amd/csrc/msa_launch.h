@@ -79,6 +79,7 @@ struct LaunchCsr {
   int32_t* dense_qmask;   // [G][nunits][kDenseMax]: bit r = row r of the unit selected the block
   int32_t* dense_slots;   // [G][nrows]: bit u = slot u of the row is computed in the dense pass
   int nunits;             // ceil(nrows / 16)
+  bool dense;             // split off the dense pass's pairs (else list every pair; dense_* unused)
 };
 void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st);
 
@@ -129,6 +130,34 @@ struct LaunchAttnDecode {
   float scale_log2;
 };
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st);
+
+// Index Branch KL alignment, one window of rows [row0, row0 + nrows) of one
+// sequence. Per-query arrays start at the window's first row; k, k_idx, loss
+// and dk_idx are indexed by position.
+struct LaunchKl {
+  const uint16_t* q;      // [i - row0][Hq][128]
+  const uint16_t* k;      // [position][G][128]
+  const uint16_t* q_idx;  // [i - row0][G][64]
+  const uint16_t* k_idx;  // [position][64]
+  const float* lse;       // [i - row0][Hq], natural log
+  const int32_t* entries; // reverse index of every selected pair
+  const int32_t* chunks;  // [chunk][4] = (group, begin, len, block)
+  const int32_t* chunk_info;  // [0] chunks
+  int64_t chunk_cap;      // grid size (>= chunks)
+  float* part_m;          // [slot], slot = (i_rel*G + g)*topk + u
+  float* part_l;
+  float* loss_part;
+  float* dq_part;         // [slot][64]
+  float* lse_idx;         // [i_rel*G + g]
+  float* loss;            // [G][n_tokens]
+  float* dq_idx;          // [i - row0][G][64]
+  float* dk_idx;          // [position][64], accumulated
+  int64_t n_tokens, row0;
+  int nrows, G, topk;
+  float scale_log2;
+};
+void launch_kl_window(const LaunchKl& a, hipStream_t st);
+void launch_zero_f32(float* p, int64_t n, hipStream_t st);
 
 struct LaunchCombine {   // decode
   const uint16_t* part_o;  // [(s*G + g)*topk + u][2048] bf16, fragment order

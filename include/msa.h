@@ -172,6 +172,36 @@ msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_c
                                void* workspace, size_t workspace_bytes, void* stream,
                                float* stage_ms);
 
+/* ---- Index Branch training signal ------------------------------------------
+ * KL alignment of the Index Branch to the Main Branch [pnsm, section 4: the
+ * main branch's attention on the selected support is the teacher, gradients
+ * reach only the index projections; yhxrc, 二]. For one sequence, per query
+ * row i and group g with support T = {j <= i : floor(j/B_k) in sel[g, i]}:
+ *   P_main(j) = mean over the group's query heads h of exp(scale q[i,h].k[j,g] - lse[i,h])
+ *   P_idx(j)  = softmax over T of q_idx[i,g] . k_idx[j]
+ *   loss[g, i] = KL(P_main || P_idx)
+ * and the gradients of sum_{g,i} loss[g, i] with respect to q_idx and k_idx
+ * only: dq_idx[i,g] = sum_T (P_idx - P_main)(j) k_idx[j] and
+ * dk_idx[j] = sum over (i, g) with j in T of (P_idx - P_main)(j) q_idx[i,g].
+ *   q, k      bf16 [seq_len, Hq, d], [seq_len, G, d]   (as passed to msa_prefill)
+ *   q_idx     bf16 [seq_len, G, d_idx];  k_idx bf16 [seq_len, d_idx]
+ *   sel       int32 [G, seq_len, topk]  msa_prefill's sel_out (ascending, -1 padded)
+ *   lse       fp32 [seq_len, Hq]        msa_prefill's lse_out (natural log), 16-byte aligned
+ *   loss      fp32 [G, seq_len]
+ *   dq_idx    fp32 [seq_len, G, d_idx]  (written)
+ *   dk_idx    fp32 [seq_len, d_idx]     (written; accumulated with atomics, so
+ *                                        the summation order, and the last bits,
+ *                                        may vary between calls)
+ *   workspace >= msa_index_kl_workspace_bytes(p, seq_len) bytes
+ * The teacher uses the forward's lse, so P_main is the forward's attention
+ * distribution up to its rounding. Returns 0 / an error status as above. */
+size_t msa_index_kl_workspace_bytes(const msa_params* p, int64_t seq_len);
+msa_status msa_index_kl_backward(const msa_params* p, int64_t seq_len,
+                                 const void* q, const void* k, const void* q_idx, const void* k_idx,
+                                 const int32_t* sel, const float* lse,
+                                 float* loss, float* dq_idx, float* dk_idx,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Stage entry points (Index Branch only) ------------------------------
  * For callers that need the selection alone, and for per-stage parity tests. */
 

@@ -127,3 +127,21 @@ def test_varlen_workspace_and_rejects_bad_args(lib):
     assert call(I64(0, 0), I64(10, 10), ptrs=[None] + [ok] * 5) == -1
     # nothing to do: returns before anything is launched
     assert call(I64(0, 17), I64(0, 0)) == 0
+
+
+def test_index_kl_rejects_bad_args(lib):
+    p = msa.params()
+    need = msa.load().msa_index_kl_workspace_bytes(ctypes.byref(p), 4096)
+    assert need > 0
+    ok = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    f = lib.msa_index_kl_backward
+    args = [ok] * 9
+    assert f(ctypes.byref(p), 4096, *args, ok, need - 1, None) == -3
+    assert f(ctypes.byref(p), 4096, *args, None, need, None) == -1
+    assert f(ctypes.byref(p), 0, *args, ok, need, None) == -1
+    assert f(ctypes.byref(p), (1 << 20) + 1, *args, ok, need, None) == -2
+    assert f(ctypes.byref(p), 4096, ok, ok, ok, ok, ok, mis, ok, ok, ok, ok, need, None) == -1  # lse misaligned
+    assert f(ctypes.byref(p), 4096, ok, ok, ok, ok, None, ok, ok, ok, ok, ok, need, None) == -1  # no sel
+    p.index_dim = 32
+    assert f(ctypes.byref(p), 4096, *args, ok, need, None) == -2
