@@ -131,7 +131,7 @@ struct KlLayout {
   int nb, nch;
   int64_t Lc, nblk, e_cap, chunk_cap, slots;
   size_t chunkcnt, chunkoff, bsum, entries, tile_start, chunks, chunk_info, part_m, part_l, loss_part, dq_part,
-      lse_idx, total;
+      lse_idx, dk_part, total;
 };
 
 bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
@@ -158,6 +158,7 @@ bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
   L->loss_part = off;  off += up((size_t)L->slots * sizeof(float));
   L->dq_part = off;    off += up((size_t)L->slots * kIndexDim * sizeof(float));
   L->lse_idx = off;    off += up((size_t)L->W * s.G * sizeof(float));
+  L->dk_part = off;    off += up((size_t)L->chunk_cap * kBlock * kIndexDim * sizeof(float));
   L->total = off;
   return true;
 }
@@ -585,7 +586,8 @@ msa_status msa_index_kl_backward(const msa_params* p, int64_t seq_len, const voi
                 lse + w0 * Hq, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.chunks),
                 at<int32_t>(workspace, L.chunk_info), chunk_cap, at<float>(workspace, L.part_m),
                 at<float>(workspace, L.part_l), at<float>(workspace, L.loss_part), at<float>(workspace, L.dq_part),
-                at<float>(workspace, L.lse_idx), loss, dq_idx + w0 * G * kIndexDim, dk_idx, N, w0, (int)Wn, G, K,
+                at<float>(workspace, L.lse_idx), loss, dq_idx + w0 * G * kIndexDim, dk_idx,
+                at<float>(workspace, L.dk_part), at<int32_t>(workspace, L.tile_start), N, w0, (int)Wn, nbw, G, K,
                 s.scale_log2};
     launch_kl_window(ka, hs);
   }

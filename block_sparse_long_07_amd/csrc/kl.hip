@@ -13,24 +13,41 @@
 //
 // Work is organised like the KV-outer main branch: the reverse index of the
 // selections lists, per (group, block), the queries that selected it (every
-// pair, no dense split), cut into chunks of up to kKlChunk queries. One
-// workgroup per chunk stages the block's K and k_idx in LDS once and takes
-// the queries 16 at a time (8 waves x 2). Pass 1 writes, per (query, slot),
-// the max and the sum of exp of the index scores over the block; a combine
-// gives each (row, group) its log-normaliser. Pass 2 recomputes the scores,
-// the teacher (S = Q K^T on MFMA; each lane holds four heads of one key) and
-// gs, writes per (query, slot) the loss term and the dq_idx contribution, and
-// accumulates dk_idx for the block's keys over the whole chunk (gs staged in
-// LDS, one key row per lane), added to the output once per chunk.
+// pair, no dense split), cut into chunks of up to 1024 queries. One workgroup
+// per chunk stages the block's K and k_idx (also transposed) in LDS once and
+// takes the queries 16 at a time. Pass 1 writes, per (query, slot), the max
+// and the sum of exp of the index scores over the block; a combine gives each
+// (row, group) its log-normaliser. Pass 2 computes the teacher of each query
+// over the block's keys (S = Q K^T on MFMA, two queries per wave, into LDS),
+// then each wave takes 16 keys for all 16 queries: the index scores in both
+// orientations on MFMA, gs in both layouts, and dk_idx^T = q_idx^T G and
+// dq_idx^T = k_idx^T G^T as MFMAs with gs split into two bf16 parts (about 16
+// significant bits). dq_idx and the loss are summed over the block's key
+// tiles in a fixed order and written per (query, slot); dk_idx is accumulated
+// over the whole chunk and written as the chunk's partial, which a last pass
+// adds, per key block and in a fixed order, to the output (no atomics: the
+// result does not depend on scheduling).
 #include "msa_device.h"
 #include "msa_launch.h"
 
 namespace msa {
 
-constexpr int kKlWaves = 8;
-constexpr int kKStride = 272;    // LDS bytes per staged K row (256 + 16: spreads the banks)
+// staged K: row r at r * 256 bytes, its 16-byte piece p at position p ^ (r & 15)
+// (the teacher's operand reads then hit 64 distinct banks per lane group)
 constexpr int kIStride = 144;    // LDS bytes per staged k_idx row (128 + 16)
-constexpr int kKlLds = kBlock * kKStride + kBlock * kIStride + 16 * kBlock * 4 + 16 * kIndexDim * 2;
+constexpr int kTStride = 272;    // LDS bytes per row of the transposed k_idx (128 keys + 8 pad)
+constexpr int kSub = 16;         // queries per sub-tile
+constexpr int kPStride = 20;     // floats per teacher row (16 queries + 4: spreads the banks)
+constexpr int kQStride = 72;     // bf16 per q_idx row (64 + 8)
+constexpr int kRStride = 17;     // floats per row of the dq reduction buffer (16 queries + 1)
+
+typedef short kl_i16x4 __attribute__((ext_vector_type(4)));
+
+// MFMA 16x16x16 bf16: lane (i, q) holds A[i][4q + j] and B[4q + j][i], j < 4;
+// the result has the 16x16x32 product's layout.
+__device__ __forceinline__ f32x4 kl_mfma16(kl_i16x4 a, kl_i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ float sum_lane_groups(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -39,36 +56,216 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// sum / max over the 16 lanes of a lane group (lanes differing in bits 0-3)
-__device__ __forceinline__ float sum16(float x) {
+// (max, sum of exp) pairs merged over the four lane groups (lanes l ^ 16, l ^ 32)
+__device__ __forceinline__ void merge_lane_groups(float& m, float& l) {
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, kWave);
-  return x;
-}
-
-__device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  for (int o = 16; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), l2 = __shfl_xor(l, o, kWave);
+    const float mn = fmaxf(m, m2);
+    l = (l == 0.f ? 0.f : l * __expf(m - mn)) + (l2 == 0.f ? 0.f : l2 * __expf(m2 - mn));
+    m = mn;
   }
 }
 
-// PASS 1: per-slot (max, sum exp) of the index scores over the block.
-// PASS 2: loss term, dq_idx contribution and the chunk's dk_idx.
-template <int PASS>
-__global__ __launch_bounds__(512, 2) void k_kl_pass(
+// g = hi + lo, both bf16 (about 16 significant bits), packed as MFMA operands
+__device__ __forceinline__ void split_bf16(const float (&g)[4], kl_i16x4& hi, kl_i16x4& lo) {
+  uint32_t h[2], l[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    h[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
+    l[j] = pack_bf16x2(g[2 * j] - bf2f(h[j] & 0xffffu), g[2 * j + 1] - bf2f(h[j] >> 16));
+  }
+  hi = __builtin_bit_cast(kl_i16x4, (u32x2){h[0], h[1]});
+  lo = __builtin_bit_cast(kl_i16x4, (u32x2){l[0], l[1]});
+}
+
+// The sub-tile's per-query data, loaded one sub-tile ahead: thread x < 16 the
+// entry and (pass 2) log-normaliser of query x; thread x < 128 the 16-byte
+// piece x & 7 of query x >> 3's q_idx row.
+struct SubMeta {
+  int ent;
+  float lz;
+  u32x4 qv;
+};
+
+template <bool LZ>
+__device__ __forceinline__ void load_meta(SubMeta& m, const int32_t* entries, const uint16_t* q_idx,
+                                          const float* lse_idx, int at, int nsub, int G, int g) {
+  const int tid = threadIdx.x;
+  m.ent = -1;
+  m.lz = 0.f;
+  m.qv = (u32x4){0u, 0u, 0u, 0u};
+  if (tid < kSub && tid < nsub) {
+    m.ent = entries[at + tid];
+    if (LZ) m.lz = lse_idx[(int64_t)(m.ent >> 4) * G + g];
+  }
+  if (tid < kSub * 8) {
+    const int n = tid >> 3;
+    if (n < nsub) {
+      const int ent = entries[at + n];
+      m.qv = ld16(q_idx + ((int64_t)(ent >> 4) * G + g) * kIndexDim + (tid & 7) * 8);
+    }
+  }
+}
+
+// publishes a SubMeta into LDS: slot, support limit and log-normaliser of each
+// query (limit -1: no query), q_idx rows and their transpose
+template <class L>
+__device__ __forceinline__ void store_meta(L& S, const SubMeta& m, int64_t row0, int64_t key0, int G, int g,
+                                           int topk) {
+  const int tid = threadIdx.x;
+  if (tid < kSub) {
+    int sl = 0, lm = -1;
+    if (m.ent >= 0) {
+      const int i_rel = m.ent >> 4;
+      sl = (i_rel * G + g) * topk + (m.ent & 15);
+      lm = (int)min<int64_t>(kBlock - 1, row0 + i_rel - key0);
+    }
+    S.slot[tid] = sl;
+    S.lim[tid] = lm;
+    S.lz[tid] = m.lz;
+  }
+  if (tid < kSub * 8) {
+    const int n = tid >> 3, ch = tid & 7;
+    *reinterpret_cast<u32x4*>(&S.qib[n][ch * 8]) = m.qv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      S.qibT[ch * 8 + 2 * j][n] = (uint16_t)(m.qv[j] & 0xffffu);
+      S.qibT[ch * 8 + 2 * j + 1][n] = (uint16_t)(m.qv[j] >> 16);
+    }
+  }
+}
+
+// index scores of the wave's 16 keys (kw ..) for the 16 queries of the
+// sub-tile: sa[r] = S_idx[query 4qd + r][key kw + c], sb[r] = S_idx[query c][key kw + 4qd + r]
+template <class L>
+__device__ __forceinline__ void index_scores_tile(const L& S, int kw, f32x4& sa, f32x4& sb) {
+  const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
+  sa = (f32x4){0.f, 0.f, 0.f, 0.f};
+  sb = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(&S.qib[c][32 * st + 8 * qd]));
+    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(S.ist + (kw + c) * kIStride + (32 * st + 8 * qd) * 2));
+    sa = mfma16x16x32(qa, ka, sa);
+    sb = mfma16x16x32(ka, qa, sb);
+  }
+}
+
+template <class L>
+__device__ __forceinline__ void stage_kidx(L& S, const uint16_t* k_idx, int64_t key0, int nvalid, bool transpose) {
+  for (int x = threadIdx.x; x < kBlock * 8; x += blockDim.x) {
+    const int r = x >> 3, ch = x & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < nvalid) v = ld16(k_idx + (key0 + r) * kIndexDim + ch * 8);
+    *reinterpret_cast<u32x4*>(S.ist + r * kIStride + ch * 16) = v;
+    if (transpose) {
+      uint16_t* col = reinterpret_cast<uint16_t*>(S.istT) + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        col[(8 * ch + 2 * j) * (kTStride / 2)] = (uint16_t)(v[j] & 0xffffu);
+        col[(8 * ch + 2 * j + 1) * (kTStride / 2)] = (uint16_t)(v[j] >> 16);
+      }
+    }
+  }
+}
+
+struct KlLds1 {
+  char ist[kBlock * kIStride];            // k_idx rows
+  uint16_t qib[kSub][kQStride];           // q_idx rows of the sub-tile
+  uint16_t qibT[kIndexDim][kSub];         // (unused here)
+  float mlb[8][kSub][2];                  // per-wave (max, sum exp)
+  float lz[kSub];
+  int lim[kSub];                          // keys <= lim are in the query's support
+  int slot[kSub];
+  char istT[1];                           // (unused here)
+};
+
+struct KlLds2 {
+  char kst[kBlock * 256];                 // K rows of the block (swizzled, see above)
+  char ist[kBlock * kIStride];            // k_idx rows
+  char istT[kIndexDim * kTStride];        // k_idx transposed: [dim][key]
+  float pbuf[kBlock][kPStride];           // teacher P_main[key][query]
+  uint16_t qib[kSub][kQStride];
+  uint16_t qibT[kIndexDim][kSub];
+  float red[4][kIndexDim][kRStride];      // dq partials [dim][query] of two key tiles each
+  float lossb[8][kSub];
+  float lz[kSub];                         // log-normaliser of each query
+  int lim[kSub];
+  int slot[kSub];
+};
+
+// Pass 1: per-slot (max, sum exp) of the index scores over the block. Wave w
+// takes keys 16w .. 16w+15 of every query of the sub-tile.
+__global__ __launch_bounds__(512) void k_kl_norm(const uint16_t* __restrict__ q_idx,
+                                                 const uint16_t* __restrict__ k_idx,
+                                                 const int32_t* __restrict__ entries,
+                                                 const int32_t* __restrict__ chunks,
+                                                 const int32_t* __restrict__ chunk_info, float* __restrict__ part_m,
+                                                 float* __restrict__ part_l, int64_t n_tokens, int64_t row0, int G,
+                                                 int topk) {
+  __shared__ __attribute__((aligned(16))) KlLds1 S;
+  const int t_id = blockIdx.x;
+  if (t_id >= chunk_info[0]) return;
+  const int g = chunks[4 * t_id], begin = chunks[4 * t_id + 1], len = chunks[4 * t_id + 2], b = chunks[4 * t_id + 3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, qd = lane >> 4;
+  const int64_t key0 = (int64_t)b * kBlock;
+  const int nvalid = (int)min<int64_t>(kBlock, n_tokens - key0);
+  const int kw = 16 * wave;
+  stage_kidx(S, k_idx, key0, nvalid, false);
+  SubMeta cur, nxt;
+  load_meta<false>(cur, entries, q_idx, nullptr, begin, min(kSub, len), G, g);
+  for (int s0 = 0; s0 < len; s0 += kSub) {
+    const int nsub = min(kSub, len - s0);
+    store_meta(S, cur, row0, key0, G, g, topk);
+    if (s0 + kSub < len) load_meta<false>(nxt, entries, q_idx, nullptr, begin + s0 + kSub, min(kSub, len - s0 - kSub), G, g);
+    __syncthreads();  // block staged; the sub-tile's queries in LDS
+    f32x4 sa, sb;
+    index_scores_tile(S, kw, sa, sb);
+    const int lm = S.lim[c];
+    float m = -__builtin_inff(), l = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (kw + 4 * qd + r <= lm) m = fmaxf(m, sb[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (kw + 4 * qd + r <= lm) l += __expf(sb[r] - m);
+    merge_lane_groups(m, l);
+    if (qd == 0) {
+      S.mlb[wave][c][0] = m;
+      S.mlb[wave][c][1] = l;
+    }
+    __syncthreads();
+    if (tid < nsub) {
+      float mm = -__builtin_inff(), ll = 0.f;
+      for (int w = 0; w < 8; ++w) {
+        const float m2 = S.mlb[w][tid][0], l2 = S.mlb[w][tid][1];
+        const float mn = fmaxf(mm, m2);
+        ll = (ll == 0.f ? 0.f : ll * __expf(mm - mn)) + (l2 == 0.f ? 0.f : l2 * __expf(m2 - mn));
+        mm = mn;
+      }
+      part_m[S.slot[tid]] = mm;
+      part_l[S.slot[tid]] = ll;
+    }
+    __syncthreads();  // before the next sub-tile overwrites the buffers
+    cur = nxt;
+  }
+}
+
+// Pass 2: loss term and dq_idx contribution per slot, and the chunk's dk_idx.
+// Per sub-tile of 16 queries: wave w computes the teacher of queries 2w, 2w+1
+// for all 128 keys into pbuf; then
+// wave w takes keys 16w .. 16w+15 for all 16 queries: S_idx on MFMA in both
+// orientations, gs in both layouts, and dk^T = q_idx^T G, dq^T = k_idx^T G^T
+// as 16x16x16 MFMAs.
+__global__ __launch_bounds__(512, 1) void k_kl_grad(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const float* __restrict__ lse_idx,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ chunks, const int32_t* __restrict__ chunk_info,
-    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ loss_part,
-    float* __restrict__ dq_part, float* __restrict__ dk_idx, int64_t n_tokens, int64_t row0, int G, int topk,
-    float scale_log2) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[kKlLds];
-  char* kst = lds_raw;
-  char* ist = kst + kBlock * kKStride;
-  float* gbuf = reinterpret_cast<float*>(ist + kBlock * kIStride);          // [16 queries][128 keys]
-  uint16_t* qibuf = reinterpret_cast<uint16_t*>(gbuf + 16 * kBlock);         // [16 queries][64]
+    float* __restrict__ loss_part, float* __restrict__ dq_part, float* __restrict__ dk_part, int64_t n_tokens,
+    int64_t row0, int G, int topk, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) KlLds2 S;
   const int t_id = blockIdx.x;
   if (t_id >= chunk_info[0]) return;
   const int g = chunks[4 * t_id], begin = chunks[4 * t_id + 1], len = chunks[4 * t_id + 2], b = chunks[4 * t_id + 3];
@@ -76,160 +273,194 @@ __global__ __launch_bounds__(512, 2) void k_kl_pass(
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
   const int64_t key0 = (int64_t)b * kBlock;
-  const int nvalid = (int)min<int64_t>(kBlock, n_tokens - key0);  // keys of the block that exist
+  const int nvalid = (int)min<int64_t>(kBlock, n_tokens - key0);
+  const int kw = 16 * wave;
 
-  // stage the block: K rows (pass 2) and k_idx rows, zero past the sequence
-  if (PASS == 2) {
-    for (int x = tid; x < kBlock * 16; x += 512) {
-      const int r = x >> 4, ch = x & 15;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < nvalid) v = ld16(k + ((key0 + r) * G + g) * kHeadDim + ch * 8);
-      *reinterpret_cast<u32x4*>(kst + r * kKStride + ch * 16) = v;
-    }
-  }
-  for (int x = tid; x < kBlock * 8; x += 512) {
-    const int r = x >> 3, ch = x & 7;
+  for (int x = tid; x < kBlock * 16; x += 512) {
+    const int r = x >> 4, ch = x & 15;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < nvalid) v = ld16(k_idx + (key0 + r) * kIndexDim + ch * 8);
-    *reinterpret_cast<u32x4*>(ist + r * kIStride + ch * 16) = v;
+    if (r < nvalid) v = ld16(k + ((key0 + r) * G + g) * kHeadDim + ch * 8);
+    *reinterpret_cast<u32x4*>(S.kst + r * 256 + ((ch ^ (r & 15)) << 4)) = v;
   }
-  __syncthreads();
+  stage_kidx(S, k_idx, key0, nvalid, true);
 
-  float dk_acc[16];
+  // the teacher's inputs of the wave's two queries
+  struct TeachIn {
+    int ent[2];
+    bf16x8 qop[2][4];
+    f32x4 lh[2];
+  };
+  auto load_teach = [&](TeachIn& t, int at, int nsub) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) dk_acc[e] = 0.f;
-
-  for (int s0 = 0; s0 < len; s0 += 16) {
-    const int nsub = min(16, len - s0);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int tq = 2 * wave + n;  // query of the sub-tile
-      if (tq >= nsub) continue;  // wave-uniform
-      const int ent = entries[begin + s0 + tq];
-      const int i_rel = ent >> 4, u = ent & 15;
-      const int64_t i = row0 + i_rel;
-      const int64_t slot = ((int64_t)i_rel * G + g) * topk + u;
-      const int lim = (int)min<int64_t>(kBlock - 1, i - key0);  // keys <= lim are in T
-      // the lane's 16 dims of q_idx[i, g]
-      float qi[16];
-      {
-        const uint16_t* src = q_idx + ((int64_t)i_rel * G + g) * kIndexDim + 16 * qd;
-        const u32x4 w0 = ld16(src), w1 = ld16(src + 8);
-        unpack8(w0, qi);
-        unpack8(w1, qi + 8);
-        if (PASS == 2 && c == 0) {
-          *reinterpret_cast<u32x4*>(qibuf + tq * kIndexDim + 16 * qd) = w0;
-          *reinterpret_cast<u32x4*>(qibuf + tq * kIndexDim + 16 * qd + 8) = w1;
-        }
-      }
-      if (PASS == 1) {
-        float m = -__builtin_inff(), l = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int kk = 16 * t + c;
-          float kv[16];
-          unpack8(*reinterpret_cast<const u32x4*>(ist + kk * kIStride + 32 * qd), kv);
-          unpack8(*reinterpret_cast<const u32x4*>(ist + kk * kIStride + 32 * qd + 16), kv + 8);
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s = __builtin_fmaf(qi[e], kv[e], s);
-          s = sum_lane_groups(s);
-          if (kk <= lim) {
-            const float mn = fmaxf(m, s);
-            l = l * __expf(m - mn) + __expf(s - mn);
-            m = mn;
-          }
-        }
-        // merge (m, l) over the 16 keys of the lane group
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float m2 = __shfl_xor(m, o, kWave), l2 = __shfl_xor(l, o, kWave);
-          const float mn = fmaxf(m, m2);
-          l = (l == 0.f ? 0.f : l * __expf(m - mn)) + (l2 == 0.f ? 0.f : l2 * __expf(m2 - mn));
-          m = mn;
-        }
-        if (lane == 0) {
-          part_m[slot] = m;
-          part_l[slot] = l;
-        }
-      } else {
-        bf16x8 qop[4];
+    for (int h = 0; h < 2; ++h) {
+      const int tq = 2 * wave + h;
+      t.ent[h] = -1;
+      if (tq < nsub) {
+        const int ent = entries[at + tq];
+        t.ent[h] = ent;
+        const int i_rel = ent >> 4;
         const uint16_t* qrow = q + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 8 * qd;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) qop[st] = as_bf16x8(ld16(qrow + 32 * st));
-        // log2 e * lse of the lane's four heads 4qd .. 4qd+3
-        const f32x4 lh = *reinterpret_cast<const f32x4*>(lse + (int64_t)i_rel * Hq + g * kHpg + 4 * qd);
-        const float l2e = 1.4426950408889634f;
-        const float lz = lse_idx[(int64_t)i_rel * G + g];
-        float loss = 0.f;
-        float dq[16];
+        for (int st = 0; st < 4; ++st) t.qop[h][st] = as_bf16x8(ld16(qrow + 32 * st));
+        t.lh[h] = *reinterpret_cast<const f32x4*>(lse + (int64_t)i_rel * Hq + g * kHpg + 4 * qd);
+      }
+    }
+  };
+  SubMeta cur, nxt;
+  TeachIn tc;
+  load_meta<true>(cur, entries, q_idx, lse_idx, begin, min(kSub, len), G, g);
+
+  f32x4 dk_acc[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dq[e] = 0.f;
+  for (int dt = 0; dt < 4; ++dt) dk_acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = 0; s0 < len; s0 += kSub) {
+    const int nsub = min(kSub, len - s0);
+    store_meta(S, cur, row0, key0, G, g, topk);
+    load_teach(tc, begin + s0, nsub);
+    if (s0 + kSub < len)
+      load_meta<true>(nxt, entries, q_idx, lse_idx, begin + s0 + kSub, min(kSub, len - s0 - kSub), G, g);
+    if (s0 == 0) __syncthreads();  // K staged
+    // teacher of queries 2w, 2w+1: S = Q K^T per key tile (lane: key c, heads
+    // 4qd .. 4qd+3; each K operand serves both queries), P_main = mean over the
+    // 16 heads of exp(z - lse)
+    {
+      const float l2e = 1.4426950408889634f;
+      int lm[2];
+      f32x4 lh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        lm[h] = tc.ent[h] < 0 ? -1 : (int)min<int64_t>(kBlock - 1, row0 + (tc.ent[h] >> 4) - key0);
+        lh[h] = tc.lh[h] * l2e;
+      }
+      const bool two = tc.ent[1] >= 0;  // wave-uniform
+      if (tc.ent[0] >= 0) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int kk = 16 * t + c;
-          // teacher: S[4qd + r][key kk] = q_h . k_kk over 4 d-steps
-          f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+          f32x4 sm0 = {0.f, 0.f, 0.f, 0.f}, sm1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
-            const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(kst + kk * kKStride + (32 * st + 8 * qd) * 2));
-            sm = mfma16x16x32(qop[st], kb, sm);
+            const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(S.kst + kk * 256 + (((4 * st + qd) ^ c) << 4)));
+            sm0 = mfma16x16x32(tc.qop[0][st], kb, sm0);
+            if (two) sm1 = mfma16x16x32(tc.qop[1][st], kb, sm1);
           }
-          float p = 0.f;
+          float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p += __builtin_amdgcn_exp2f(sm[r] * scale_log2 - lh[r] * l2e);
-          const bool in_t = kk <= lim;
-          p = sum_lane_groups(p);
-          const float pm = in_t ? p * (1.0f / kHpg) : 0.f;
-          // student
-          float kv[16];
-          unpack8(*reinterpret_cast<const u32x4*>(ist + kk * kIStride + 32 * qd), kv);
-          unpack8(*reinterpret_cast<const u32x4*>(ist + kk * kIStride + 32 * qd + 16), kv + 8);
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s = __builtin_fmaf(qi[e], kv[e], s);
-          s = sum_lane_groups(s);
-          const float lp = s - lz;  // log P_idx
-          const float gs = in_t ? __expf(lp) - pm : 0.f;
-          if (in_t && pm > 0.f) loss += pm * (__logf(pm) - lp);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) dq[e] = __builtin_fmaf(gs, kv[e], dq[e]);
-          if (qd == 0) gbuf[tq * kBlock + kk] = gs;
+          for (int r = 0; r < 4; ++r) {
+            p0 += __builtin_amdgcn_exp2f(__builtin_fmaf(sm0[r], scale_log2, -lh[0][r]));
+            p1 += __builtin_amdgcn_exp2f(__builtin_fmaf(sm1[r], scale_log2, -lh[1][r]));
+          }
+          p0 = sum_lane_groups(p0);
+          p1 = sum_lane_groups(p1);
+          if (qd == 0) {
+            S.pbuf[kk][2 * wave] = kk <= lm[0] ? p0 * (1.0f / kHpg) : 0.f;
+            S.pbuf[kk][2 * wave + 1] = kk <= lm[1] ? p1 * (1.0f / kHpg) : 0.f;
+          }
         }
-        loss = sum16(loss);
-        if (lane == 0) loss_part[slot] = loss;
+      } else if (qd == 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dq[e] = sum16(dq[e]);
-        if (c == 0) {
-          float* dst = dq_part + slot * kIndexDim + 16 * qd;
-#pragma unroll
-          for (int e = 0; e < 16; e += 4)
-            *reinterpret_cast<f32x4*>(dst + e) = (f32x4){dq[e], dq[e + 1], dq[e + 2], dq[e + 3]};
-        }
+        for (int t = 0; t < 8; ++t) S.pbuf[16 * t + c][2 * wave] = S.pbuf[16 * t + c][2 * wave + 1] = 0.f;
       }
     }
-    if (PASS == 2) {
-      __syncthreads();  // gs and q_idx of the sub-tile staged
-      // wave w: keys 16w + c; the lane's 16 dims 16qd ..
-      const int kk = 16 * wave + c;
-      for (int n = 0; n < nsub; ++n) {
-        const float gv = gbuf[n * kBlock + kk];
-        float qv[16];
-        unpack8(*reinterpret_cast<const u32x4*>(qibuf + n * kIndexDim + 16 * qd), qv);
-        unpack8(*reinterpret_cast<const u32x4*>(qibuf + n * kIndexDim + 16 * qd + 8), qv + 8);
+    __syncthreads();  // the sub-tile's queries and teacher ready
+
+    f32x4 sa, sb;
+    index_scores_tile(S, kw, sa, sb);
+    // gs in layout a (lane: key kw + c, queries 4qd + r) and b (lane: query c,
+    // keys kw + 4qd + r); the loss terms in layout b
+    float ga[4], gb[4];
+    float loss = 0.f;
+    {
+      const f32x4 pm4 = *reinterpret_cast<const f32x4*>(&S.pbuf[kw + c][4 * qd]);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dk_acc[e] = __builtin_fmaf(gv, qv[e], dk_acc[e]);
+      for (int r = 0; r < 4; ++r) {
+        const int n = 4 * qd + r;
+        ga[r] = kw + c <= S.lim[n] ? __expf(sa[r] - S.lz[n]) - pm4[r] : 0.f;
       }
-      __syncthreads();  // before the next sub-tile overwrites the buffers
+      const int lm = S.lim[c];
+      const float lzc = S.lz[c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kw + 4 * qd + r;
+        const float pm = S.pbuf[kk][c];
+        const float lp = sb[r] - lzc;
+        const bool in_t = kk <= lm;
+        gb[r] = in_t ? __expf(lp) - pm : 0.f;
+        if (in_t && pm > 0.f) loss += pm * (__logf(pm) - lp);
+      }
     }
+    loss = sum_lane_groups(loss);
+    if (qd == 0) S.lossb[wave][c] = loss;
+    kl_i16x4 gah, gal, gbh, gbl;
+    split_bf16(ga, gah, gal);
+    split_bf16(gb, gbh, gbl);
+    f32x4 dq[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      // dk^T[16dt + i][key] += sum_n q_idx[n][16dt + i] G[n][key]
+      const kl_i16x4 qa = *reinterpret_cast<const kl_i16x4*>(&S.qibT[16 * dt + c][4 * qd]);
+      dk_acc[dt] = kl_mfma16(qa, gah, dk_acc[dt]);
+      dk_acc[dt] = kl_mfma16(qa, gal, dk_acc[dt]);
+      // dq^T[16dt + i][query] = sum over the wave's keys of k_idx[key][16dt + i] G^T[key][query]
+      const kl_i16x4 ka = *reinterpret_cast<const kl_i16x4*>(S.istT + (16 * dt + c) * kTStride + (kw + 4 * qd) * 2);
+      dq[dt] = kl_mfma16(ka, gbh, (f32x4){0.f, 0.f, 0.f, 0.f});
+      dq[dt] = kl_mfma16(ka, gbl, dq[dt]);
+    }
+    // dq over the 8 key tiles, in a fixed order: waves 0-3 store, waves 4-7 add
+    // (tile w + (w - 4)), then one thread per (query, dim) sums the four
+    if (wave < 4) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.red[wave][16 * dt + 4 * qd + r][c] = dq[dt][r];
+    }
+    __syncthreads();
+    if (wave >= 4) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.red[wave - 4][16 * dt + 4 * qd + r][c] += dq[dt][r];
+    }
+    __syncthreads();
+    for (int x = tid; x < kSub * kIndexDim; x += 512) {
+      const int n = x >> 6, d = x & 63;
+      if (n < nsub)
+        dq_part[(int64_t)S.slot[n] * kIndexDim + d] = (S.red[0][d][n] + S.red[1][d][n]) + (S.red[2][d][n] + S.red[3][d][n]);
+    }
+    if (tid < nsub) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) v += S.lossb[w][tid];
+      loss_part[S.slot[tid]] = v;
+    }
+    __syncthreads();  // before the next sub-tile overwrites the buffers
+    cur = nxt;
   }
-  if (PASS == 2) {
-    const int kk = 16 * wave + c;
-    if (kk < nvalid) {
-      float* dst = dk_idx + (key0 + kk) * kIndexDim + 16 * qd;
+  // the chunk's dk_idx rows [128 keys][64]: lane (key kw + c, qd) holds dims
+  // 16dt + 4qd .. +3
+  float* dst = dk_part + (int64_t)t_id * kBlock * kIndexDim + (kw + c) * kIndexDim + 4 * qd;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) atomicAdd(dst + e, dk_acc[e]);
+  for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = dk_acc[dt];
+}
+
+// dk_idx of key block b (eight workgroups per block, an eighth of its rows each): the chunk partials of every
+// group's list for b, added in (group, chunk) order to the rows' running sums
+__global__ __launch_bounds__(256) void k_kl_dk(const float* __restrict__ dk_part, const int32_t* __restrict__ tile_start,
+                                               float* __restrict__ dk_idx, int64_t n_tokens, int nbw, int G) {
+  const int b = blockIdx.x;
+  const int64_t key0 = (int64_t)b * kBlock;
+  const int nvalid = (int)min<int64_t>(kBlock, n_tokens - key0);
+  constexpr int kPer = kBlock * kIndexDim / 4 / 8;  // f32x4 of the workgroup's eighth
+  for (int x = blockIdx.y * kPer + threadIdx.x; x < (blockIdx.y + 1) * kPer; x += blockDim.x) {
+    const int kk = (x * 4) / kIndexDim;
+    if (kk >= nvalid) continue;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(dk_idx + key0 * kIndexDim + x * 4);
+    for (int g = 0; g < G; ++g) {
+      const int t0 = tile_start[g * nbw + b], t1 = tile_start[g * nbw + b + 1];
+      for (int t = t0; t < t1; ++t) acc = acc + *reinterpret_cast<const f32x4*>(dk_part + (int64_t)t * kBlock * kIndexDim + x * 4);
     }
+    *reinterpret_cast<f32x4*>(dk_idx + key0 * kIndexDim + x * 4) = acc;
   }
 }
 
@@ -274,15 +505,16 @@ __global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t
 
 void launch_kl_window(const LaunchKl& a, hipStream_t st) {
   if (a.nrows <= 0) return;
-  hipLaunchKernelGGL(k_kl_pass<1>, dim3(a.chunk_cap), dim3(512), 0, st, a.q, a.k, a.q_idx, a.k_idx, a.lse,
-                     a.lse_idx, a.entries, a.chunks, a.chunk_info, a.part_m, a.part_l, a.loss_part, a.dq_part,
-                     a.dk_idx, a.n_tokens, a.row0, a.G, a.topk, a.scale_log2);
+  hipLaunchKernelGGL(k_kl_norm, dim3(a.chunk_cap), dim3(512), 0, st, a.q_idx, a.k_idx, a.entries, a.chunks,
+                     a.chunk_info, a.part_m, a.part_l, a.n_tokens, a.row0, a.G, a.topk);
   const int64_t rows = (int64_t)a.nrows * a.G;
   hipLaunchKernelGGL(k_kl_lse, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a.part_m, a.part_l,
                      a.lse_idx, a.nrows, a.row0, a.G, a.topk);
-  hipLaunchKernelGGL(k_kl_pass<2>, dim3(a.chunk_cap), dim3(512), 0, st, a.q, a.k, a.q_idx, a.k_idx, a.lse,
-                     a.lse_idx, a.entries, a.chunks, a.chunk_info, a.part_m, a.part_l, a.loss_part, a.dq_part,
-                     a.dk_idx, a.n_tokens, a.row0, a.G, a.topk, a.scale_log2);
+  hipLaunchKernelGGL(k_kl_grad, dim3(a.chunk_cap), dim3(512), 0, st, a.q, a.k, a.q_idx, a.k_idx, a.lse, a.lse_idx,
+                     a.entries, a.chunks, a.chunk_info, a.loss_part, a.dq_part, a.dk_part, a.n_tokens, a.row0, a.G,
+                     a.topk, a.scale_log2);
+  hipLaunchKernelGGL(k_kl_dk, dim3(a.nbw, 8), dim3(256), 0, st, a.dk_part, a.tile_start, a.dk_idx, a.n_tokens, a.nbw,
+                     a.G);
   hipLaunchKernelGGL(k_kl_out, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a.loss_part, a.dq_part,
                      a.loss, a.dq_idx, a.nrows, a.row0, a.n_tokens, a.G, a.topk);
 }

@@ -151,9 +151,11 @@ struct LaunchKl {
   float* lse_idx;         // [i_rel*G + g]
   float* loss;            // [G][n_tokens]
   float* dq_idx;          // [i - row0][G][64]
-  float* dk_idx;          // [position][64], accumulated
+  float* dk_idx;          // [position][64], accumulated over windows
+  float* dk_part;         // [chunk][128][64]: each chunk's dk_idx rows
+  const int32_t* tile_start;  // [G*nbw + 1]: first chunk of each (group, block) list
   int64_t n_tokens, row0;
-  int nrows, G, topk;
+  int nrows, nbw, G, topk;
   float scale_log2;
 };
 void launch_kl_window(const LaunchKl& a, hipStream_t st);

@@ -189,9 +189,8 @@ msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_c
  *   lse       fp32 [seq_len, Hq]        msa_prefill's lse_out (natural log), 16-byte aligned
  *   loss      fp32 [G, seq_len]
  *   dq_idx    fp32 [seq_len, G, d_idx]  (written)
- *   dk_idx    fp32 [seq_len, d_idx]     (written; accumulated with atomics, so
- *                                        the summation order, and the last bits,
- *                                        may vary between calls)
+ *   dk_idx    fp32 [seq_len, d_idx]     (written; summed in a fixed order, so the
+ *                                        result is the same on every call)
  *   workspace >= msa_index_kl_workspace_bytes(p, seq_len) bytes
  * The teacher uses the forward's lse, so P_main is the forward's attention
  * distribution up to its rounding. Returns 0 / an error status as above. */

@@ -104,3 +104,16 @@ def test_kl_backward_32k_sampled_and_identities():
     rt = torch.as_tensor(rows, device="cuda")
     compare_loss(loss[:, rt].T, ref["loss"], "loss (sampled)")
     compare_grad(dq[rt], ref["dq_idx"], "dq_idx (sampled)")
+
+
+def test_kl_backward_deterministic():
+    """Every sum is taken in a fixed order (no atomics): two calls agree bit for bit."""
+    inp = syn.PrefillInputs(3000, dims(4, 16), 12, "planted", n_planted=3)
+    q, k, v, qi, ki = prefill_device_inputs(inp)
+    _, sel, lse = msa.prefill(q, k, v, qi, ki, topk=16, want_sel=True, want_lse=True)
+    a = msa.index_kl_backward(q[0], k[0], qi[0], ki[0], sel[0].contiguous(), lse[0].contiguous(), topk=16)
+    a = [x.clone() for x in a]
+    b = msa.index_kl_backward(q[0], k[0], qi[0], ki[0], sel[0].contiguous(), lse[0].contiguous(), topk=16)
+    torch.cuda.synchronize()
+    for x, y, name in zip(a, b, ("loss", "dq_idx", "dk_idx")):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32)), name
