@@ -27,6 +27,8 @@
 // over the whole chunk and written as the chunk's partial, which a last pass
 // adds, per key block and in a fixed order, to the output (no atomics: the
 // result does not depend on scheduling).
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -36,12 +38,48 @@ namespace msa {
 // (the teacher's operand reads then hit 64 distinct banks per lane group)
 constexpr int kIStride = 144;    // LDS bytes per staged k_idx row (128 + 16)
 constexpr int kTStride = 272;    // LDS bytes per row of the transposed k_idx (128 keys + 8 pad)
-constexpr int kSub = 16;         // queries per sub-tile
-constexpr int kPStride = 20;     // floats per teacher row (16 queries + 4: spreads the banks)
+constexpr int kSub = 16;         // queries per sub-tile of pass 1
+constexpr int kSub2 = 16;        // queries per sub-tile of pass 2 (MFMA column blocks of 16)
+constexpr int kPStride = kSub2 + 4;  // floats per teacher row (spreads the banks)
 constexpr int kQStride = 72;     // bf16 per q_idx row (64 + 8)
-constexpr int kRStride = 17;     // floats per row of the dq reduction buffer (16 queries + 1)
+constexpr int kRStride = kSub2 + 1;  // floats per row of the dq reduction buffer
 
 typedef short kl_i16x4 __attribute__((ext_vector_type(4)));
+
+// Scheduling pattern of one pipelined region: NM MFMAs, NV VALU and ND LDS
+// reads spread evenly between them; nothing moves across the region's end.
+template <int NM, int NV, int ND, int I = 0>
+__device__ __forceinline__ void kl_sched_region() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    constexpr int vi = (NV * (I + 1)) / NM - (NV * I) / NM;
+    constexpr int di = (ND * (I + 1)) / NM - (ND * I) / NM;
+    if constexpr (vi > 0) __builtin_amdgcn_sched_group_barrier(0x002, vi, 0);  // VALU
+    if constexpr (di > 0) __builtin_amdgcn_sched_group_barrier(0x100, di, 0);  // LDS read
+    kl_sched_region<NM, NV, ND, I + 1>();
+  } else {
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Workgroup barrier for LDS data: this wave's LDS operations complete, then
+// s_barrier. Unlike __syncthreads it does not wait for outstanding global
+// loads, so data prefetched into registers stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // MFMA 16x16x16 bf16: lane (i, q) holds A[i][4q + j] and B[4q + j][i], j < 4;
 // the result has the 16x16x32 product's layout.
@@ -88,18 +126,18 @@ struct SubMeta {
   u32x4 qv;
 };
 
-template <bool LZ>
+template <bool LZ, int NQ>
 __device__ __forceinline__ void load_meta(SubMeta& m, const int32_t* entries, const uint16_t* q_idx,
                                           const float* lse_idx, int at, int nsub, int G, int g) {
   const int tid = threadIdx.x;
   m.ent = -1;
   m.lz = 0.f;
   m.qv = (u32x4){0u, 0u, 0u, 0u};
-  if (tid < kSub && tid < nsub) {
+  if (tid < NQ && tid < nsub) {
     m.ent = entries[at + tid];
     if (LZ) m.lz = lse_idx[(int64_t)(m.ent >> 4) * G + g];
   }
-  if (tid < kSub * 8) {
+  if (tid < NQ * 8) {
     const int n = tid >> 3;
     if (n < nsub) {
       const int ent = entries[at + n];
@@ -110,11 +148,11 @@ __device__ __forceinline__ void load_meta(SubMeta& m, const int32_t* entries, co
 
 // publishes a SubMeta into LDS: slot, support limit and log-normaliser of each
 // query (limit -1: no query), q_idx rows and their transpose
-template <class L>
+template <int NQ, class L>
 __device__ __forceinline__ void store_meta(L& S, const SubMeta& m, int64_t row0, int64_t key0, int G, int g,
                                            int topk) {
   const int tid = threadIdx.x;
-  if (tid < kSub) {
+  if (tid < NQ) {
     int sl = 0, lm = -1;
     if (m.ent >= 0) {
       const int i_rel = m.ent >> 4;
@@ -125,7 +163,7 @@ __device__ __forceinline__ void store_meta(L& S, const SubMeta& m, int64_t row0,
     S.lim[tid] = lm;
     S.lz[tid] = m.lz;
   }
-  if (tid < kSub * 8) {
+  if (tid < NQ * 8) {
     const int n = tid >> 3, ch = tid & 7;
     *reinterpret_cast<u32x4*>(&S.qib[n][ch * 8]) = m.qv;
 #pragma unroll
@@ -136,16 +174,17 @@ __device__ __forceinline__ void store_meta(L& S, const SubMeta& m, int64_t row0,
   }
 }
 
-// index scores of the wave's 16 keys (kw ..) for the 16 queries of the
-// sub-tile: sa[r] = S_idx[query 4qd + r][key kw + c], sb[r] = S_idx[query c][key kw + 4qd + r]
+// index scores of the wave's 16 keys (kw ..) for queries 16j .. 16j+15 of the
+// sub-tile: sa[r] = S_idx[query 16j + 4qd + r][key kw + c],
+// sb[r] = S_idx[query 16j + c][key kw + 4qd + r]
 template <class L>
-__device__ __forceinline__ void index_scores_tile(const L& S, int kw, f32x4& sa, f32x4& sb) {
+__device__ __forceinline__ void index_scores_tile(const L& S, int kw, int j, f32x4& sa, f32x4& sb) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
   sa = (f32x4){0.f, 0.f, 0.f, 0.f};
   sb = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(&S.qib[c][32 * st + 8 * qd]));
+    const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(&S.qib[16 * j + c][32 * st + 8 * qd]));
     const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(S.ist + (kw + c) * kIStride + (32 * st + 8 * qd) * 2));
     sa = mfma16x16x32(qa, ka, sa);
     sb = mfma16x16x32(ka, qa, sb);
@@ -186,13 +225,13 @@ struct KlLds2 {
   char ist[kBlock * kIStride];            // k_idx rows
   char istT[kIndexDim * kTStride];        // k_idx transposed: [dim][key]
   float pbuf[kBlock][kPStride];           // teacher P_main[key][query]
-  uint16_t qib[kSub][kQStride];
-  uint16_t qibT[kIndexDim][kSub];
+  uint16_t qib[kSub2][kQStride];
+  uint16_t qibT[kIndexDim][kSub2];
   float red[4][kIndexDim][kRStride];      // dq partials [dim][query] of two key tiles each
-  float lossb[8][kSub];
-  float lz[kSub];                         // log-normaliser of each query
-  int lim[kSub];
-  int slot[kSub];
+  float lossb[8][kSub2];
+  float lz[kSub2];                        // log-normaliser of each query
+  int lim[kSub2];
+  int slot[kSub2];
 };
 
 // Pass 1: per-slot (max, sum exp) of the index scores over the block. Wave w
@@ -215,14 +254,15 @@ __global__ __launch_bounds__(512) void k_kl_norm(const uint16_t* __restrict__ q_
   const int kw = 16 * wave;
   stage_kidx(S, k_idx, key0, nvalid, false);
   SubMeta cur, nxt;
-  load_meta<false>(cur, entries, q_idx, nullptr, begin, min(kSub, len), G, g);
+  load_meta<false, kSub>(cur, entries, q_idx, nullptr, begin, min(kSub, len), G, g);
   for (int s0 = 0; s0 < len; s0 += kSub) {
     const int nsub = min(kSub, len - s0);
-    store_meta(S, cur, row0, key0, G, g, topk);
-    if (s0 + kSub < len) load_meta<false>(nxt, entries, q_idx, nullptr, begin + s0 + kSub, min(kSub, len - s0 - kSub), G, g);
-    __syncthreads();  // block staged; the sub-tile's queries in LDS
+    store_meta<kSub>(S, cur, row0, key0, G, g, topk);
+    if (s0 + kSub < len)
+      load_meta<false, kSub>(nxt, entries, q_idx, nullptr, begin + s0 + kSub, min(kSub, len - s0 - kSub), G, g);
+    lds_barrier();  // block staged; the sub-tile's queries in LDS
     f32x4 sa, sb;
-    index_scores_tile(S, kw, sa, sb);
+    index_scores_tile(S, kw, 0, sa, sb);
     const int lm = S.lim[c];
     float m = -__builtin_inff(), l = 0.f;
 #pragma unroll
@@ -236,7 +276,7 @@ __global__ __launch_bounds__(512) void k_kl_norm(const uint16_t* __restrict__ q_
       S.mlb[wave][c][0] = m;
       S.mlb[wave][c][1] = l;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < nsub) {
       float mm = -__builtin_inff(), ll = 0.f;
       for (int w = 0; w < 8; ++w) {
@@ -248,17 +288,17 @@ __global__ __launch_bounds__(512) void k_kl_norm(const uint16_t* __restrict__ q_
       part_m[S.slot[tid]] = mm;
       part_l[S.slot[tid]] = ll;
     }
-    __syncthreads();  // before the next sub-tile overwrites the buffers
+    lds_barrier();  // before the next sub-tile overwrites the buffers
     cur = nxt;
   }
 }
 
 // Pass 2: loss term and dq_idx contribution per slot, and the chunk's dk_idx.
-// Per sub-tile of 16 queries: wave w computes the teacher of queries 2w, 2w+1
-// for all 128 keys into pbuf; then
-// wave w takes keys 16w .. 16w+15 for all 16 queries: S_idx on MFMA in both
-// orientations, gs in both layouts, and dk^T = q_idx^T G, dq^T = k_idx^T G^T
-// as 16x16x16 MFMAs.
+// Per sub-tile of kSub2 queries: wave w computes the teacher of its kSub2/8
+// queries for all 128 keys into pbuf (key tiles software-pipelined); then wave
+// w takes keys 16w .. 16w+15 for all the sub-tile's queries (column blocks of
+// 16): S_idx on MFMA in both orientations, gs in both layouts, and
+// dk^T = q_idx^T G, dq^T = k_idx^T G^T as 16x16x16 MFMAs.
 __global__ __launch_bounds__(512, 1) void k_kl_grad(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const float* __restrict__ lse_idx,
@@ -284,16 +324,17 @@ __global__ __launch_bounds__(512, 1) void k_kl_grad(
   }
   stage_kidx(S, k_idx, key0, nvalid, true);
 
-  // the teacher's inputs of the wave's two queries
+  // the teacher's inputs of the wave's queries TQ*w ..
+  constexpr int TQ = kSub2 / 8;
   struct TeachIn {
-    int ent[2];
-    bf16x8 qop[2][4];
-    f32x4 lh[2];
+    int ent[TQ];
+    bf16x8 qop[TQ][4];
+    f32x4 lh[TQ];
   };
   auto load_teach = [&](TeachIn& t, int at, int nsub) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int tq = 2 * wave + h;
+    for (int h = 0; h < TQ; ++h) {
+      const int tq = TQ * wave + h;
       t.ent[h] = -1;
       if (tq < nsub) {
         const int ent = entries[at + tq];
@@ -307,123 +348,152 @@ __global__ __launch_bounds__(512, 1) void k_kl_grad(
     }
   };
   SubMeta cur, nxt;
-  TeachIn tc;
-  load_meta<true>(cur, entries, q_idx, lse_idx, begin, min(kSub, len), G, g);
+  TeachIn tc, tn;
+  load_meta<true, kSub2>(cur, entries, q_idx, lse_idx, begin, min(kSub2, len), G, g);
+  load_teach(tc, begin, min(kSub2, len));
 
   f32x4 dk_acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dk_acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = 0; s0 < len; s0 += kSub) {
-    const int nsub = min(kSub, len - s0);
-    store_meta(S, cur, row0, key0, G, g, topk);
-    load_teach(tc, begin + s0, nsub);
-    if (s0 + kSub < len)
-      load_meta<true>(nxt, entries, q_idx, lse_idx, begin + s0 + kSub, min(kSub, len - s0 - kSub), G, g);
-    if (s0 == 0) __syncthreads();  // K staged
-    // teacher of queries 2w, 2w+1: S = Q K^T per key tile (lane: key c, heads
-    // 4qd .. 4qd+3; each K operand serves both queries), P_main = mean over the
+  for (int s0 = 0; s0 < len; s0 += kSub2) {
+    const int nsub = min(kSub2, len - s0);
+    store_meta<kSub2>(S, cur, row0, key0, G, g, topk);
+    // the next sub-tile's inputs stream in while this one is computed
+    if (s0 + kSub2 < len) {
+      load_meta<true, kSub2>(nxt, entries, q_idx, lse_idx, begin + s0 + kSub2, min(kSub2, len - s0 - kSub2), G, g);
+      load_teach(tn, begin + s0 + kSub2, min(kSub2, len - s0 - kSub2));
+    }
+    if (s0 == 0) lds_barrier();  // K staged
+    // teacher of the wave's queries: S = Q K^T per key tile (lane: key c, heads
+    // 4qd .. 4qd+3; each K operand serves all of them), P_main = mean over the
     // 16 heads of exp(z - lse)
     {
       const float l2e = 1.4426950408889634f;
-      int lm[2];
-      f32x4 lh[2];
+      int lm[TQ];
+      f32x4 lh[TQ];
+      int nq = 0;  // valid queries of the wave (a prefix; wave-uniform)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < TQ; ++h) {
         lm[h] = tc.ent[h] < 0 ? -1 : (int)min<int64_t>(kBlock - 1, row0 + (tc.ent[h] >> 4) - key0);
         lh[h] = tc.lh[h] * l2e;
+        nq += tc.ent[h] >= 0;
       }
-      const bool two = tc.ent[1] >= 0;  // wave-uniform
-      if (tc.ent[0] >= 0) {
+      // key tiles software-pipelined: the MFMAs of tile t+1 are issued between
+      // the exponentials of tile t (their K operands read one tile ahead)
+      f32x4 sm[2][TQ];
+      bf16x8 kb[2][4];
+      auto read_k = [&](bf16x8 (&dst)[4], int t) {
+        const int kk = 16 * t + c;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int kk = 16 * t + c;
-          f32x4 sm0 = {0.f, 0.f, 0.f, 0.f}, sm1 = {0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < 4; ++st)
+          dst[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(S.kst + kk * 256 + (((4 * st + qd) ^ c) << 4)));
+      };
+      auto qk = [&](f32x4 (&dst)[TQ], const bf16x8 (&kop)[4]) {
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(S.kst + kk * 256 + (((4 * st + qd) ^ c) << 4)));
-            sm0 = mfma16x16x32(tc.qop[0][st], kb, sm0);
-            if (two) sm1 = mfma16x16x32(tc.qop[1][st], kb, sm1);
-          }
-          float p0 = 0.f, p1 = 0.f;
+        for (int h = 0; h < TQ; ++h) dst[h] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p0 += __builtin_amdgcn_exp2f(__builtin_fmaf(sm0[r], scale_log2, -lh[0][r]));
-            p1 += __builtin_amdgcn_exp2f(__builtin_fmaf(sm1[r], scale_log2, -lh[1][r]));
-          }
-          p0 = sum_lane_groups(p0);
-          p1 = sum_lane_groups(p1);
-          if (qd == 0) {
-            S.pbuf[kk][2 * wave] = kk <= lm[0] ? p0 * (1.0f / kHpg) : 0.f;
-            S.pbuf[kk][2 * wave + 1] = kk <= lm[1] ? p1 * (1.0f / kHpg) : 0.f;
-          }
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int h = 0; h < TQ; ++h)
+            if (h < nq) dst[h] = mfma16x16x32(tc.qop[h][st], kop[st], dst[h]);
+      };
+      read_k(kb[0], 0);
+      qk(sm[0], kb[0]);
+      read_k(kb[1], 1);
+      static_for<0, 8>([&](auto it) {
+        constexpr int t = decltype(it)::value;
+        if constexpr (t + 2 < 8) read_k(kb[t & 1], t + 2);
+        if constexpr (t + 1 < 8) qk(sm[(t + 1) & 1], kb[(t + 1) & 1]);
+        const int kk = 16 * t + c;
+#pragma unroll
+        for (int h = 0; h < TQ; ++h) {
+          float p = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            p += __builtin_amdgcn_exp2f(__builtin_fmaf(sm[t & 1][h][r], scale_log2, -lh[h][r]));
+          p = sum_lane_groups(p);
+          if (qd == 0) S.pbuf[kk][TQ * wave + h] = kk <= lm[h] ? p * (1.0f / kHpg) : 0.f;
         }
-      } else if (qd == 0) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) S.pbuf[16 * t + c][2 * wave] = S.pbuf[16 * t + c][2 * wave + 1] = 0.f;
-      }
+        constexpr int nm = t + 1 < 8 ? 4 * TQ : 0, nd = t + 2 < 8 ? 4 : 0;
+        kl_sched_region<nm, TQ * 14, nd>();
+      });
     }
-    __syncthreads();  // the sub-tile's queries and teacher ready
+    lds_barrier();  // the sub-tile's queries and teacher ready
 
-    f32x4 sa, sb;
-    index_scores_tile(S, kw, sa, sb);
-    // gs in layout a (lane: key kw + c, queries 4qd + r) and b (lane: query c,
-    // keys kw + 4qd + r); the loss terms in layout b
-    float ga[4], gb[4];
-    float loss = 0.f;
-    {
-      const f32x4 pm4 = *reinterpret_cast<const f32x4*>(&S.pbuf[kw + c][4 * qd]);
+    // index part: wave w, keys kw .. kw+15, queries in column blocks of 16
+    constexpr int NJ = kSub2 / 16;
+    float loss[NJ];
+    f32x4 dq[NJ][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = 4 * qd + r;
-        ga[r] = kw + c <= S.lim[n] ? __expf(sa[r] - S.lz[n]) - pm4[r] : 0.f;
+    for (int j = 0; j < NJ; ++j) {
+      f32x4 sa, sb;
+      index_scores_tile(S, kw, j, sa, sb);
+      // gs in layout a (lane: key kw + c, queries 16j + 4qd + r) and b (lane:
+      // query 16j + c, keys kw + 4qd + r); the loss terms in layout b
+      float ga[4], gb[4];
+      float ls = 0.f;
+      {
+        const f32x4 pm4 = *reinterpret_cast<const f32x4*>(&S.pbuf[kw + c][16 * j + 4 * qd]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = 16 * j + 4 * qd + r;
+          ga[r] = kw + c <= S.lim[n] ? __expf(sa[r] - S.lz[n]) - pm4[r] : 0.f;
+        }
+        const int n = 16 * j + c;
+        const int lm = S.lim[n];
+        const float lzc = S.lz[n];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = kw + 4 * qd + r;
+          const float pm = S.pbuf[kk][n];
+          const float lp = sb[r] - lzc;
+          const bool in_t = kk <= lm;
+          gb[r] = in_t ? __expf(lp) - pm : 0.f;
+          if (in_t && pm > 0.f) ls += pm * (__logf(pm) - lp);
+        }
       }
-      const int lm = S.lim[c];
-      const float lzc = S.lz[c];
+      loss[j] = sum_lane_groups(ls);
+      kl_i16x4 gah, gal, gbh, gbl;
+      split_bf16(ga, gah, gal);
+      split_bf16(gb, gbh, gbl);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = kw + 4 * qd + r;
-        const float pm = S.pbuf[kk][c];
-        const float lp = sb[r] - lzc;
-        const bool in_t = kk <= lm;
-        gb[r] = in_t ? __expf(lp) - pm : 0.f;
-        if (in_t && pm > 0.f) loss += pm * (__logf(pm) - lp);
+      for (int dt = 0; dt < 4; ++dt) {
+        // dk^T[16dt + i][key] += sum_n q_idx[n][16dt + i] G[n][key]
+        const kl_i16x4 qa = *reinterpret_cast<const kl_i16x4*>(&S.qibT[16 * dt + c][16 * j + 4 * qd]);
+        dk_acc[dt] = kl_mfma16(qa, gah, dk_acc[dt]);
+        dk_acc[dt] = kl_mfma16(qa, gal, dk_acc[dt]);
+        // dq^T[16dt + i][query] = sum over the wave's keys of k_idx[key][16dt + i] G^T[key][query]
+        const kl_i16x4 ka = *reinterpret_cast<const kl_i16x4*>(S.istT + (16 * dt + c) * kTStride + (kw + 4 * qd) * 2);
+        dq[j][dt] = kl_mfma16(ka, gbh, (f32x4){0.f, 0.f, 0.f, 0.f});
+        dq[j][dt] = kl_mfma16(ka, gbl, dq[j][dt]);
       }
     }
-    loss = sum_lane_groups(loss);
-    if (qd == 0) S.lossb[wave][c] = loss;
-    kl_i16x4 gah, gal, gbh, gbl;
-    split_bf16(ga, gah, gal);
-    split_bf16(gb, gbh, gbl);
-    f32x4 dq[4];
+    if (qd == 0) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      // dk^T[16dt + i][key] += sum_n q_idx[n][16dt + i] G[n][key]
-      const kl_i16x4 qa = *reinterpret_cast<const kl_i16x4*>(&S.qibT[16 * dt + c][4 * qd]);
-      dk_acc[dt] = kl_mfma16(qa, gah, dk_acc[dt]);
-      dk_acc[dt] = kl_mfma16(qa, gal, dk_acc[dt]);
-      // dq^T[16dt + i][query] = sum over the wave's keys of k_idx[key][16dt + i] G^T[key][query]
-      const kl_i16x4 ka = *reinterpret_cast<const kl_i16x4*>(S.istT + (16 * dt + c) * kTStride + (kw + 4 * qd) * 2);
-      dq[dt] = kl_mfma16(ka, gbh, (f32x4){0.f, 0.f, 0.f, 0.f});
-      dq[dt] = kl_mfma16(ka, gbl, dq[dt]);
+      for (int j = 0; j < NJ; ++j) S.lossb[wave][16 * j + c] = loss[j];
     }
-    // dq over the 8 key tiles, in a fixed order: waves 0-3 store, waves 4-7 add
-    // (tile w + (w - 4)), then one thread per (query, dim) sums the four
+    // dq over the 8 key tiles in a fixed order: waves 0-3 store, waves 4-7 add
+    // theirs (tile w + (w - 4)), then one thread per (query, dim) sums the four
     if (wave < 4) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S.red[wave][16 * dt + 4 * qd + r][c] = dq[dt][r];
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.red[wave][16 * dt + 4 * qd + r][16 * j + c] = dq[j][dt][r];
     }
-    __syncthreads();
+    lds_barrier();
     if (wave >= 4) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S.red[wave - 4][16 * dt + 4 * qd + r][c] += dq[dt][r];
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.red[wave - 4][16 * dt + 4 * qd + r][16 * j + c] += dq[j][dt][r];
     }
-    __syncthreads();
-    for (int x = tid; x < kSub * kIndexDim; x += 512) {
+    lds_barrier();
+    for (int x = tid; x < kSub2 * kIndexDim; x += 512) {
       const int n = x >> 6, d = x & 63;
       if (n < nsub)
         dq_part[(int64_t)S.slot[n] * kIndexDim + d] = (S.red[0][d][n] + S.red[1][d][n]) + (S.red[2][d][n] + S.red[3][d][n]);
@@ -434,8 +504,9 @@ __global__ __launch_bounds__(512, 1) void k_kl_grad(
       for (int w = 0; w < 8; ++w) v += S.lossb[w][tid];
       loss_part[S.slot[tid]] = v;
     }
-    __syncthreads();  // before the next sub-tile overwrites the buffers
+    lds_barrier();  // before the next sub-tile overwrites the buffers
     cur = nxt;
+    tc = tn;
   }
   // the chunk's dk_idx rows [128 keys][64]: lane (key kw + c, qd) holds dims
   // 16dt + 4qd .. +3
