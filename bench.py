@@ -11,7 +11,9 @@ F_main / t_prefill, where F_main = 4 * d * hpg * sum over (query, group) of the
 attended token count and t_prefill is the whole prefill call (index branch
 included). Decode KV GB/s (algorithmic bytes / whole decode call) is reported
 alongside, with per-stage times from the profiled entry points and the
-roofline of the dominant kernel.
+roofline of the dominant kernel. Side measurements (not part of a step):
+chunked and variable-length prefill, the Index Branch KL-alignment
+backward, and prefill / decode at B_k 64 and 32.
 """
 from __future__ import annotations
 
@@ -57,11 +59,12 @@ def prefill_flops(rows, n_groups=G, hpg=HQ // G, d=D, topk=TOPK):
 def prefill_flops_full(n, **kw):
     # closed form summed per block for speed
     topk = kw.get("topk", TOPK)
+    bk = kw.get("bk", BK)
     tot = 0
-    for blk in range((n + BK - 1) // BK):
-        lo, hi = blk * BK, min(n, (blk + 1) * BK)
+    for blk in range((n + bk - 1) // bk):
+        lo, hi = blk * bk, min(n, (blk + 1) * bk)
         cnt = hi - lo
-        tot += cnt * BK * (min(topk, blk + 1) - 1) + sum(range(1, cnt + 1))
+        tot += cnt * bk * (min(topk, blk + 1) - 1) + sum(range(1, cnt + 1))
     return 4.0 * kw.get("d", D) * kw.get("hpg", HQ // G) * kw.get("n_groups", G) * tot
 
 
@@ -74,14 +77,14 @@ def index_flops_full(n, topk=TOPK):
     return 2.0 * DI * G * tot
 
 
-def decode_bytes(ctx_lens, topk=TOPK):
+def decode_bytes(ctx_lens, topk=TOPK, bk=BK):
     tot = 0
     for L in ctx_lens:
         i = L - 1
-        b_loc = i // BK
-        scored = BK * b_loc if b_loc >= topk else 0
+        b_loc = i // bk
+        scored = bk * b_loc if b_loc >= topk else 0
         tot += scored * DI * 2                                # k_idx keys scored
-        tot += G * attended_tokens(i, topk) * 2 * D * 2       # K and V of the attended tokens
+        tot += G * attended_tokens(i, topk, bk) * 2 * D * 2   # K and V of the attended tokens
         tot += HQ * D * 2 * 2 + G * DI * 2                    # q, out, q_idx
     return float(tot)
 
@@ -150,21 +153,82 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def kernel_roofline(name, ms, flops, nbytes):
+def kernel_roofline(name, ms, flops, nbytes, measured=True):
     """Roofline position of one kernel: the bound is whichever of the MFMA
     time (flops at the bf16 peak) and the HBM time (algorithmic bytes at the
-    HBM peak) is larger; achieved and frac are in that bound's unit."""
+    HBM peak) is larger; achieved and frac are in that bound's unit.
+    measured=False: no counter figures exist for this launch configuration."""
     t = ms * 1e-3
     mfma_bound = flops / (MFMA_PEAK_TFLOPS * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         ach, peak, unit = flops / t / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s"
     else:
         ach, peak, unit = nbytes / t / 1e9, HBM_PEAK_GBS, "GB/s"
-    traffic = MEASURED_TRAFFIC.get(name) if MEASURED_TRAFFIC["source"] == source_hash() else None
+    traffic = MEASURED_TRAFFIC.get(name) if measured and MEASURED_TRAFFIC["source"] == source_hash() else None
     return {"kernel": name, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(ach, 2), "peak": peak,
             "unit": unit, "frac": round(ach / peak, 4), "traffic": traffic, "ms": round(ms, 4),
             "algorithmic_tflop": round(flops / 1e12, 4), "algorithmic_gb": round(nbytes / 1e9, 4),
             "tflops": round(flops / t / 1e12, 2), "GB/s": round(nbytes / t / 1e9, 1)}
+
+
+def attention_rooflines(torch, sel, n, stage, bk=BK, topk=TOPK, measured=True):
+    """Both attention kernels' roofline positions from the actual selection
+    sel [G, n, k]: algorithmic flops per attended key, algorithmic bytes = each
+    pass's K/V blocks once, the (query, group) inputs and outputs, and the
+    KV-outer partials written once and read once. Both kernels stage 128 keys
+    at a time, so at B_k < 128 they execute 128/B_k times the flops of a full
+    block ("executed_tflop")."""
+    ps = pair_stats(torch, sel, n, bk=bk)
+    q_bytes = HQ // G * D * 2                     # one (query, group): 16 heads x 128 dims, bf16
+    part_bytes = q_bytes + HQ // G * 4            # normalised bf16 partial + fp32 lse per head
+    kv_block = 2 * bk * D * 2                     # K and V of one block of one group
+    b_kv = ps["sparse_pairs"] * (q_bytes + part_bytes) + ps["kv_sparse"] * kv_block
+    b_dm = (n * G * (2 * q_bytes + topk * 4) + ps["kv_dense"] * kv_block + ps["sparse_pairs"] * part_bytes)
+    kernels = [kernel_roofline("k_attn_prefill (KV-outer)", stage["kv_outer_attn"], ps["F_sparse"], b_kv, measured),
+               kernel_roofline("k_attn_dense (dense + merge)", stage["dense_attn_merge"], ps["F_dense"], b_dm,
+                               measured)]
+    kernels[0]["executed_tflop"] = round(ps["sparse_pairs"] * 4.0 * D * (HQ // G) * 128 / 1e12, 4)
+    # the dense pass's MFMA work including the masked rows of its unit blocks
+    kernels[1]["executed_tflop"] = round(ps["dense_unit_blocks"] * 16 * 4.0 * D * (HQ // G) * 128 / 1e12, 4)
+    return ps, kernels
+
+
+def block_size_variants(torch, msa, pre, dec_in, ctx_lens, topk, reps, sizes=(64, 32)):
+    """The bench prefill and decode at the smaller block sizes the pages
+    ablate (same inputs, same k: a budget of k * B_k keys per query). Prefill
+    TFLOP/s counts the attended keys (F_main at that B_k); decode GB/s its
+    algorithmic bytes at that B_k."""
+    n = pre[0].shape[1]
+    res = {}
+    for bk in sizes:
+        p = msa.params(HQ, G, D, DI, bk, topk)
+        ws = torch.empty(msa.prefill_workspace_bytes(p, 1, n), dtype=torch.uint8, device=pre[0].device)
+        out = torch.empty_like(pre[0])
+        ms = _time_calls(torch, lambda: msa.prefill(*pre, topk=topk, block_size=bk, workspace=ws, out=out), reps)
+        st = []
+        for _ in range(3):
+            x = []
+            msa.prefill(*pre, topk=topk, block_size=bk, workspace=ws, out=out, stage_ms=x)
+            st.append(x)
+        stage = dict(zip(msa.PREFILL_STAGES, (float(v) for v in np.mean(np.array(st), axis=0))))
+        _, sel, _ = msa.prefill(*pre, topk=topk, block_size=bk, workspace=ws, out=out, want_sel=True)
+        ps, kernels = attention_rooflines(torch, sel[0], n, stage, bk=bk, topk=topk, measured=False)
+        del sel, ws, out
+        f = prefill_flops_full(n, topk=topk, bk=bk)
+        assert abs(ps["F_dense"] + ps["F_sparse"] - f) <= 1e-9 * f, "pair split does not cover F_main"
+        wsd = torch.empty(msa.decode_workspace_bytes(p, dec_in[0].shape[0], dec_in[2].shape[1]), dtype=torch.uint8,
+                          device=pre[0].device)
+        outd = torch.empty_like(dec_in[0])
+        dms = _time_calls(torch, lambda: msa.decode(*dec_in, topk=topk, block_size=bk, workspace=wsd, out=outd),
+                          reps)
+        db = decode_bytes(ctx_lens, topk, bk)
+        del wsd, outd
+        res[str(bk)] = {"prefill": {"ms": round(ms, 4), "F_main_tflop": round(f / 1e12, 4),
+                                    "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                                    "stage_ms": {k: round(v, 4) for k, v in stage.items()}, "kernels": kernels},
+                        "decode": {"ms": round(dms, 4), "bytes_gb": round(db / 1e9, 4),
+                                   "GB/s": round(db / (dms * 1e-3) / 1e9, 1)}}
+    return res
 
 
 # ---- rocprofv3 summaries -------------------------------------------------------
@@ -355,8 +419,8 @@ def main():
                     help="no GPU work: condense the rocprofv3 CSV output under DIR to text and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-serving", action="store_true",
-                    help="skip the chunked / variable-length prefill and KL-backward measurements (profiling runs "
-                         "use this so that per-kernel averages cover the headline workload only)")
+                    help="skip the chunked / variable-length prefill, KL-backward and B_k 64 / 32 measurements "
+                         "(profiling runs use this so that per-kernel averages cover the headline workload only)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
@@ -433,23 +497,15 @@ def main():
 
     # roofline of the two attention kernels from the actual selection
     _, sel, _ = msa.prefill(*pre, topk=TOPK, workspace=ws_p, out=out_p, want_sel=True)
-    ps = pair_stats(torch, sel[0], N_PREFILL)
+    ps, kernels = attention_rooflines(torch, sel[0], N_PREFILL, stage)
     del sel
     assert abs(ps["F_dense"] + ps["F_sparse"] - f_main) <= 1e-9 * f_main, "pair split does not cover F_main"
-    q_bytes = HQ // G * D * 2                     # one (query, group): 16 heads x 128 dims, bf16
-    part_bytes = q_bytes + HQ // G * 4            # normalised bf16 partial + fp32 lse per head
-    kv_block = 2 * BK * D * 2                     # K and V of one block of one group
-    b_kv = ps["sparse_pairs"] * (q_bytes + part_bytes) + ps["kv_sparse"] * kv_block
-    b_dm = (N_PREFILL * G * (2 * q_bytes + TOPK * 4) + ps["kv_dense"] * kv_block
-            + ps["sparse_pairs"] * part_bytes)
-    kernels = [kernel_roofline("k_attn_prefill (KV-outer)", stage["kv_outer_attn"], ps["F_sparse"], b_kv),
-               kernel_roofline("k_attn_dense (dense + merge)", stage["dense_attn_merge"], ps["F_dense"], b_dm)]
-    # the dense pass's MFMA work including the masked rows of its unit blocks
-    kernels[1]["executed_tflop"] = round(ps["dense_unit_blocks"] * 16 * 4.0 * D * (HQ // G) * BK / 1e12, 4)
     dom = max(kernels, key=lambda r: r["ms"])
 
     chunked, varlen = (None, None) if args.no_serving else serving_shapes(torch, msa, pre, TOPK, args.steps)
     kl = None if args.no_serving else kl_backward_measure(torch, msa, pre, TOPK, args.steps)
+    variants = (None if args.no_serving else
+                block_size_variants(torch, msa, pre, dec_in, dec.ctx_lens, TOPK, args.steps))
 
     res = {
         "metric": METRIC,
@@ -487,6 +543,7 @@ def main():
         "chunked_prefill": chunked,
         "varlen_prefill": varlen,
         "index_kl_backward": kl,
+        "block_size_variants": variants,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)

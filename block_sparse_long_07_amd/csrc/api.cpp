@@ -26,11 +26,16 @@ using namespace msa;
 
 constexpr int64_t kWindowMax = 65536;  // query rows per prefill window
 constexpr int kTileQ = 16;             // queries per KV-outer tile
-constexpr int64_t kMaxSeq = 1 << 20;   // LDS reverse-index masks cover <= 8192 blocks
+// longest sequence at B_k = 128: the reverse index keeps one 64-bit LDS mask
+// per block (<= 8192); shorter blocks scale it down (and bound the pooled
+// scores of a window, which grow with the number of blocks)
+constexpr int64_t kMaxSeq = 1 << 20;
 constexpr size_t kAlign = 256;
 
 struct Shape {
   int Hq, G, k;
+  int bk, bk_shift;  // B_k and log2 B_k
+  int64_t max_seq;   // longest supported sequence / context
   float scale_log2;
 };
 
@@ -40,13 +45,17 @@ msa_status check_params(const msa_params* p, Shape* s) {
       p->block_size <= 0 || p->topk <= 0)
     return MSA_ERR_INVALID_ARG;
   if (p->num_q_heads % p->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
-  if (p->head_dim != kHeadDim || p->index_dim != kIndexDim || p->block_size != kBlock ||
+  if (p->head_dim != kHeadDim || p->index_dim != kIndexDim ||
+      (p->block_size != 128 && p->block_size != 64 && p->block_size != 32) ||
       p->num_q_heads / p->num_kv_heads != kHpg || p->num_kv_heads > 8 || p->topk > kMaxTopk)
     return MSA_ERR_UNSUPPORTED;
   if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARG;
   s->Hq = p->num_q_heads;
   s->G = p->num_kv_heads;
   s->k = p->topk;
+  s->bk = p->block_size;
+  s->bk_shift = p->block_size == 128 ? 7 : p->block_size == 64 ? 6 : 5;
+  s->max_seq = kMaxSeq * p->block_size / kBlock;
   const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   s->scale_log2 = scale * 1.4426950408889634f;
   return MSA_OK;
@@ -68,11 +77,11 @@ int cu_count() {
   return cached[dev];
 }
 
-// entries of rows [a, b): G * sum_i min(k, floor(i/128) + 1)
-int64_t entries_in(int64_t a, int64_t b, int G, int k) {
+// entries of rows [a, b): G * sum_i min(k, floor(i/B_k) + 1)
+int64_t entries_in(int64_t a, int64_t b, int G, int k, int bk) {
   int64_t e = 0;
-  for (int64_t blk = a / kBlock; blk * kBlock < b; ++blk) {
-    const int64_t lo = std::max(a, blk * kBlock), hi = std::min(b, (blk + 1) * kBlock);
+  for (int64_t blk = a / bk; blk * bk < b; ++blk) {
+    const int64_t lo = std::max(a, blk * bk), hi = std::min(b, (blk + 1) * bk);
     e += (hi - lo) * std::min<int64_t>(k, blk + 1);
   }
   return e * G;
@@ -91,8 +100,8 @@ struct PrefillLayout {
 // n_ctx: positions of the longest context; max_rows: most query rows of one
 // sequence in the call.
 bool prefill_layout(const Shape& s, int64_t n_ctx, int64_t max_rows, PrefillLayout* L) {
-  if (n_ctx <= 0 || n_ctx > kMaxSeq || max_rows <= 0 || max_rows > n_ctx) return false;
-  L->nb = (int)cdiv(n_ctx, kBlock);
+  if (n_ctx <= 0 || n_ctx > s.max_seq || max_rows <= 0 || max_rows > n_ctx) return false;
+  L->nb = (int)cdiv(n_ctx, s.bk);
   L->nbs = (L->nb + 3) & ~3;
   L->W = std::min<int64_t>(cdiv(max_rows, kBlock) * kBlock, kWindowMax);
   L->nch = cdiv(L->W, 64);
@@ -135,7 +144,7 @@ struct KlLayout {
 };
 
 bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
-  if (N <= 0 || N > kMaxSeq) return false;
+  if (N <= 0 || N > kMaxSeq || s.bk != kBlock) return false;
   L->nb = (int)cdiv(N, kBlock);
   L->W = std::min<int64_t>(cdiv(N, kBlock) * kBlock, kWindowMax);
   L->nch = (int)cdiv(L->W, 64);
@@ -170,7 +179,7 @@ struct DecodeLayout {
 
 bool decode_layout(const Shape& s, int32_t B, int64_t max_ctx, DecodeLayout* L) {
   if (B <= 0 || max_ctx <= 0) return false;
-  L->nb = (int)cdiv(max_ctx, kBlock);
+  L->nb = (int)cdiv(max_ctx, s.bk);
   const size_t items = (size_t)B * s.G * s.k;
   size_t off = 0;
   L->sblk = off;     off += up((size_t)B * s.G * L->nb * sizeof(float));
@@ -246,22 +255,24 @@ void prefill_window(const Shape& s, const PrefillLayout& L, const SeqIO& io, int
   const int G = s.G, Hq = s.Hq, K = s.k;
   const int64_t n_ctx = io.q_start + io.q_len;
   const int64_t r0 = w0 - io.q_start;  // the window's first row among the call's rows
-  const int nbw = (int)((w0 + Wn - 1) / kBlock + 1);
+  const int nbw = (int)((w0 + Wn - 1) / s.bk + 1);
   const uint16_t* qw = io.q + r0 * Hq * kHeadDim;
   clk.mark();
   // 1. index scores for query blocks that have more than k-1 older blocks
+  // 128-row query blocks with a row whose own block is >= k
   LaunchIndexPrefill ia{io.q_idx + r0 * G * kIndexDim, io.k_idx, at<float>(workspace, L.sblk), w0, w0 + Wn,
-                        (int)std::max<int64_t>(K, w0 / kBlock), nbw, L.nbs, G};
+                        (int)std::max<int64_t>((int64_t)K * s.bk / kBlock, w0 / kBlock),
+                        (int)((w0 + Wn - 1) / kBlock + 1), L.nbs, G, s.bk};
   launch_index_prefill(ia, hs);
   clk.mark();
   // 2. top-k selection
   int32_t* selw = io.sel ? io.sel + r0 * K : at<int32_t>(workspace, L.sel);
   const int64_t gstride = io.sel ? io.sel_gstride : L.W * K;
-  LaunchSelect sa{at<float>(workspace, L.sblk), L.nbs, selw, gstride, K, Wn, G, K, w0, nullptr};
+  LaunchSelect sa{at<float>(workspace, L.sblk), L.nbs, selw, gstride, K, Wn, G, K, w0, nullptr, s.bk_shift};
   launch_select(sa, hs);
   clk.mark();
   // 3. reverse index and tile schedule
-  const int64_t e_w = entries_in(w0, w0 + Wn, G, K);
+  const int64_t e_w = entries_in(w0, w0 + Wn, G, K, s.bk);
   const int64_t tile_cap = cdiv(e_w, kTileQ) + (int64_t)G * nbw;
   const int nunits = (int)cdiv(Wn, 16);
   int32_t* dcnt = at<int32_t>(workspace, L.dense_cnt);
@@ -271,21 +282,22 @@ void prefill_window(const Shape& s, const PrefillLayout& L, const SeqIO& io, int
                at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
                at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
                at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist,
-               at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits, true};
+               at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits, true,
+               s.bk_shift};
   launch_csr_and_tiles(ca, hs);
   clk.mark();
   // 4. KV-outer attention over the pairs not shared by a whole unit
   LaunchAttnPrefill aa{qw, io.k, io.v, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
                        at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
                        at<float>(workspace, L.part_lse), n_ctx, G, nbw, K, s.scale_log2,
-                       (int)std::min<int64_t>(cu_count(), tile_cap)};
+                       (int)std::min<int64_t>(cu_count(), tile_cap), s.bk};
   launch_attn_prefill(aa, hs);
   clk.mark();
   // 5. query-stationary attention over the units' shared blocks + merge
   LaunchAttnDense da{qw, io.k, io.v, dcnt, dlist, at<int32_t>(workspace, L.dense_qmask),
                      at<int32_t>(workspace, L.dense_slots), at<uint16_t>(workspace, L.part_o),
                      at<float>(workspace, L.part_lse), io.out + r0 * Hq * kHeadDim,
-                     io.lse ? io.lse + r0 * Hq : nullptr, n_ctx, w0, (int)Wn, nunits, G, K, s.scale_log2};
+                     io.lse ? io.lse + r0 * Hq : nullptr, n_ctx, w0, (int)Wn, nunits, G, K, s.scale_log2, s.bk};
   launch_attn_dense(da, hs);
   clk.mark();
 }
@@ -313,7 +325,7 @@ msa_status run_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
   msa_status st = check_params(p, &s);
   if (st != MSA_OK) return st;
   if (batch <= 0 || seq_len <= 0) return MSA_ERR_INVALID_ARG;
-  if (seq_len > kMaxSeq) return MSA_ERR_UNSUPPORTED;
+  if (seq_len > s.max_seq) return MSA_ERR_UNSUPPORTED;
   for (const void* ptr : {q, k, v, q_idx, k_idx, (const void*)out})
     if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
   if ((sel_out && !aligned(sel_out, 4)) || (lse_out && !aligned(lse_out, 4))) return MSA_ERR_INVALID_ARG;
@@ -496,19 +508,20 @@ msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const
   clk.mark();
   int32_t* sel = sel_out ? sel_out : at<int32_t>(workspace, L.sel);
   LaunchIndexDecode ia{static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx_cache), ctx_lens,
-                       at<float>(workspace, L.sblk), max_ctx, L.nb, batch, s.G, s.k};
+                       at<float>(workspace, L.sblk), max_ctx, L.nb, batch, s.G, s.k, s.bk};
   launch_index_decode(ia, hs);
   clk.mark();
-  LaunchSelect sa{at<float>(workspace, L.sblk), L.nb, sel, s.k, (int64_t)s.G * s.k, batch, s.G, s.k, 0, ctx_lens};
+  LaunchSelect sa{at<float>(workspace, L.sblk), L.nb, sel, s.k, (int64_t)s.G * s.k, batch, s.G, s.k, 0, ctx_lens,
+                  s.bk_shift};
   launch_select(sa, hs);
   clk.mark();
   LaunchAttnDecode aa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                       static_cast<const uint16_t*>(v_cache), ctx_lens, sel, at<uint16_t>(workspace, L.part_o),
-                      at<float>(workspace, L.part_lse), max_ctx, batch, s.G, s.k, s.scale_log2};
+                      at<float>(workspace, L.part_lse), max_ctx, batch, s.G, s.k, s.scale_log2, s.bk};
   launch_attn_decode(aa, hs);
   clk.mark();
   LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse),
-                   static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, ctx_lens};
+                   static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, ctx_lens, s.bk_shift};
   launch_combine(cb, hs);
   clk.mark();
   return finish();
@@ -571,7 +584,7 @@ msa_status msa_index_kl_backward(const msa_params* p, int64_t seq_len, const voi
     const int64_t Wn = std::min(L.W, N - w0);
     const int nbw = (int)((w0 + Wn - 1) / kBlock + 1);
     const int32_t* selw = sel + w0 * K;
-    const int64_t e_w = entries_in(w0, w0 + Wn, G, K);
+    const int64_t e_w = entries_in(w0, w0 + Wn, G, K, kBlock);
     const int64_t chunk_cap = cdiv(e_w, kKlChunk) + (int64_t)G * nbw;
     // every selected pair, in chunks of up to kKlChunk queries per (group, block)
     LaunchCsr ca{selw, N * K, K, w0, (int)Wn, nbw, G,
@@ -579,7 +592,7 @@ msa_status msa_index_kl_backward(const msa_params* p, int64_t seq_len, const voi
                  at<int32_t>(workspace, L.bsum), at<int32_t>(workspace, L.entries),
                  at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.chunks),
                  at<int32_t>(workspace, L.chunk_info), kKlChunk, chunk_cap, nullptr, nullptr, nullptr, nullptr,
-                 (int)cdiv(Wn, 16), false};
+                 (int)cdiv(Wn, 16), false, 7};
     launch_csr_and_tiles(ca, hs);
     LaunchKl ka{static_cast<const uint16_t*>(q) + w0 * Hq * kHeadDim, static_cast<const uint16_t*>(k),
                 static_cast<const uint16_t*>(q_idx) + w0 * G * kIndexDim, static_cast<const uint16_t*>(k_idx),
@@ -600,13 +613,14 @@ msa_status msa_index_scores(const msa_params* p, int64_t seq_len, const void* q_
   msa_status st = check_params(p, &s);
   if (st != MSA_OK) return st;
   if (seq_len <= 0) return MSA_ERR_INVALID_ARG;
-  if (seq_len > kMaxSeq) return MSA_ERR_UNSUPPORTED;
+  if (seq_len > s.max_seq) return MSA_ERR_UNSUPPORTED;
   if (!q_idx || !k_idx || !scores || !aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 4))
     return MSA_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  const int nb = (int)cdiv(seq_len, kBlock);
+  const int nb = (int)cdiv(seq_len, s.bk);
+  // 128-row query blocks holding a row whose own block is >= k
   LaunchIndexPrefill ia{static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), scores, 0,
-                        seq_len, s.k, nb, nb, s.G};
+                        seq_len, (int)((int64_t)s.k * s.bk / kBlock), (int)cdiv(seq_len, kBlock), nb, s.G, s.bk};
   launch_index_prefill(ia, static_cast<hipStream_t>(stream));
   return finish();
 }
@@ -619,8 +633,9 @@ msa_status msa_select_blocks(const msa_params* p, int64_t seq_len, const float* 
   if (seq_len <= 0) return MSA_ERR_INVALID_ARG;
   if (!scores || !sel_out || !aligned(scores, 4) || !aligned(sel_out, 4)) return MSA_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  const int nb = (int)cdiv(seq_len, kBlock);
-  LaunchSelect sa{scores, nb, sel_out, seq_len * s.k, s.k, seq_len, s.G, s.k, 0, nullptr};
+  if (seq_len > s.max_seq) return MSA_ERR_UNSUPPORTED;
+  const int nb = (int)cdiv(seq_len, s.bk);
+  LaunchSelect sa{scores, nb, sel_out, seq_len * s.k, s.k, seq_len, s.G, s.k, 0, nullptr, s.bk_shift};
   launch_select(sa, static_cast<hipStream_t>(stream));
   return finish();
 }

@@ -87,10 +87,10 @@ __device__ __forceinline__ StageOffsets stage_offsets(int64_t rstride, int wave)
   return {(uint32_t)(((int64_t)r * rstride + ck * 8) * 2), (uint32_t)(((int64_t)r * rstride + cv * 8) * 2)};
 }
 
-// Element offset of key block b, group g in a [tokens][G][128] K or V array,
-// from 32-bit uniform ints (blocks * 128 * G stays below 2^31).
-__device__ __forceinline__ uint64_t block_elems(int b, int G, int g) {
-  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(b * kBlock * G + g) * kHeadDim;
+// Element offset of key block b (of bk keys), group g in a [tokens][G][128] K
+// or V array, from 32-bit uniform ints (blocks * bk * G stays below 2^31).
+__device__ __forceinline__ uint64_t block_elems(int b, int bk, int G, int g) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(b * bk * G + g) * kHeadDim;
 }
 
 // Load i (0 .. 8*nwaves/4 - 1) of the fast path below: K (even i) or V (odd
@@ -567,6 +567,7 @@ constexpr int kAttnWaves = 8;
 // K/V of tile j+1 stream into the other LDS stage, the wave's entries of tile
 // j+1 and then their Q are loaded, and the descriptor of tile j+2 is read.
 // Tiles are claimed from the queue kClaim at a time, one chunk ahead.
+template <int BK>
 __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ tiles, int32_t* __restrict__ tile_info,
@@ -597,9 +598,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     return d;
   };
   auto stage_tile = [&](const Tile& d, lds_char* dst) {
-    const uint64_t e = block_elems(d.b, G, d.g);
-    stage_block(dst, k + e, v + e, rstride, (int)min<int64_t>(kBlock, n_tokens - (int64_t)d.b * kBlock), wave,
-                kAttnWaves, soff);
+    const uint64_t e = block_elems(d.b, BK, G, d.g);
+    stage_block(dst, k + e, v + e, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)d.b * BK), wave, kAttnWaves,
+                soff);
   };
   QueryGroup<kAttnQN> qg;
   auto fetch_q = [&](const int (&ent)[kAttnQN], int tg) {
@@ -661,9 +662,16 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     }
     if (e0 < cur.len) {
       // once the scores no longer need Q, the next tile's is loaded
-      attend_block<true, false>(qg, stage, k0, nullptr, scale_log2, 0u, [&](int i) {
+      auto hook = [&](int i) {
         if (i == 4 && next_work) fetch_q(nent, nxt.g);
-      });
+      };
+      if constexpr (BK == kBlock) {
+        attend_block<true, false>(qg, stage, k0, nullptr, scale_log2, 0u, hook);
+      } else {
+        // a block of BK < 128 keys in a 128-key stage: keys >= BK masked
+        const int lim[kAttnQN] = {BK - 1, BK - 1};
+        attend_block<true, true>(qg, stage, k0, lim, scale_log2, 0u, hook);
+      }
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
         if (e0 + n < cur.len) {
@@ -699,6 +707,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
 // every row's output and lse are written here, once, without atomics (the
 // second phase of the two-phase combine [pnsm, section 7]):
 //   out = o / l,   lse = (m*c + log2 l) * ln 2.
+template <int BK>
 __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ dense_cnt, const int32_t* __restrict__ dense_list,
@@ -716,7 +725,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   const StageOffsets soff = stage_offsets(rstride, wave);
   const int64_t list0 = ((int64_t)g * nunits + unit) * kDenseMax;
   const int i_rel0 = unit * 16 + wave * kAttnQN;
-  const int b_loc = (int)((row0 + unit * 16) / kBlock);
+  const int b_loc = (int)((row0 + unit * 16) / BK);
   const int nsel = min(topk, b_loc + 1);
 
   // independent loads first: the unit's list and the rows that selected each
@@ -733,8 +742,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   }
   {
     const int b0 = __builtin_amdgcn_readfirstlane(lane_blk);
-    const uint64_t e0 = block_elems(b0, G, g);
-    stage_block(lds, k + e0, v + e0, rstride, (int)min<int64_t>(kBlock, n_tokens - (int64_t)b0 * kBlock), wave,
+    const uint64_t e0 = block_elems(b0, BK, G, g);
+    stage_block(lds, k + e0, v + e0, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)b0 * BK), wave,
                 kAttnWaves, soff);
   }
   // slots of each query's selection computed KV-outer: the valid ones the
@@ -802,10 +811,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     // per SIMD): their partners start computing while they wait for room in
     // the memory queue
     const int b2 = __builtin_amdgcn_readlane(lane_blk, d + 1);
-    const uint64_t e2 = block_elems(b2, G, g);
+    const uint64_t e2 = block_elems(b2, BK, G, g);
     if (wave < 4)
       stage_block(lds + ((d + 1) & 1) * kStage, k + e2, v + e2, rstride,
-                  (int)min<int64_t>(kBlock, n_tokens - (int64_t)b2 * kBlock), wave, 4, soff);
+                  (int)min<int64_t>(BK, n_tokens - (int64_t)b2 * BK), wave, 4, soff);
     // merge the slot's partial, then refill the slot right away: the load has
     // the whole block's compute to arrive
     if (pend_n >= 0) {
@@ -819,8 +828,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     // with none that did skips it
     const unsigned skip =
         ~((unsigned)__builtin_amdgcn_readlane(lane_qm, d) >> (wave * kAttnQN)) & ((1u << kAttnQN) - 1u);
-    if (skip != (1u << kAttnQN) - 1u)
-      attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [](int) {});
+    if (skip != (1u << kAttnQN) - 1u) {
+      if constexpr (BK == kBlock) {
+        attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [](int) {});
+      } else {
+        const int lim[kAttnQN] = {BK - 1, BK - 1};  // keys >= BK of the stage masked
+        attend_block<false, true>(qg, lds + (d & 1) * kStage, k0, lim, scale_log2, skip, [](int) {});
+      }
+    }
   }
 
   // The remaining partials stream through two 8 KiB LDS regions of the wave
@@ -873,7 +888,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     issue_round(0, cA, nA0, nA1);
     int lim[kAttnQN];
 #pragma unroll
-    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * kBlock);
+    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * BK);
     attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [](int) {});
   }
   wait_lgkmcnt0();  // the last block's stage is free
@@ -913,6 +928,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
 
 // Decode: one workgroup per (sequence, group, selected slot). All four waves
 // stage the block; wave 0 computes the 16 heads.
+template <int BK>
 __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      const uint16_t* __restrict__ v,
@@ -928,17 +944,18 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   if (b < 0) return;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 15, qd = (tid >> 4) & 3;
   const int64_t i = ctx_lens[sq] - 1;
-  const int64_t key0 = (int64_t)b * kBlock;
+  const int64_t key0 = (int64_t)b * BK;
   const int Hq = G * kHpg;
   const int64_t base = ((int64_t)sq * max_ctx * G + key0 * G + g) * kHeadDim;
-  stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(kBlock, max_ctx - key0), wave, 4,
+  // only positions < ctx_len are read: later cache rows may hold anything
+  stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(BK, i + 1 - key0), wave, 4,
               stage_offsets((int64_t)G * kHeadDim, wave));
   QueryGroup<1> qg;
   if (wave == 0) load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
   wait_loads();
   __syncthreads();
   if (wave != 0) return;
-  int lim[1] = {((i >> 7) == b) ? (int)(i - key0) : kBlock};
+  int lim[1] = {(i / BK == b) ? (int)(i - key0) : BK - 1};
   KHalf k0;
   load_k_half(k0, lds);
   attend_block<true, true>(qg, lds, k0, lim, scale_log2, 0u, [](int) {});
@@ -946,23 +963,53 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
                 part_lse + (int64_t)item * kHpg);
 }
 
-void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_prefill, dim3(a.grid), dim3(512), 0, st, a.q, a.k, a.v, a.entries, a.tiles,
+template <int BK>
+static void launch_attn_prefill_bk(const LaunchAttnPrefill& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_attn_prefill<BK>, dim3(a.grid), dim3(512), 0, st, a.q, a.k, a.v, a.entries, a.tiles,
                      a.tile_info, a.part_o, a.part_lse, a.n_tokens, a.G, a.nbw, a.topk, a.scale_log2);
+}
+
+void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
+  switch (a.bk) {
+    case 128: launch_attn_prefill_bk<128>(a, st); break;
+    case 64: launch_attn_prefill_bk<64>(a, st); break;
+    case 32: launch_attn_prefill_bk<32>(a, st); break;
+    default: break;
+  }
+}
+
+template <int BK>
+static void launch_attn_dense_bk(const LaunchAttnDense& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_attn_dense<BK>, dim3(a.nunits, a.G), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v,
+                     a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.part_o, a.part_lse, a.out,
+                     a.lse_out, a.n_tokens, a.row0, a.nrows, a.nunits, a.G, a.topk, a.scale_log2);
 }
 
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {
   if (a.nunits <= 0) return;
-  hipLaunchKernelGGL(k_attn_dense, dim3(a.nunits, a.G), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v, a.dense_cnt, a.dense_list,
-                     a.dense_qmask, a.dense_slots, a.part_o, a.part_lse, a.out, a.lse_out, a.n_tokens, a.row0, a.nrows,
-                     a.nunits, a.G, a.topk, a.scale_log2);
+  switch (a.bk) {
+    case 128: launch_attn_dense_bk<128>(a, st); break;
+    case 64: launch_attn_dense_bk<64>(a, st); break;
+    case 32: launch_attn_dense_bk<32>(a, st); break;
+    default: break;
+  }
+}
+
+template <int BK>
+static void launch_attn_decode_bk(const LaunchAttnDecode& a, hipStream_t st, int items) {
+  hipLaunchKernelGGL(k_attn_decode<BK>, dim3(items), dim3(256), 0, st, a.q, a.k, a.v, a.ctx_lens, a.sel, a.part_o,
+                     a.part_lse, a.max_ctx, a.G, a.topk, a.scale_log2);
 }
 
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st) {
   const int items = a.batch * a.G * a.topk;
   if (items <= 0) return;
-  hipLaunchKernelGGL(k_attn_decode, dim3(items), dim3(256), 0, st, a.q, a.k, a.v, a.ctx_lens, a.sel, a.part_o,
-                     a.part_lse, a.max_ctx, a.G, a.topk, a.scale_log2);
+  switch (a.bk) {
+    case 128: launch_attn_decode_bk<128>(a, st, items); break;
+    case 64: launch_attn_decode_bk<64>(a, st, items); break;
+    case 32: launch_attn_decode_bk<32>(a, st, items); break;
+    default: break;
+  }
 }
 
 }  // namespace msa

@@ -18,13 +18,13 @@ namespace msa {
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o,
                                                  const float* __restrict__ part_lse, uint16_t* __restrict__ out,
                                                  float* __restrict__ lse_out, int G, int topk,
-                                                 const int32_t* __restrict__ ctx_lens) {
+                                                 const int32_t* __restrict__ ctx_lens, int bk_shift) {
   const int64_t rg = blockIdx.x;
   const int64_t rr = rg / G;
   const int g = (int)(rg % G);
   const int t = threadIdx.x, h = t >> 4, d0 = (t & 15) * 8;
   const int dt = d0 >> 4, qd = (d0 & 15) >> 2;
-  const int b_loc = (ctx_lens[rr] - 1) / kBlock;
+  const int b_loc = (ctx_lens[rr] - 1) >> bk_shift;
   const int nsel = min(topk, b_loc + 1);
   const int64_t slot0 = rg * topk;
 
@@ -67,7 +67,7 @@ void launch_combine(const LaunchCombine& a, hipStream_t st) {
   const int64_t n = a.nrows * a.G;
   if (n <= 0) return;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)n), dim3(256), 0, st, a.part_o, a.part_lse, a.out, a.lse_out, a.G,
-                     a.topk, a.ctx_lens);
+                     a.topk, a.ctx_lens, a.bk_shift);
 }
 
 }  // namespace msa

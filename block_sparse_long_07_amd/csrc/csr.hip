@@ -61,13 +61,14 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
                                                    int topk, int64_t row0, int nrows, int nbw, int nch,
                                                    int32_t* __restrict__ chunkcnt, int32_t* __restrict__ dense_cnt,
                                                    int32_t* __restrict__ dense_list, int32_t* __restrict__ dense_qmask,
-                                                   int32_t* __restrict__ dense_slots, int nunits, bool dense) {
+                                                   int32_t* __restrict__ dense_slots, int nunits, bool dense,
+                                                   int bk_shift) {
   extern __shared__ unsigned long long mask[];
   __shared__ int cand[kChunk / kUnit][kDenseMax];
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int i0 = chunk * kChunk;
   const int nq = min(kChunk, nrows - i0);
-  const int bmax = (int)((row0 + i0 + nq - 1) / kBlock);
+  const int bmax = (int)((row0 + i0 + nq - 1) >> bk_shift);
   chunk_masks(sel, sel_gstride, topk, g, i0, nq, bmax, mask);
   for (int b = threadIdx.x; b < nbw; b += blockDim.x) {
     int cnt = 0;
@@ -133,12 +134,12 @@ __global__ __launch_bounds__(256) void k_csr_count(const int32_t* __restrict__ s
 __global__ __launch_bounds__(256) void k_csr_scatter(const int32_t* __restrict__ sel, int64_t sel_gstride,
                                                      int topk, int64_t row0, int nrows, int nbw, int nch,
                                                      const int32_t* __restrict__ chunkoff,
-                                                     int32_t* __restrict__ entries, bool dense) {
+                                                     int32_t* __restrict__ entries, bool dense, int bk_shift) {
   extern __shared__ unsigned long long mask[];
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int i0 = chunk * kChunk;
   const int nq = min(kChunk, nrows - i0);
-  const int bmax = (int)((row0 + i0 + nq - 1) / kBlock);
+  const int bmax = (int)((row0 + i0 + nq - 1) >> bk_shift);
   chunk_masks(sel, sel_gstride, topk, g, i0, nq, bmax, mask);
   const int32_t* s = sel + (int64_t)g * sel_gstride + (int64_t)i0 * topk;
   for (int e = threadIdx.x; e < nq * topk; e += blockDim.x) {
@@ -301,14 +302,15 @@ void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st) {
   const size_t lds = (size_t)a.nbw * sizeof(unsigned long long);
   dim3 grid(nch, a.G);
   hipLaunchKernelGGL(k_csr_count, grid, dim3(256), lds, st, a.sel, a.sel_gstride, a.topk, a.row0, a.nrows,
-                     a.nbw, nch, a.chunkcnt, a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.nunits, a.dense);
+                     a.nbw, nch, a.chunkcnt, a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.nunits, a.dense,
+                     a.bk_shift);
   const int64_t n = (int64_t)a.G * a.nbw * nch;
   const int nblk = (int)((n + kScanTile - 1) / kScanTile);
   hipLaunchKernelGGL(k_scan_reduce, dim3(nblk), dim3(256), 0, st, a.chunkcnt, n, a.bsum);
   hipLaunchKernelGGL(k_scan_bsums, dim3(1), dim3(1024), 0, st, a.bsum, nblk);
   hipLaunchKernelGGL(k_scan_final, dim3(nblk), dim3(256), 0, st, a.chunkcnt, n, a.bsum, a.chunkoff);
   hipLaunchKernelGGL(k_csr_scatter, grid, dim3(256), lds, st, a.sel, a.sel_gstride, a.topk, a.row0, a.nrows,
-                     a.nbw, nch, a.chunkoff, a.entries, a.dense);
+                     a.nbw, nch, a.chunkoff, a.entries, a.dense, a.bk_shift);
   const int L = a.G * a.nbw;
   hipLaunchKernelGGL(k_tiles_count, dim3(1), dim3(1024), 0, st, a.chunkoff, nch, L, a.tile_q, a.tile_start,
                      a.tile_info);

@@ -28,7 +28,9 @@ constexpr int kKC = 8;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-__device__ __forceinline__ void stage_kidx(lds_char* dst, const uint16_t* src_rows, int wave) {
+// Stages key rows 0..127 of a 128-key stage; rows >= nvalid repeat row
+// nvalid-1 (they only feed blocks no query row reads).
+__device__ __forceinline__ void stage_kidx(lds_char* dst, const uint16_t* src_rows, int wave, int nvalid) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -36,26 +38,35 @@ __device__ __forceinline__ void stage_kidx(lds_char* dst, const uint16_t* src_ro
     const int slot = s0 + lane;
     const int r = slot >> 3, p = slot & 7;
     const int x = p ^ ((r >> 1) & 7);
-    lds_dma16(src_rows + r * kIndexDim + x * 8, dst + s0 * 16);
+    lds_dma16(src_rows + min(r, nvalid - 1) * kIndexDim + x * 8, dst + s0 * 16);
   }
 }
 
-template <int G>
+// SUB = 128 / B_k blocks per 128-key stage (1, 2 or 4): each stage yields SUB
+// pooled scores per row, from its key tiles s*8/SUB .. (s+1)*8/SUB - 1. With
+// SUB > 1 a query block's own stage also holds blocks older than some of its
+// rows, so it is scored too; every row writes only its blocks b < b_loc.
+template <int G, int SUB>
 __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __restrict__ q_idx,
                                                           const uint16_t* __restrict__ k_idx,
                                                           float* __restrict__ sblk, int64_t row0,
                                                           int64_t row_end, int qb_begin, int nb) {
-  constexpr int RT = 2 * G;  // 16-row tiles per wave
+  constexpr int RT = 2 * G;        // 16-row tiles per wave
+  constexpr int NS = kKC / SUB;    // stages per chunk: the chunk yields kKC blocks
+  constexpr int TPB = 8 / SUB;     // key tiles per block
+  constexpr int BKS = kBlock / SUB;
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * 16384];
   lds_char* lds = (lds_char*)lds_raw;
   const int qb = qb_begin + (int)blockIdx.y;
-  const int kb0 = (int)blockIdx.x * kKC;
-  if (kb0 >= qb) return;
-  const int kb1 = min(kb0 + kKC, qb);
+  const int last = SUB > 1 ? qb : qb - 1;  // last stage holding a block older than some row
+  const int kb0 = (int)blockIdx.x * NS;
+  if (kb0 > last) return;
+  const int kb1 = min(kb0 + NS, last + 1);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, qd = lane >> 4;
+  auto stage_rows = [&](int kb) { return (int)min<int64_t>(kBlock, row_end - (int64_t)kb * kBlock); };
 
-  stage_kidx(lds, k_idx + (int64_t)kb0 * kBlock * kIndexDim, wave);
+  stage_kidx(lds, k_idx + (int64_t)kb0 * kBlock * kIndexDim, wave, stage_rows(kb0));
 
   // flat index row (i*G + g) of this wave's first row; the window's rows are
   // [row0, row_end) (a query block can start before or end after them)
@@ -74,27 +85,29 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
   }
 
   // pooled scores of the chunk: lane group qd keeps the rows of tiles rt = qd
-  // (mod 4), eight blocks each, and writes them as one 32-byte run per row
+  // (mod 4), kKC blocks each, and writes them as one 32-byte run per row
   float res[(RT + 3) / 4][kKC];
 #pragma unroll
   for (int j = 0; j < (RT + 3) / 4; ++j)
 #pragma unroll
     for (int x = 0; x < kKC; ++x) res[j][x] = -__builtin_inff();
 
-  // fully unrolled over the chunk's blocks, so every pooled maximum lands in
-  // a fixed register (the block position x is a constant)
+  // fully unrolled over the chunk's stages, so every pooled maximum lands in
+  // a fixed register (the block position is a constant)
 #pragma unroll
-  for (int x = 0; x < kKC; ++x) {
+  for (int x = 0; x < NS; ++x) {
     const int kb = kb0 + x;
     if (kb >= kb1) break;
     wait_vmcnt0();
-    __syncthreads();  // block kb staged; the other stage is free
+    __syncthreads();  // stage kb staged; the other buffer is free
     if (kb + 1 < kb1)
-      stage_kidx(lds + ((x + 1) & 1) * 16384, k_idx + (int64_t)(kb + 1) * kBlock * kIndexDim, wave);
+      stage_kidx(lds + ((x + 1) & 1) * 16384, k_idx + (int64_t)(kb + 1) * kBlock * kIndexDim, wave,
+                 stage_rows(kb + 1));
     const lds_char* st = lds + (x & 1) * 16384;
-    float mx[RT];
+    float mx[SUB][RT];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
+      const int sb = t / TPB;
       const int r = 16 * t + c;
       const int sw = (c >> 1) & 7;
       const u32x4 v0 = *(const lds_u32x4*)(st + r * 128 + ((qd ^ sw) << 4));
@@ -105,36 +118,42 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mfma16x16x32(a0, qop[rt][0], acc);
         acc = mfma16x16x32(a1, qop[rt][1], acc);
-        float m = t == 0 ? fmaxf(acc[0], acc[1]) : fmaxf(fmaxf(mx[rt], acc[0]), acc[1]);
-        mx[rt] = fmaxf(fmaxf(m, acc[2]), acc[3]);
+        float m = t % TPB == 0 ? fmaxf(acc[0], acc[1]) : fmaxf(fmaxf(mx[sb][rt], acc[0]), acc[1]);
+        mx[sb][rt] = fmaxf(fmaxf(m, acc[2]), acc[3]);
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) mx[rt] = max_lane_groups(mx[rt]);
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) mx[sb][rt] = max_lane_groups(mx[sb][rt]);
     // all four lane groups now hold the block maxima; group qd keeps tiles rt = qd mod 4
 #pragma unroll
-    for (int j = 0; j < (RT + 3) / 4; ++j) {
-      float v = mx[4 * j];
+    for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int u = 1; u < 4; ++u)
-        if (4 * j + u < RT) v = qd == u ? mx[4 * j + u] : v;
-      res[j][x] = v;
-    }
+      for (int j = 0; j < (RT + 3) / 4; ++j) {
+        float v = mx[sb][4 * j];
+#pragma unroll
+        for (int u = 1; u < 4; ++u)
+          if (4 * j + u < RT) v = qd == u ? mx[sb][4 * j + u] : v;
+        res[j][x * SUB + sb] = v;
+      }
   }
-  const int nkb = kb1 - kb0;
+  const int nkb = (kb1 - kb0) * SUB;  // blocks of the chunk
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t row = flat0 + rt * 16 + c;
     if ((rt & 3) != qd || row < flat_lo || row >= flat_end) continue;
-    float* dst = sblk + (row - flat_lo) * nb + kb0;
+    // blocks the row reads: b < b_loc
+    const int nout = SUB == 1 ? nkb : max(0, min(nkb, (int)((row / G) / BKS) - kb0 * SUB));
+    float* dst = sblk + (row - flat_lo) * nb + kb0 * SUB;
     const float* rv = res[rt >> 2];
-    if (nkb == kKC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+    if (nout == kKC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
       *reinterpret_cast<f32x4*>(dst) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
       *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){rv[4], rv[5], rv[6], rv[7]};
     } else {
 #pragma unroll
       for (int xx = 0; xx < kKC; ++xx)
-        if (xx < nkb) dst[xx] = rv[xx];
+        if (xx < nout) dst[xx] = rv[xx];
     }
   }
 }
@@ -145,19 +164,22 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
 // line); lanes c < G of the MFMA column dimension carry the G index query heads.
 constexpr int kDecKB = 8;
 
-template <int G>
+template <int G, int SUB>
 __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict__ q_idx,
                                                       const uint16_t* __restrict__ k_idx,
                                                       const int32_t* __restrict__ ctx_lens,
                                                       float* __restrict__ sblk, int64_t max_ctx,
                                                       int nb, int topk) {
+  constexpr int TPB = 8 / SUB;  // key tiles per block
+  constexpr int BKS = kBlock / SUB;
   const int sq = (int)blockIdx.y;
   const int L = ctx_lens[sq];
-  const int b_loc = (L - 1) / kBlock;
+  const int b_loc = (L - 1) / BKS;
   if (b_loc < topk) return;  // every older block is selected; no scores needed
   const int kb0 = (int)blockIdx.x * kDecKB;
-  if (kb0 >= b_loc) return;
-  const int kb1 = min(kb0 + kDecKB, b_loc);
+  const int nst = (b_loc + SUB - 1) / SUB;  // 128-key stages holding an older block
+  if (kb0 >= nst) return;
+  const int kb1 = min(kb0 + kDecKB, nst);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, qd = lane >> 4;
 
@@ -170,7 +192,7 @@ __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict
   }
   const uint16_t* kbase = k_idx + (int64_t)sq * max_ctx * kIndexDim;
 
-  // two key blocks per iteration: all 32 loads are issued before the first MFMA
+  // two stages per iteration: all 32 loads are issued before the first MFMA
   for (int kb = kb0 + wave; kb < kb1; kb += 8) {
     const int kb2 = kb + 4;
     const bool two = kb2 < kb1;
@@ -180,70 +202,102 @@ __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict
       const int blk = h ? (two ? kb2 : kb) : kb;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint16_t* krow = kbase + ((int64_t)blk * kBlock + 16 * t + c) * kIndexDim + 8 * qd;
+        // rows past the context feed only blocks >= b_loc (SUB > 1)
+        const int64_t key = min<int64_t>((int64_t)blk * kBlock + 16 * t + c, L - 1);
+        const uint16_t* krow = kbase + key * kIndexDim + 8 * qd;
         a[h][t][0] = ld16(krow);
         a[h][t][1] = ld16(krow + 32);
       }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float mx = -__builtin_inff();
+      float mx[SUB];
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) mx[sb] = -__builtin_inff();
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mfma16x16x32(as_bf16x8(a[h][t][0]), qop[0], acc);
         acc = mfma16x16x32(as_bf16x8(a[h][t][1]), qop[1], acc);
-        mx = fmaxf(mx, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        mx[t / TPB] = fmaxf(mx[t / TPB], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
       }
-      mx = max_lane_groups(mx);
       const int blk = h ? kb2 : kb;
-      if (qd == 0 && c < G && (h == 0 || two)) sblk[((int64_t)sq * G + c) * nb + blk] = mx;
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        const float m = max_lane_groups(mx[sb]);
+        const int b = blk * SUB + sb;
+        if (qd == 0 && c < G && (h == 0 || two) && b < b_loc) sblk[((int64_t)sq * G + c) * nb + b] = m;
+      }
     }
   }
 }
 
-template <int G>
+template <int G, int SUB>
 static void launch_prefill_g(const LaunchIndexPrefill& a, hipStream_t st) {
   const int n_qb = a.qb_end - a.qb_begin;
   if (n_qb <= 0) return;
-  const int chunks = (a.qb_end - 1 + kKC - 1) / kKC;
+  constexpr int NS = kKC / SUB;
+  const int stages = SUB > 1 ? a.qb_end : a.qb_end - 1;  // stages of the last query block
+  const int chunks = (stages + NS - 1) / NS;
+  if (chunks <= 0) return;
   dim3 grid(chunks, n_qb);
-  hipLaunchKernelGGL(k_index_prefill<G>, grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.sblk, a.row0, a.row_end,
-                     a.qb_begin, a.nb);
+  hipLaunchKernelGGL((k_index_prefill<G, SUB>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.sblk, a.row0,
+                     a.row_end, a.qb_begin, a.nb);
 }
 
-void launch_index_prefill(const LaunchIndexPrefill& a, hipStream_t st) {
+template <int SUB>
+static void launch_prefill_sub(const LaunchIndexPrefill& a, hipStream_t st) {
   switch (a.G) {
-    case 1: launch_prefill_g<1>(a, st); break;
-    case 2: launch_prefill_g<2>(a, st); break;
-    case 3: launch_prefill_g<3>(a, st); break;
-    case 4: launch_prefill_g<4>(a, st); break;
-    case 5: launch_prefill_g<5>(a, st); break;
-    case 6: launch_prefill_g<6>(a, st); break;
-    case 7: launch_prefill_g<7>(a, st); break;
-    case 8: launch_prefill_g<8>(a, st); break;
+    case 1: launch_prefill_g<1, SUB>(a, st); break;
+    case 2: launch_prefill_g<2, SUB>(a, st); break;
+    case 3: launch_prefill_g<3, SUB>(a, st); break;
+    case 4: launch_prefill_g<4, SUB>(a, st); break;
+    case 5: launch_prefill_g<5, SUB>(a, st); break;
+    case 6: launch_prefill_g<6, SUB>(a, st); break;
+    case 7: launch_prefill_g<7, SUB>(a, st); break;
+    case 8: launch_prefill_g<8, SUB>(a, st); break;
     default: break;
   }
 }
 
-template <int G>
+void launch_index_prefill(const LaunchIndexPrefill& a, hipStream_t st) {
+  switch (a.bk) {
+    case 128: launch_prefill_sub<1>(a, st); break;
+    case 64: launch_prefill_sub<2>(a, st); break;
+    case 32: launch_prefill_sub<4>(a, st); break;
+    default: break;
+  }
+}
+
+template <int G, int SUB>
 static void launch_decode_g(const LaunchIndexDecode& a, hipStream_t st) {
-  const int chunks = (a.nb + kDecKB - 1) / kDecKB;
+  const int stages = (int)((a.max_ctx + kBlock - 1) / kBlock);
+  const int chunks = (stages + kDecKB - 1) / kDecKB;
   dim3 grid(chunks, a.batch);
-  hipLaunchKernelGGL(k_index_decode<G>, grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.ctx_lens, a.sblk,
+  hipLaunchKernelGGL((k_index_decode<G, SUB>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.ctx_lens, a.sblk,
                      a.max_ctx, a.nb, a.topk);
 }
 
-void launch_index_decode(const LaunchIndexDecode& a, hipStream_t st) {
+template <int SUB>
+static void launch_decode_sub(const LaunchIndexDecode& a, hipStream_t st) {
   switch (a.G) {
-    case 1: launch_decode_g<1>(a, st); break;
-    case 2: launch_decode_g<2>(a, st); break;
-    case 3: launch_decode_g<3>(a, st); break;
-    case 4: launch_decode_g<4>(a, st); break;
-    case 5: launch_decode_g<5>(a, st); break;
-    case 6: launch_decode_g<6>(a, st); break;
-    case 7: launch_decode_g<7>(a, st); break;
-    case 8: launch_decode_g<8>(a, st); break;
+    case 1: launch_decode_g<1, SUB>(a, st); break;
+    case 2: launch_decode_g<2, SUB>(a, st); break;
+    case 3: launch_decode_g<3, SUB>(a, st); break;
+    case 4: launch_decode_g<4, SUB>(a, st); break;
+    case 5: launch_decode_g<5, SUB>(a, st); break;
+    case 6: launch_decode_g<6, SUB>(a, st); break;
+    case 7: launch_decode_g<7, SUB>(a, st); break;
+    case 8: launch_decode_g<8, SUB>(a, st); break;
+    default: break;
+  }
+}
+
+void launch_index_decode(const LaunchIndexDecode& a, hipStream_t st) {
+  switch (a.bk) {
+    case 128: launch_decode_sub<1>(a, st); break;
+    case 64: launch_decode_sub<2>(a, st); break;
+    case 32: launch_decode_sub<4>(a, st); break;
     default: break;
   }
 }

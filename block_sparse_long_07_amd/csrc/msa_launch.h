@@ -25,9 +25,10 @@ struct LaunchIndexPrefill {
   const uint16_t* k_idx;  // [position][64]
   float* sblk;            // rows (i - row0)*G + g, row stride nb
   int64_t row0, row_end;  // the window's rows [row0, row_end)
-  int qb_begin, qb_end;   // query blocks scored: [qb_begin, qb_end)
+  int qb_begin, qb_end;   // 128-row query blocks scored: [qb_begin, qb_end)
   int nb;                 // row stride of sblk
   int G;
+  int bk;                 // B_k: 128, 64 or 32 (pooled scores per B_k keys)
 };
 void launch_index_prefill(const LaunchIndexPrefill& a, hipStream_t st);
 
@@ -38,6 +39,7 @@ struct LaunchIndexDecode {
   float* sblk;            // [(s*G + g)*nb + b]
   int64_t max_ctx;
   int nb, batch, G, topk;
+  int bk;                 // B_k: 128, 64 or 32
 };
 void launch_index_decode(const LaunchIndexDecode& a, hipStream_t st);
 
@@ -52,6 +54,7 @@ struct LaunchSelect {
   int G, topk;
   int64_t row0;
   const int32_t* ctx_lens;
+  int bk_shift;           // log2 B_k
 };
 void launch_select(const LaunchSelect& a, hipStream_t st);
 
@@ -80,6 +83,7 @@ struct LaunchCsr {
   int32_t* dense_slots;   // [G][nrows]: bit u = slot u of the row is computed in the dense pass
   int nunits;             // ceil(nrows / 16)
   bool dense;             // split off the dense pass's pairs (else list every pair; dense_* unused)
+  int bk_shift;           // log2 B_k
 };
 void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st);
 
@@ -96,6 +100,7 @@ struct LaunchAttnPrefill {
   int G, nbw, topk;
   float scale_log2;
   int grid;               // persistent workgroups
+  int bk;                 // B_k: 128, 64 or 32
 };
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st);
 
@@ -114,6 +119,7 @@ struct LaunchAttnDense {
   int64_t n_tokens, row0;
   int nrows, nunits, G, topk;
   float scale_log2;
+  int bk;
 };
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st);
 
@@ -128,6 +134,7 @@ struct LaunchAttnDecode {
   int64_t max_ctx;
   int batch, G, topk;
   float scale_log2;
+  int bk;
 };
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st);
 
@@ -169,6 +176,7 @@ struct LaunchCombine {   // decode
   int64_t nrows;
   int G, topk;
   const int32_t* ctx_lens;
+  int bk_shift;            // log2 B_k
 };
 void launch_combine(const LaunchCombine& a, hipStream_t st);
 

@@ -64,14 +64,14 @@ template <int KM1>
 __global__ __launch_bounds__(256) void k_select(const float* __restrict__ sblk, int nb,
                                                 int32_t* __restrict__ sel, int64_t sel_gstride,
                                                 int64_t sel_rstride, int64_t nrows, int G, int64_t row0,
-                                                const int32_t* __restrict__ ctx_lens) {
+                                                const int32_t* __restrict__ ctx_lens, int bk_shift) {
   const int s = threadIdx.x & 15;
   const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   const bool valid = r < nrows * G;
   const int64_t rr = valid ? r / G : 0;
   const int g = valid ? (int)(r % G) : 0;
   int b_loc = 0;
-  if (valid) b_loc = ctx_lens ? (ctx_lens[rr] - 1) / kBlock : (int)((row0 + rr) / kBlock);
+  if (valid) b_loc = ctx_lens ? (ctx_lens[rr] - 1) >> bk_shift : (int)((row0 + rr) >> bk_shift);
   // candidates this row must rank (0 when every older block is taken anyway)
   const int need = (KM1 > 0 && valid && b_loc > KM1) ? b_loc : 0;
 
@@ -167,12 +167,12 @@ template <int KM1>
 __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sblk, int nb,
                                                     int32_t* __restrict__ sel, int64_t sel_gstride,
                                                     int64_t sel_rstride, int G, int64_t row0,
-                                                    const int32_t* __restrict__ ctx_lens) {
+                                                    const int32_t* __restrict__ ctx_lens, int bk_shift) {
   const int lane = threadIdx.x;
   const int64_t r = blockIdx.x;
   const int64_t rr = r / G;
   const int g = (int)(r % G);
-  const int b_loc = ctx_lens ? (ctx_lens[rr] - 1) / kBlock : (int)((row0 + rr) / kBlock);
+  const int b_loc = ctx_lens ? (ctx_lens[rr] - 1) >> bk_shift : (int)((row0 + rr) >> bk_shift);
   int32_t* out = sel + (int64_t)g * sel_gstride + rr * sel_rstride;
   if (b_loc <= KM1) {
     if (lane <= KM1) out[lane] = (lane <= b_loc) ? lane : -1;
@@ -254,10 +254,10 @@ void launch_select(const LaunchSelect& a, hipStream_t st) {
   case K:                                                                                               \
     if (per_wave)                                                                                       \
       hipLaunchKernelGGL(k_select_wave<K - 1>, grid, dim3(64), 0, st, a.sblk, a.nb, a.sel,              \
-                         a.sel_gstride, a.sel_rstride, a.G, a.row0, a.ctx_lens);                        \
+                         a.sel_gstride, a.sel_rstride, a.G, a.row0, a.ctx_lens, a.bk_shift);            \
     else                                                                                                \
       hipLaunchKernelGGL(k_select<K - 1>, grid, dim3(256), 0, st, a.sblk, a.nb, a.sel, a.sel_gstride,   \
-                         a.sel_rstride, a.nrows, a.G, a.row0, a.ctx_lens);                              \
+                         a.sel_rstride, a.nrows, a.G, a.row0, a.ctx_lens, a.bk_shift);                  \
     break;
   switch (a.topk) {
     MSA_SEL_CASE(1)

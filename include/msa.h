@@ -35,9 +35,13 @@
  *     launch (hipGetLastError); asynchronous device faults surface at the
  *     caller's next synchronisation.
  *   - Calls are reentrant; concurrent calls need distinct workspaces.
- *   - Supported shapes: head_dim 128, index_dim 64, block_size 128,
- *     num_q_heads / num_kv_heads == 16, 1 <= num_kv_heads <= 8, 1 <= topk <= 16.
- *     Anything else returns MSA_ERR_UNSUPPORTED.
+ *   - Supported shapes: head_dim 128, index_dim 64, block_size 128, 64 or 32
+ *     (the block sizes the pages ablate [pnsm, section 8: block-size ablation
+ *     in its evidence table]), num_q_heads / num_kv_heads == 16,
+ *     1 <= num_kv_heads <= 8, 1 <= topk <= 16. Sequences and contexts hold at
+ *     most 2^20 * block_size / 128 positions (2^20, 2^19, 2^18). The
+ *     KL-alignment backward takes block_size 128 only. Anything else returns
+ *     MSA_ERR_UNSUPPORTED.
  */
 #ifndef MSA_H
 #define MSA_H
@@ -62,7 +66,7 @@ typedef struct {
   int32_t num_kv_heads;  /* G: KV heads = GQA groups = index query heads (4) */
   int32_t head_dim;      /* d = 128 */
   int32_t index_dim;     /* d_idx = 64: width of q_idx / k_idx */
-  int32_t block_size;    /* B_k = 128 keys per selectable block [pnsm, section 2] */
+  int32_t block_size;    /* B_k keys per selectable block: 128 [pnsm, section 2], 64 or 32 */
   int32_t topk;          /* k blocks per (query, group), the forced local block included (16) */
   float softmax_scale;   /* main-branch logit scale; <= 0 selects 1/sqrt(head_dim) */
 } msa_params;
@@ -117,7 +121,8 @@ size_t msa_prefill_varlen_workspace_bytes(const msa_params* p, int64_t max_q_len
  *   sel_out  optional int32 [G, T, topk] (ascending, -1 padded)
  *   lse_out  optional fp32 [T, Hq]
  *   workspace  >= msa_prefill_varlen_workspace_bytes(p, max q_len, max_ctx) bytes
- * T = 0 returns MSA_OK at once. max_ctx above 2^20 is MSA_ERR_UNSUPPORTED. */
+ * T = 0 returns MSA_OK at once. max_ctx above the longest supported context
+ * (2^20 at block_size 128) is MSA_ERR_UNSUPPORTED. */
 msa_status msa_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ctx,
                               const int64_t* q_start, const int64_t* q_len,
                               const void* q, const void* q_idx,
@@ -137,7 +142,8 @@ size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t ma
  *   k_cache, v_cache  bf16 [batch, max_ctx, G, d]
  *   k_idx_cache  bf16 [batch, max_ctx, d_idx]
  *   ctx_lens     device int32 [batch], 1 <= ctx_lens[b] <= max_ctx (device values
- *                are not checked on the host; out-of-range values are undefined)
+ *                are not checked on the host; out-of-range values are undefined);
+ *                cache positions >= ctx_lens[b] are never read
  *   out          bf16 [batch, Hq, d]
  *   sel_out      optional int32 [batch, G, topk] (ascending, -1 padded)
  *   lse_out      optional fp32 [batch, Hq] */

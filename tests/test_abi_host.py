@@ -52,7 +52,8 @@ def test_workspace_sizes(lib):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("head_dim", 64, -2), ("index_dim", 32, -2), ("block_size", 64, -2), ("topk", 17, -2),
+    ("head_dim", 64, -2), ("index_dim", 32, -2), ("block_size", 96, -2), ("block_size", 256, -2),
+    ("block_size", 16, -2), ("topk", 17, -2),
     ("topk", 0, -1), ("num_kv_heads", 3, -1), ("num_q_heads", 32, -2), ("num_kv_heads", 0, -1),
 ])
 def test_prefill_rejects_bad_params(lib, field, value, status):
@@ -97,8 +98,35 @@ def test_stage_entry_points_reject_bad_args(lib):
     assert lib.msa_index_scores(ctypes.byref(p), 0, ok, ok, ok, None) == -1
     assert lib.msa_index_scores(ctypes.byref(p), 256, None, ok, ok, None) == -1
     assert lib.msa_select_blocks(ctypes.byref(p), 256, ok, None, None) == -1
-    p.block_size = 64
+    p.block_size = 96
     assert lib.msa_select_blocks(ctypes.byref(p), 256, ok, ok, None) == -2
+
+
+@pytest.mark.parametrize("bk", [128, 64, 32])
+def test_block_size_limits(lib, bk):
+    """The longest sequence shrinks with B_k (the per-window block count is
+    what is bounded); the KL-alignment backward takes B_k = 128 only."""
+    p = msa.params(block_size=bk)
+    longest = (1 << 20) * bk // 128
+    assert msa.prefill_workspace_bytes(p, 1, longest) > 0
+    assert msa.prefill_workspace_bytes(p, 1, longest + 1) == 0
+    assert msa.prefill_varlen_workspace_bytes(p, 4096, longest) > 0
+    assert msa.prefill_varlen_workspace_bytes(p, 4096, longest + 1) == 0
+    ok = ctypes.c_void_p(1 << 20)
+    need = lib.msa_prefill_workspace_bytes(ctypes.byref(p), 1, 256)
+    assert lib.msa_prefill(ctypes.byref(p), 1, longest + 1, *[ok] * 6, None, None, ok, need, None) == -2
+    assert lib.msa_index_scores(ctypes.byref(p), longest + 1, ok, ok, ok, None) == -2
+    assert lib.msa_select_blocks(ctypes.byref(p), longest + 1, ok, ok, None) == -2
+    # decode: the workspace holds one pooled score per block of the longest context
+    d = msa.decode_workspace_bytes(p, 4, 8192)
+    assert d >= 4 * 4 * (8192 // bk) * 4
+    kl_need = lib.msa_index_kl_workspace_bytes(ctypes.byref(p), 4096)
+    if bk == 128:
+        assert kl_need > 0
+    else:
+        assert kl_need == 0
+        big = lib.msa_index_kl_workspace_bytes(ctypes.byref(msa.params()), 4096)
+        assert lib.msa_index_kl_backward(ctypes.byref(p), 4096, *[ok] * 9, ok, big, None) == -2
 
 
 def test_varlen_workspace_and_rejects_bad_args(lib):
