@@ -13,7 +13,8 @@ included). Decode KV GB/s (algorithmic bytes / whole decode call) is reported
 alongside, with per-stage times from the profiled entry points and the
 roofline of the dominant kernel. Side measurements (not part of a step):
 chunked and variable-length prefill, the Index Branch KL-alignment
-backward, and prefill / decode at B_k 64 and 32.
+backward, prefill / decode at B_k 64 and 32, and the Index Branch
+projections from hidden states.
 """
 from __future__ import annotations
 
@@ -231,6 +232,48 @@ def block_size_variants(torch, msa, pre, dec_in, ctx_lens, topk, reps, sizes=(64
     return res
 
 
+# The hidden size the index projections read: the pages give the head layout
+# (64 query heads of 128) but not the model width; this reading takes
+# d_model = 64 * 128.
+D_MODEL = 8192
+
+
+def projection_measure(torch, msa, n, batch, reps, d_model=D_MODEL):
+    """Index Branch projections (G index query heads + the shared key head,
+    one GEMM) for the n-token prefill and for one decode step of `batch`
+    sequences (key appended to each cache). Algorithmic work: 2 n d_model
+    64 (G+1) flops; bytes: x once, the weights once, the bf16 outputs once."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    cols = 64 * (G + 1)
+    x = torch.randn((n, d_model), generator=g, device=dev).to(torch.bfloat16)
+    wq = (torch.randn((G, DI, d_model), generator=g, device=dev) * d_model ** -0.5).to(torch.bfloat16)
+    wk = (torch.randn((DI, d_model), generator=g, device=dev) * d_model ** -0.5).to(torch.bfloat16)
+    qi = torch.empty((n, G, DI), dtype=torch.bfloat16, device=dev)
+    ki = torch.empty((n, DI), dtype=torch.bfloat16, device=dev)
+    p = msa.params(HQ, G, D, DI)
+    ws = torch.empty(max(msa.index_project_workspace_bytes(p, n, d_model),
+                         msa.index_project_workspace_bytes(p, batch, d_model)), dtype=torch.uint8, device=dev)
+    res = {"d_model": d_model}
+    ms = _time_calls(torch, lambda: msa.index_project(x, wq, wk, q_idx=qi, k_idx=ki, workspace=ws), reps)
+    fl = 2.0 * n * d_model * cols
+    nb = (n * d_model + cols * d_model + n * cols) * 2
+    t_mfma, t_hbm = fl / (MFMA_PEAK_TFLOPS * 1e12), nb / (HBM_PEAK_GBS * 1e9)
+    res["prefill"] = {"tokens": n, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                      "GB/s": round(nb / (ms * 1e-3) / 1e9, 1), "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                      "frac": round(max(t_mfma, t_hbm) / (ms * 1e-3), 4)}
+    cache = torch.zeros((batch, 4096, DI), dtype=torch.bfloat16, device=dev)
+    lens = torch.full((batch,), 4096, dtype=torch.int32, device=dev)
+    xd = x[:batch].contiguous()
+    qd = torch.empty((batch, G, DI), dtype=torch.bfloat16, device=dev)
+    ms = _time_calls(torch, lambda: msa.index_project_decode(xd, wq, wk, cache, lens, q_idx=qd, workspace=ws), reps)
+    fl = 2.0 * batch * d_model * cols
+    nb = (batch * d_model + cols * d_model + batch * cols) * 2
+    res["decode"] = {"batch": batch, "ms": round(ms, 4), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
+                     "frac": round(nb / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4)}
+    return res
+
+
 # ---- rocprofv3 summaries -------------------------------------------------------
 
 def summarize_rocprof(d):
@@ -419,7 +462,8 @@ def main():
                     help="no GPU work: condense the rocprofv3 CSV output under DIR to text and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-serving", action="store_true",
-                    help="skip the chunked / variable-length prefill, KL-backward and B_k 64 / 32 measurements "
+                    help="skip the chunked / variable-length prefill, KL-backward, B_k 64 / 32 and projection "
+                         "measurements "
                          "(profiling runs use this so that per-kernel averages cover the headline workload only)")
     args = ap.parse_args()
     if args.summarize_rocprof:
@@ -506,6 +550,7 @@ def main():
     kl = None if args.no_serving else kl_backward_measure(torch, msa, pre, TOPK, args.steps)
     variants = (None if args.no_serving else
                 block_size_variants(torch, msa, pre, dec_in, dec.ctx_lens, TOPK, args.steps))
+    proj = None if args.no_serving else projection_measure(torch, msa, N_PREFILL, DEC_B, args.steps)
 
     res = {
         "metric": METRIC,
@@ -544,6 +589,7 @@ def main():
         "varlen_prefill": varlen,
         "index_kl_backward": kl,
         "block_size_variants": variants,
+        "index_projection": proj,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)

@@ -23,7 +23,8 @@ _STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_UNSUPPORTED",
 EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_prefill_varlen_workspace_bytes",
             "msa_prefill_varlen", "msa_decode_workspace_bytes", "msa_decode", "msa_prefill_profiled",
             "msa_decode_profiled", "msa_index_kl_workspace_bytes", "msa_index_kl_backward", "msa_index_scores",
-            "msa_select_blocks", "msa_status_string")
+            "msa_select_blocks", "msa_status_string", "msa_index_project_workspace_bytes", "msa_index_project",
+            "msa_index_project_decode")
 PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
 DECODE_STAGES = ("index_score", "select", "attn", "combine")
 
@@ -80,6 +81,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_index_scores.restype = ctypes.c_int
     lib.msa_select_blocks.argtypes = [P, i64, vp, vp, vp]
     lib.msa_select_blocks.restype = ctypes.c_int
+    lib.msa_index_project_workspace_bytes.argtypes = [P, i64, i32]
+    lib.msa_index_project_workspace_bytes.restype = sz
+    lib.msa_index_project.argtypes = [P, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_index_project.restype = ctypes.c_int
+    lib.msa_index_project_decode.argtypes = [P, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_index_project_decode.restype = ctypes.c_int
     lib.msa_status_string.argtypes = [ctypes.c_int]
     lib.msa_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -273,6 +280,71 @@ def index_kl_backward(q, k, q_idx, k_idx, sel, lse, *, topk=16, block_size=128, 
                                      _ptr(lse), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(workspace), nbytes,
                                      _stream(dev)), "msa_index_kl_backward")
     return loss, dq, dk
+
+
+def index_project_workspace_bytes(p: MsaParams, n_tokens: int, d_model: int) -> int:
+    return int(load().msa_index_project_workspace_bytes(ctypes.byref(p), n_tokens, d_model))
+
+
+def _project_args(x, w_qi, w_ki):
+    for t, name in ((x, "x"), (w_qi, "w_qi"), (w_ki, "w_ki")):
+        _need(t, torch.bfloat16, name)
+    n, dm = x.shape
+    G, di, dm2 = w_qi.shape
+    if dm2 != dm or tuple(w_ki.shape) != (di, dm):
+        raise ValueError(f"weights {tuple(w_qi.shape)} / {tuple(w_ki.shape)} do not match x {tuple(x.shape)}")
+    return n, dm, G, di, params(16 * G, G, 128, di)
+
+
+def _project_workspace(lib, p, n, dm, workspace, dev, what):
+    nbytes = int(lib.msa_index_project_workspace_bytes(ctypes.byref(p), n, dm))
+    if nbytes == 0:
+        raise MsaError(-2, what)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return workspace, nbytes
+
+
+def index_project(x, w_qi, w_ki, *, q_idx=None, k_idx=None, workspace: Optional[torch.Tensor] = None):
+    """Index Branch projections of hidden states x [n, d_model] (bf16):
+    q_idx [n, G, d_idx] = x W_qi[g]^T per group, k_idx [n, d_idx] = x W_ki^T,
+    with w_qi [G, d_idx, d_model] and w_ki [d_idx, d_model]. k_idx may be a
+    contiguous slice of a cache (the chunk's rows); both are written."""
+    lib = load()
+    n, dm, G, di, p = _project_args(x, w_qi, w_ki)
+    dev = x.device
+    if q_idx is None:
+        q_idx = torch.empty((n, G, di), dtype=torch.bfloat16, device=dev)
+    if k_idx is None:
+        k_idx = torch.empty((n, di), dtype=torch.bfloat16, device=dev)
+    _need(q_idx, torch.bfloat16, "q_idx")
+    _need(k_idx, torch.bfloat16, "k_idx")
+    workspace, nbytes = _project_workspace(lib, p, n, dm, workspace, dev, "msa_index_project_workspace_bytes")
+    _check(lib.msa_index_project(ctypes.byref(p), n, dm, _ptr(x), _ptr(w_qi), _ptr(w_ki), _ptr(q_idx), _ptr(k_idx),
+                                 _ptr(workspace), nbytes, _stream(dev)), "msa_index_project")
+    return q_idx, k_idx
+
+
+def index_project_decode(x, w_qi, w_ki, k_idx_cache, ctx_lens, *, q_idx=None,
+                         workspace: Optional[torch.Tensor] = None):
+    """Decode-step projections: x [B, d_model] -> q_idx [B, G, d_idx]
+    (returned), and the key head appended in place at row ctx_lens[b]-1 of
+    k_idx_cache [B, max_ctx, d_idx]."""
+    lib = load()
+    B, dm, G, di, p = _project_args(x, w_qi, w_ki)
+    dev = x.device
+    _need(k_idx_cache, torch.bfloat16, "k_idx_cache")
+    _need(ctx_lens, torch.int32, "ctx_lens")
+    if k_idx_cache.dim() != 3 or k_idx_cache.shape[0] != B or k_idx_cache.shape[2] != di or ctx_lens.numel() != B:
+        raise ValueError("k_idx_cache must be [B, max_ctx, d_idx] and ctx_lens [B]")
+    if q_idx is None:
+        q_idx = torch.empty((B, G, di), dtype=torch.bfloat16, device=dev)
+    _need(q_idx, torch.bfloat16, "q_idx")
+    workspace, nbytes = _project_workspace(lib, p, B, dm, workspace, dev, "msa_index_project_workspace_bytes")
+    _check(lib.msa_index_project_decode(ctypes.byref(p), B, k_idx_cache.shape[1], dm, _ptr(x), _ptr(w_qi),
+                                        _ptr(w_ki), _ptr(ctx_lens), _ptr(q_idx), _ptr(k_idx_cache),
+                                        _ptr(workspace), nbytes, _stream(dev)), "msa_index_project_decode")
+    return q_idx
 
 
 def index_scores(q_idx, k_idx, *, num_q_heads=None, topk=16, block_size=128, scores=None):

@@ -197,6 +197,33 @@ T* at(void* base, size_t off) {
 
 msa_status finish() { return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
+// d_model: whole 64-wide slices; tokens bounded so every index stays well
+// inside int64 and the grid inside its limits
+bool project_args_ok(int64_t n_tokens, int32_t d_model) {
+  return n_tokens > 0 && n_tokens <= (int64_t)1 << 28 && d_model >= 64 && d_model <= 65536 && d_model % 64 == 0;
+}
+
+msa_status run_index_project(const msa_params* p, int64_t n_tokens, int32_t d_model, const void* x,
+                             const void* w_qi, const void* w_ki, const int32_t* ctx_lens, int64_t max_ctx,
+                             void* q_idx, void* k_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  if (!project_args_ok(n_tokens, d_model)) return n_tokens > 0 && d_model > 0 ? MSA_ERR_UNSUPPORTED
+                                                                                : MSA_ERR_INVALID_ARG;
+  for (const void* ptr : {x, w_qi, w_ki, (const void*)q_idx, (const void*)k_idx})
+    if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  const ProjectPlan pl = plan_index_project(n_tokens, d_model, s.G);
+  if (workspace_bytes < pl.part_floats * sizeof(float)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  (void)hipGetLastError();
+  LaunchProject a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_qi),
+                  static_cast<const uint16_t*>(w_ki), n_tokens, d_model, s.G, static_cast<uint16_t*>(q_idx),
+                  static_cast<uint16_t*>(k_idx), ctx_lens, max_ctx, static_cast<float*>(workspace)};
+  launch_index_project(a, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
 }  // namespace
 
 extern "C" {
@@ -605,6 +632,28 @@ msa_status msa_index_kl_backward(const msa_params* p, int64_t seq_len, const voi
     launch_kl_window(ka, hs);
   }
   return finish();
+}
+
+size_t msa_index_project_workspace_bytes(const msa_params* p, int64_t n_tokens, int32_t d_model) {
+  Shape s;
+  if (check_params(p, &s) != MSA_OK || !project_args_ok(n_tokens, d_model)) return 0;
+  return up(std::max<size_t>(1, plan_index_project(n_tokens, d_model, s.G).part_floats * sizeof(float)));
+}
+
+msa_status msa_index_project(const msa_params* p, int64_t n_tokens, int32_t d_model, const void* x,
+                             const void* w_qi, const void* w_ki, void* q_idx, void* k_idx, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return run_index_project(p, n_tokens, d_model, x, w_qi, w_ki, nullptr, 0, q_idx, k_idx, workspace,
+                           workspace_bytes, stream);
+}
+
+msa_status msa_index_project_decode(const msa_params* p, int32_t batch, int64_t max_ctx, int32_t d_model,
+                                    const void* x, const void* w_qi, const void* w_ki, const int32_t* ctx_lens,
+                                    void* q_idx, void* k_idx_cache, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (batch <= 0 || max_ctx <= 0 || !ctx_lens || !aligned(ctx_lens, 4)) return MSA_ERR_INVALID_ARG;
+  return run_index_project(p, batch, d_model, x, w_qi, w_ki, ctx_lens, max_ctx, q_idx, k_idx_cache, workspace,
+                           workspace_bytes, stream);
 }
 
 msa_status msa_index_scores(const msa_params* p, int64_t seq_len, const void* q_idx, const void* k_idx,

@@ -168,6 +168,28 @@ struct LaunchKl {
 void launch_kl_window(const LaunchKl& a, hipStream_t st);
 void launch_zero_f32(float* p, int64_t n, hipStream_t st);
 
+// Index Branch projections (one GEMM for the G query heads and the key head).
+struct LaunchProject {
+  const uint16_t* x;      // [n][d_model]
+  const uint16_t* w_qi;   // [G*64][d_model]
+  const uint16_t* w_ki;   // [64][d_model]
+  int64_t n;
+  int d_model, G;
+  uint16_t* q_idx;        // [n][G][64]
+  uint16_t* k_idx;        // key head rows: t, or t*max_ctx + ctx_lens[t]-1 when ctx_lens is set
+  const int32_t* ctx_lens;
+  int64_t max_ctx;
+  float* part;            // fp32 partials when d_model is split (plan.part_floats floats)
+};
+struct ProjectPlan {
+  int parts, nc;          // column parts and 64-column units per workgroup
+  int64_t m_tiles;        // 128-token tiles
+  int splits, stages_per_split;
+  size_t part_floats;     // scratch for split partials (0: none)
+};
+ProjectPlan plan_index_project(int64_t n, int d_model, int G);
+void launch_index_project(const LaunchProject& a, hipStream_t st);
+
 struct LaunchCombine {   // decode
   const uint16_t* part_o;  // [(s*G + g)*topk + u][2048] bf16, fragment order
   const float* part_lse;

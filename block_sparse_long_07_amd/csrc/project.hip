@@ -1,0 +1,244 @@
+// Index Branch projections: the G index query heads (one per GQA group) and
+// the one shared index key head are linear maps of the hidden states
+// [yhxrc, 二: one scoring head per group plus one shared key head; yifor,
+// 工程實踐啟示: two added projection matrices]:
+//   q_idx[t, g, :] = W_qi[g] x[t],   k_idx[row(t), :] = W_ki x[t]
+// computed as one GEMM of x [n, d_model] against the stacked weights
+// [64 (G+1), d_model], so x is read once for both. The key head is written
+// straight into its cache row (row(t) = t, or ctx_lens[t]-1 of sequence t in
+// decode). fp32 accumulation; outputs rounded to bf16 (nearest even).
+//
+// Workgroup: 128 tokens x NC 64-column units (all G+1 units when G+1 <= 5,
+// else two parts), 8 waves as 2 (tokens) x 4 (columns); each wave holds
+// 4 x NC accumulator tiles of 16 x 16 (NC = 1 for few tokens: more
+// workgroups, each with one 64-column unit). d_model is consumed in 32-wide slices
+// staged in a ring of four LDS buffers (three slices in flight while one is
+// computed) by direct-to-LDS loads with an XOR swizzle
+// of the 16-byte chunks, so the MFMA operand reads are conflict-free. The
+// MFMA computes (W x^T) tiles: each lane ends with 4 consecutive output
+// columns of one token, stored as 8 bytes. Small batches (decode) split
+// d_model across workgroups; the fp32 partials are then summed in a fixed
+// order by a second kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+namespace {
+
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int kPRows = 128;  // tokens per workgroup
+constexpr int kPK = 32;      // d_model slice per stage (one MFMA k-step)
+constexpr int kRing = 4;     // LDS stages: three loads in flight behind the one computed
+constexpr int kXBytes = kPRows * kPK * 2;
+
+// Number of 64-slot load rounds of a wave for NROWS rows of 4 chunks.
+template <int NROWS>
+__device__ __forceinline__ int wave_loads(int wave) {
+  int n = 0;
+#pragma unroll
+  for (int it = 0; it < (NROWS * 4 + 511) / 512; ++it) n += (it * 512 + wave * 64 < NROWS * 4) ? 1 : 0;
+  return n;
+}
+
+// Stages 32-element slices of NROWS rows into LDS rows of 64 bytes; LDS chunk
+// p of row r holds global chunk p ^ ((r >> 1) & 3) (rows 0, 2, 4, 6 of a
+// 16-row operand read then fall in distinct banks). row_ptr(r) gives row r's
+// first element at the slice.
+template <int NROWS, typename RowPtr>
+__device__ __forceinline__ void stage_rows(lds_char* dst, RowPtr row_ptr, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int it = 0; it < (NROWS * 4 + 511) / 512; ++it) {
+    const int s0 = it * 512 + wave * 64;
+    if (s0 < NROWS * 4) {
+      const int slot = s0 + lane;
+      const int r = slot >> 2, p = slot & 3;
+      lds_dma16(row_ptr(r) + ((p ^ ((r >> 1) & 3)) << 3), dst + s0 * 16);
+    }
+  }
+}
+
+// MFMA operand of row r (LDS), k-chunk j (8 elements at 8j of the slice).
+__device__ __forceinline__ bf16x8 lds_chunk(const lds_char* base, int r, int j) {
+  const u32x4 v = *(const lds_u32x4*)(base + r * 64 + ((j ^ ((r >> 1) & 3)) << 4));
+  return as_bf16x8(v);
+}
+
+}  // namespace
+
+template <int NC>
+__global__ __launch_bounds__(512, 1) void k_index_project(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_qi, const uint16_t* __restrict__ w_ki,
+    int64_t n, int d_model, int G, int stages_per_split, uint16_t* __restrict__ q_idx,
+    uint16_t* __restrict__ k_idx, const int32_t* __restrict__ ctx_lens, int64_t max_ctx,
+    float* __restrict__ part) {
+  constexpr int kWRows = NC * 64;
+  constexpr int kStage = kXBytes + kWRows * 64;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kRing * kStage];
+  lds_char* lds = (lds_char*)lds_raw;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, qd = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t m0 = (int64_t)blockIdx.x * kPRows;
+  const int col0 = (int)blockIdx.y * kWRows;  // first stacked weight row of this part
+  const int ncols = 64 * (G + 1);
+  const int nk = d_model / kPK;
+  const int st0 = (int)blockIdx.z * stages_per_split;
+  const int st1 = min(nk, st0 + stages_per_split);
+
+  // rows past the tokens or past the stacked weights repeat a valid row; their
+  // results are never stored
+  auto x_row = [&](int r) { return x + min<int64_t>(m0 + r, n - 1) * d_model; };
+  auto w_row = [&](int r) {
+    const int gc = min(col0 + r, ncols - 1);
+    return gc < 64 * G ? w_qi + (int64_t)gc * d_model : w_ki + (int64_t)(gc - 64 * G) * d_model;
+  };
+  auto load_stage = [&](int st) {
+    lds_char* dst = lds + ((st - st0) % kRing) * kStage;
+    const int k0 = st * kPK;
+    stage_rows<kPRows>(dst, [&](int r) { return x_row(r) + k0; }, tid);
+    stage_rows<kWRows>(dst + kXBytes, [&](int r) { return w_row(r) + k0; }, tid);
+  };
+  const int per_stage = wave_loads<kPRows>(wave) + wave_loads<kWRows>(wave);  // this wave's loads per stage
+
+  f32x4 acc[4][NC];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) acc[rt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int st = st0; st < min(st1, st0 + kRing - 1); ++st) load_stage(st);
+  for (int st = st0; st < st1; ++st) {
+    // stage st has landed once at most the later stages' loads are pending
+    wait_vmcnt_upto(min(kRing - 2, st1 - 1 - st) * per_stage);
+    __syncthreads();  // every wave's part of stage st is in LDS; stage st-1's buffer is free
+    if (st + kRing - 1 < st1) load_stage(st + kRing - 1);
+    const lds_char* xs = lds + ((st - st0) % kRing) * kStage;
+    const lds_char* ws = xs + kXBytes;
+    bf16x8 xb[4], wa[NC];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) xb[rt] = lds_chunk(xs, wm * 64 + rt * 16 + c, qd);
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) wa[ct] = lds_chunk(ws, wn * NC * 16 + ct * 16 + c, qd);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) acc[rt][ct] = mfma16x16x32(wa[ct], xb[rt], acc[rt][ct]);
+  }
+
+  // lane (c, qd) of tile (rt, ct) holds token m0 + wm*64 + rt*16 + c, stacked
+  // columns col0 + wn*NC*16 + ct*16 + 4qd .. +3
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int64_t t = m0 + wm * 64 + rt * 16 + c;
+    if (t >= n) continue;
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      const int gc = col0 + wn * NC * 16 + ct * 16 + 4 * qd;
+      if (gc >= ncols) continue;
+      const f32x4 v = acc[rt][ct];
+      if (part) {
+        *reinterpret_cast<f32x4*>(part + ((int64_t)blockIdx.z * n + t) * ncols + gc) = v;
+        continue;
+      }
+      const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      uint16_t* dst;
+      if (gc < 64 * G) {
+        dst = q_idx + t * (int64_t)(64 * G) + gc;
+      } else {
+        const int64_t row = ctx_lens ? t * max_ctx + ctx_lens[t] - 1 : t;
+        dst = k_idx + row * 64 + (gc - 64 * G);
+      }
+      *reinterpret_cast<u32x2*>(dst) = o;
+    }
+  }
+}
+
+// Sum of the d_model splits' partials in split order, rounded to bf16.
+__global__ __launch_bounds__(256) void k_index_project_reduce(const float* __restrict__ part, int64_t n, int G,
+                                                              int splits, uint16_t* __restrict__ q_idx,
+                                                              uint16_t* __restrict__ k_idx,
+                                                              const int32_t* __restrict__ ctx_lens, int64_t max_ctx) {
+  const int ncols = 64 * (G + 1);
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 4-column group
+  if (e >= n * (ncols / 4)) return;
+  const int64_t t = e / (ncols / 4);
+  const int gc = (int)(e % (ncols / 4)) * 4;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + t * ncols + gc);
+  for (int z = 1; z < splits; ++z) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + ((int64_t)z * n + t) * ncols + gc);
+    s[0] += v[0];
+    s[1] += v[1];
+    s[2] += v[2];
+    s[3] += v[3];
+  }
+  const u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+  uint16_t* dst;
+  if (gc < 64 * G) {
+    dst = q_idx + t * (int64_t)(64 * G) + gc;
+  } else {
+    const int64_t row = ctx_lens ? t * max_ctx + ctx_lens[t] - 1 : t;
+    dst = k_idx + row * 64 + (gc - 64 * G);
+  }
+  *reinterpret_cast<u32x2*>(dst) = o;
+}
+
+ProjectPlan plan_index_project(int64_t n, int d_model, int G) {
+  ProjectPlan pl;
+  const int units = G + 1;
+  pl.m_tiles = (n + kPRows - 1) / kPRows;
+  if (pl.m_tiles * ((units + 4) / 5) >= 64) {
+    // many tokens: each workgroup takes all (or half) of the columns, so x is
+    // read once (or twice)
+    pl.parts = units <= 5 ? 1 : 2;
+    pl.nc = (units + pl.parts - 1) / pl.parts;
+  } else {
+    // few tokens (decode): one 64-column unit per workgroup, d_model split
+    pl.parts = units;
+    pl.nc = 1;
+  }
+  const int nk = d_model / kPK;
+  const int64_t base = pl.m_tiles * pl.parts;
+  // about two workgroups per CU; each split at least four slices deep, and the
+  // fp32 partials (splits x n x columns) kept below half the weights' bytes
+  int64_t splits = 1;
+  if (base < 256)
+    splits = std::max<int64_t>(1, std::min<int64_t>({(512 + base - 1) / base, nk / 4, d_model / (4 * n)}));
+  pl.stages_per_split = (int)((nk + splits - 1) / splits);
+  pl.splits = (nk + pl.stages_per_split - 1) / pl.stages_per_split;
+  pl.part_floats = pl.splits > 1 ? (size_t)pl.splits * n * 64 * units : 0;
+  return pl;
+}
+
+template <int NC>
+static void launch_nc(const LaunchProject& a, const ProjectPlan& pl, hipStream_t st) {
+  float* part = pl.splits > 1 ? a.part : nullptr;
+  hipLaunchKernelGGL(k_index_project<NC>, dim3((unsigned)pl.m_tiles, pl.parts, pl.splits), dim3(512), 0, st, a.x,
+                     a.w_qi, a.w_ki, a.n, a.d_model, a.G, pl.stages_per_split, a.q_idx, a.k_idx, a.ctx_lens,
+                     a.max_ctx, part);
+}
+
+void launch_index_project(const LaunchProject& a, hipStream_t st) {
+  const ProjectPlan pl = plan_index_project(a.n, a.d_model, a.G);
+  switch (pl.nc) {
+    case 1: launch_nc<1>(a, pl, st); break;
+    case 2: launch_nc<2>(a, pl, st); break;
+    case 3: launch_nc<3>(a, pl, st); break;
+    case 4: launch_nc<4>(a, pl, st); break;
+    case 5: launch_nc<5>(a, pl, st); break;
+    default: return;
+  }
+  if (pl.splits > 1) {
+    const int64_t groups = a.n * 16 * (a.G + 1);
+    hipLaunchKernelGGL(k_index_project_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, a.part,
+                       a.n, a.G, pl.splits, a.q_idx, a.k_idx, a.ctx_lens, a.max_ctx);
+  }
+}
+
+}  // namespace msa

@@ -207,6 +207,39 @@ msa_status msa_index_kl_backward(const msa_params* p, int64_t seq_len,
                                  float* loss, float* dq_idx, float* dk_idx,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Index Branch projections ----------------------------------------------
+ * The index heads are linear maps of the layer's hidden states: one index query
+ * head per group and one index key head shared by all groups [yhxrc, 二; yifor,
+ * 工程實踐啟示: the branch adds two projection matrices]. One call computes
+ * both from one read of x (no bias or activation; fp32 accumulation, outputs
+ * rounded to bf16, nearest even):
+ *   q_idx[t, g, :] = W_qi[g] x[t],   k_idx row of token t = W_ki x[t]
+ *   x      bf16 [n_tokens, d_model]      hidden states; d_model a multiple of 64,
+ *                                        64 .. 65536 (else MSA_ERR_UNSUPPORTED)
+ *   w_qi   bf16 [G, d_idx, d_model]      (out_features x in_features)
+ *   w_ki   bf16 [d_idx, d_model]
+ *   q_idx  bf16 [n_tokens, G, d_idx]     written
+ *   k_idx  bf16 [n_tokens, d_idx]        written (msa_index_project), or
+ *   k_idx_cache bf16 [batch, max_ctx, d_idx]: row ctx_lens[b]-1 of sequence b
+ *                                        written, no other row touched
+ *                                        (msa_index_project_decode: the decode
+ *                                        step's key appended to its cache)
+ *   workspace  >= msa_index_project_workspace_bytes(p, n_tokens, d_model) bytes
+ *              (scratch for small n_tokens, where d_model is split across
+ *              workgroups and the partials summed in a fixed order)
+ * Every pointer 16-byte aligned, the workspace 256-byte aligned. n_tokens up
+ * to 2^28. For a chunk of a longer sequence, pass k_idx at its first cache
+ * row. Results do not depend on the stream's other work or on earlier calls. */
+size_t msa_index_project_workspace_bytes(const msa_params* p, int64_t n_tokens, int32_t d_model);
+msa_status msa_index_project(const msa_params* p, int64_t n_tokens, int32_t d_model,
+                             const void* x, const void* w_qi, const void* w_ki,
+                             void* q_idx, void* k_idx,
+                             void* workspace, size_t workspace_bytes, void* stream);
+msa_status msa_index_project_decode(const msa_params* p, int32_t batch, int64_t max_ctx, int32_t d_model,
+                                    const void* x, const void* w_qi, const void* w_ki,
+                                    const int32_t* ctx_lens, void* q_idx, void* k_idx_cache,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Stage entry points (Index Branch only) ------------------------------
  * For callers that need the selection alone, and for per-stage parity tests. */
 

@@ -173,3 +173,28 @@ def test_index_kl_rejects_bad_args(lib):
     assert f(ctypes.byref(p), 4096, ok, ok, ok, ok, None, ok, ok, ok, ok, ok, need, None) == -1  # no sel
     p.index_dim = 32
     assert f(ctypes.byref(p), 4096, *args, ok, need, None) == -2
+
+
+def test_index_project_rejects_bad_args(lib):
+    p = msa.params()
+    need = msa.index_project_workspace_bytes(p, 64, 8192)
+    assert need >= 64 * 8192 // 64 * 4  # small batches split d_model: fp32 partials
+    assert msa.index_project_workspace_bytes(p, 1 << 20, 8192) > 0
+    assert msa.index_project_workspace_bytes(p, 64, 100) == 0      # d_model not a multiple of 64
+    assert msa.index_project_workspace_bytes(p, 0, 8192) == 0
+    ok = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    f = lib.msa_index_project
+    assert f(ctypes.byref(p), 64, 8192, ok, ok, ok, ok, ok, ok, need - 1, None) == -3
+    assert f(ctypes.byref(p), 64, 100, ok, ok, ok, ok, ok, ok, need, None) == -2
+    assert f(ctypes.byref(p), 64, 1 << 17, ok, ok, ok, ok, ok, ok, need, None) == -2
+    assert f(ctypes.byref(p), 0, 8192, ok, ok, ok, ok, ok, ok, need, None) == -1
+    assert f(ctypes.byref(p), 64, 8192, mis, ok, ok, ok, ok, ok, need, None) == -1
+    assert f(ctypes.byref(p), 64, 8192, ok, ok, ok, None, ok, ok, need, None) == -1
+    assert f(ctypes.byref(p), 64, 8192, ok, ok, ok, ok, ok, None, need, None) == -1
+    d = lib.msa_index_project_decode
+    assert d(ctypes.byref(p), 64, 4096, 8192, ok, ok, ok, None, ok, ok, ok, need, None) == -1   # no ctx_lens
+    assert d(ctypes.byref(p), 0, 4096, 8192, ok, ok, ok, ok, ok, ok, ok, need, None) == -1
+    assert d(ctypes.byref(p), 64, 4096, 8192, ok, ok, ok, ok, ok, ok, ok, need - 1, None) == -3
+    p.index_dim = 32
+    assert f(ctypes.byref(p), 64, 8192, ok, ok, ok, ok, ok, ok, need, None) == -2
