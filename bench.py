@@ -176,9 +176,10 @@ def attention_rooflines(torch, sel, n, stage, bk=BK, topk=TOPK, measured=True):
     """Both attention kernels' roofline positions from the actual selection
     sel [G, n, k]: algorithmic flops per attended key, algorithmic bytes = each
     pass's K/V blocks once, the (query, group) inputs and outputs, and the
-    KV-outer partials written once and read once. Both kernels stage 128 keys
-    at a time, so at B_k < 128 they execute 128/B_k times the flops of a full
-    block ("executed_tflop")."""
+    KV-outer partials written once and read once. "executed_tflop" counts the
+    MFMA work as issued: every key of each selected block (the causal tail of
+    the own block included) and, in the dense pass, all 16 rows of a unit
+    against each of its listed blocks."""
     ps = pair_stats(torch, sel, n, bk=bk)
     q_bytes = HQ // G * D * 2                     # one (query, group): 16 heads x 128 dims, bf16
     part_bytes = q_bytes + HQ // G * 4            # normalised bf16 partial + fp32 lse per head
@@ -188,9 +189,9 @@ def attention_rooflines(torch, sel, n, stage, bk=BK, topk=TOPK, measured=True):
     kernels = [kernel_roofline("k_attn_prefill (KV-outer)", stage["kv_outer_attn"], ps["F_sparse"], b_kv, measured),
                kernel_roofline("k_attn_dense (dense + merge)", stage["dense_attn_merge"], ps["F_dense"], b_dm,
                                measured)]
-    kernels[0]["executed_tflop"] = round(ps["sparse_pairs"] * 4.0 * D * (HQ // G) * 128 / 1e12, 4)
+    kernels[0]["executed_tflop"] = round(ps["sparse_pairs"] * 4.0 * D * (HQ // G) * bk / 1e12, 4)
     # the dense pass's MFMA work including the masked rows of its unit blocks
-    kernels[1]["executed_tflop"] = round(ps["dense_unit_blocks"] * 16 * 4.0 * D * (HQ // G) * 128 / 1e12, 4)
+    kernels[1]["executed_tflop"] = round(ps["dense_unit_blocks"] * 16 * 4.0 * D * (HQ // G) * bk / 1e12, 4)
     return ps, kernels
 
 

@@ -124,6 +124,18 @@ __device__ __forceinline__ void stage_block(lds_char* stage, const uint16_t* kr0
   }
 }
 
+// A block of BK keys (BK < 128: the first BK rows of the stage; the layout of
+// those rows is the one above).
+template <int BK>
+__device__ __forceinline__ void stage_block_bk(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
+                                               int64_t rstride, int nvalid, int wave, int nwaves,
+                                               const StageOffsets& off) {
+  if constexpr (BK == kBlock)
+    stage_block(stage, kr0, vr0, rstride, nvalid, wave, nwaves, off);
+  else
+    stage_rows<BK, kVOff>(stage, kr0, vr0, rstride, nvalid, wave, nwaves);
+}
+
 __device__ __forceinline__ void wait_loads() { wait_vmcnt0(); }
 
 // K A-operand of key tile t, d-step st: lane (c, qd) holds K[16t + c][32st + 8qd .. +7].
@@ -464,6 +476,96 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
   }
 }
 
+// Online-softmax update with one staged block of NT key tiles (NT = BK/16 =
+// 2 or 4: a block of 32 or 64 keys in the first rows of the stage): the
+// arithmetic of attend_block (scores kept raw, lazy rescale, the denominator
+// accumulated through a tile of ones) on the block's keys only, without the
+// two-half pipelining. MASKED, skip and hook as in attend_block (hook(4) once
+// Q is no longer read).
+template <bool FIRST, bool MASKED, int NT, int VOFF = kVOff, class QG, class H>
+__device__ __forceinline__ void attend_short(QG& qg, const lds_char* stage, const int* lim, float scale_log2,
+                                             unsigned skip, H hook) {
+  static_assert(NT == 2 || NT == 4, "blocks of 32 or 64 keys");
+  constexpr int QN = QG::kQN;
+  const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
+  f32x4 s[QN][4];
+#pragma unroll
+  for (int n = 0; n < QN; ++n)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    hook(st);
+    bf16x8 a[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) a[t] = lds_k(stage, t, st, c, qd);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int n = 0; n < QN; ++n) s[n][t] = mfma16x16x32(a[t], qg.qop[n][st], s[n][t]);
+  }
+  hook(4);
+  float mx[QN], mc[QN];
+#pragma unroll
+  for (int n = 0; n < QN; ++n) {
+    if (MASKED) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * t + 4 * qd + r > lim[n]) s[n][t][r] = -__builtin_inff();
+    }
+    float x = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) x = fmaxf(fmaxf(x, fmaxf(s[n][t][0], s[n][t][1])), fmaxf(s[n][t][2], s[n][t][3]));
+    mx[n] = ((skip >> n) & 1u) ? -__builtin_inff() : max_lane_groups(x);
+  }
+  if (FIRST) {
+#pragma unroll
+    for (int n = 0; n < QN; ++n) qg.m[n] = mx[n];
+  } else {
+    bool need = false;
+#pragma unroll
+    for (int n = 0; n < QN; ++n) need |= (mx[n] - qg.m[n]) * scale_log2 > kLazy;
+    if (__any(need)) {
+#pragma unroll
+      for (int n = 0; n < QN; ++n) {
+        const float mnew = fmaxf(qg.m[n], mx[n]);
+        const float alpha = mnew == qg.m[n] ? 1.0f : __builtin_amdgcn_exp2f((qg.m[n] - mnew) * scale_log2);
+#pragma unroll
+        for (int t = 0; t < 9; ++t) qg.o[n][t] *= alpha;
+        qg.m[n] = mnew;
+      }
+    }
+  }
+  bf16x8 p[QN][2];
+#pragma unroll
+  for (int n = 0; n < QN; ++n) {
+    mc[n] = ((skip >> n) & 1u) ? __builtin_inff() : qg.m[n] * scale_log2;
+#pragma unroll
+    for (int j = 0; j < NT / 2; ++j) exp_unit(s, mc, scale_log2, p, n, j);
+  }
+  const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
+  const bf16x8 ones = as_bf16x8((u32x4){one2, one2, one2, one2});
+#pragma unroll
+  for (int st = 0; st < NT / 2; ++st) {
+    hook(5 + st);
+    bf16x8 va[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) va[dt] = lds_vt<VOFF>(stage, dt, st, c, qd);
+#pragma unroll
+    for (int dt = 0; dt < 9; ++dt) {
+      const bf16x8 a = dt < 8 ? va[dt] : ones;
+#pragma unroll
+      for (int n = 0; n < QN; ++n)
+        qg.o[n][dt] = (FIRST && st == 0) ? mfma16x16x32(a, p[n][st], (f32x4){0.f, 0.f, 0.f, 0.f})
+                                         : mfma16x16x32(a, p[n][st], qg.o[n][dt]);
+    }
+  }
+#pragma unroll
+  for (int i = 5 + NT / 2; i < 13; ++i) hook(i);
+}
+
 // Softmax partial of one query, normalised, in fragment order: element (head
 // c, dim 16dt + 4qd + r) sits at dt*256 + (16qd + c)*4 + r of the 2048-element
 // slot, so each of the eight stores of a wave writes 512 contiguous bytes.
@@ -599,8 +701,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   };
   auto stage_tile = [&](const Tile& d, lds_char* dst) {
     const uint64_t e = block_elems(d.b, BK, G, d.g);
-    stage_block(dst, k + e, v + e, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)d.b * BK), wave, kAttnWaves,
-                soff);
+    stage_block_bk<BK>(dst, k + e, v + e, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)d.b * BK), wave,
+                       kAttnWaves, soff);
   };
   QueryGroup<kAttnQN> qg;
   auto fetch_q = [&](const int (&ent)[kAttnQN], int tg) {
@@ -640,7 +742,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     asm volatile("" ::: "memory");
     const lds_char* stage = lds + (j & 1) * kStage;
     KHalf k0;
-    if (e0 < cur.len) load_k_half(k0, stage);
+    if (BK == kBlock && e0 < cur.len) load_k_half(k0, stage);
     // chunk c+1 is claimed when chunk c starts; it is first read two tiles
     // later (for tile kClaim*(c+1)), after at least one more barrier
     if (tid == 0 && j % kClaim == 0) s_t[(j / kClaim + 1) & 1] = atomicAdd(&tile_info[1], kClaim);
@@ -665,13 +767,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
       auto hook = [&](int i) {
         if (i == 4 && next_work) fetch_q(nent, nxt.g);
       };
-      if constexpr (BK == kBlock) {
+      if constexpr (BK == kBlock)
         attend_block<true, false>(qg, stage, k0, nullptr, scale_log2, 0u, hook);
-      } else {
-        // a block of BK < 128 keys in a 128-key stage: keys >= BK masked
-        const int lim[kAttnQN] = {BK - 1, BK - 1};
-        attend_block<true, true>(qg, stage, k0, lim, scale_log2, 0u, hook);
-      }
+      else
+        attend_short<true, false, BK / 16>(qg, stage, nullptr, scale_log2, 0u, hook);
 #pragma unroll
       for (int n = 0; n < kAttnQN; ++n) {
         if (e0 + n < cur.len) {
@@ -743,8 +842,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   {
     const int b0 = __builtin_amdgcn_readfirstlane(lane_blk);
     const uint64_t e0 = block_elems(b0, BK, G, g);
-    stage_block(lds, k + e0, v + e0, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)b0 * BK), wave,
-                kAttnWaves, soff);
+    stage_block_bk<BK>(lds, k + e0, v + e0, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)b0 * BK), wave,
+                       kAttnWaves, soff);
   }
   // slots of each query's selection computed KV-outer: the valid ones the
   // dense pass does not cover
@@ -806,15 +905,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     wait_loads();
     __syncthreads();  // stage d&1 and the slot complete; stage (d+1)&1 free
     KHalf k0;
-    load_k_half(k0, lds + (d & 1) * kStage);
+    if constexpr (BK == kBlock) load_k_half(k0, lds + (d & 1) * kStage);
     // block d+1 streams into the other stage, loaded by waves 0-3 only (one
     // per SIMD): their partners start computing while they wait for room in
     // the memory queue
     const int b2 = __builtin_amdgcn_readlane(lane_blk, d + 1);
     const uint64_t e2 = block_elems(b2, BK, G, g);
     if (wave < 4)
-      stage_block(lds + ((d + 1) & 1) * kStage, k + e2, v + e2, rstride,
-                  (int)min<int64_t>(BK, n_tokens - (int64_t)b2 * BK), wave, 4, soff);
+      stage_block_bk<BK>(lds + ((d + 1) & 1) * kStage, k + e2, v + e2, rstride,
+                         (int)min<int64_t>(BK, n_tokens - (int64_t)b2 * BK), wave, 4, soff);
     // merge the slot's partial, then refill the slot right away: the load has
     // the whole block's compute to arrive
     if (pend_n >= 0) {
@@ -829,12 +928,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const unsigned skip =
         ~((unsigned)__builtin_amdgcn_readlane(lane_qm, d) >> (wave * kAttnQN)) & ((1u << kAttnQN) - 1u);
     if (skip != (1u << kAttnQN) - 1u) {
-      if constexpr (BK == kBlock) {
+      if constexpr (BK == kBlock)
         attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [](int) {});
-      } else {
-        const int lim[kAttnQN] = {BK - 1, BK - 1};  // keys >= BK of the stage masked
-        attend_block<false, true>(qg, lds + (d & 1) * kStage, k0, lim, scale_log2, skip, [](int) {});
-      }
+      else
+        attend_short<false, false, BK / 16>(qg, lds + (d & 1) * kStage, nullptr, scale_log2, skip, [](int) {});
     }
   }
 
@@ -882,14 +979,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     wait_loads();
     __syncthreads();
     KHalf k0;
-    load_k_half(k0, lds + last * kStage);
+    if constexpr (BK == kBlock) load_k_half(k0, lds + last * kStage);
     if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
     wait_lgkmcnt0();  // the slot is read out: it holds the lse of the rounds
     issue_round(0, cA, nA0, nA1);
     int lim[kAttnQN];
 #pragma unroll
     for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * BK);
-    attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [](int) {});
+    if constexpr (BK == kBlock)
+      attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [](int) {});
+    else
+      attend_short<false, true, BK / 16>(qg, lds + last * kStage, lim, scale_log2, 0u, [](int) {});
   }
   wait_lgkmcnt0();  // the last block's stage is free
   asm volatile("" ::: "memory");
@@ -948,17 +1048,21 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   const int Hq = G * kHpg;
   const int64_t base = ((int64_t)sq * max_ctx * G + key0 * G + g) * kHeadDim;
   // only positions < ctx_len are read: later cache rows may hold anything
-  stage_block(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(BK, i + 1 - key0), wave, 4,
-              stage_offsets((int64_t)G * kHeadDim, wave));
+  stage_block_bk<BK>(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(BK, i + 1 - key0), wave, 4,
+                     stage_offsets((int64_t)G * kHeadDim, wave));
   QueryGroup<1> qg;
   if (wave == 0) load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
   wait_loads();
   __syncthreads();
   if (wave != 0) return;
   int lim[1] = {(i / BK == b) ? (int)(i - key0) : BK - 1};
-  KHalf k0;
-  load_k_half(k0, lds);
-  attend_block<true, true>(qg, lds, k0, lim, scale_log2, 0u, [](int) {});
+  if constexpr (BK == kBlock) {
+    KHalf k0;
+    load_k_half(k0, lds);
+    attend_block<true, true>(qg, lds, k0, lim, scale_log2, 0u, [](int) {});
+  } else {
+    attend_short<true, true, BK / 16>(qg, lds, lim, scale_log2, 0u, [](int) {});
+  }
   store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
                 part_lse + (int64_t)item * kHpg);
 }
