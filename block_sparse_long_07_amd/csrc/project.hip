@@ -170,13 +170,23 @@ __global__ __launch_bounds__(256) void k_index_project_reduce(const float* __res
   if (e >= n * (ncols / 4)) return;
   const int64_t t = e / (ncols / 4);
   const int gc = (int)(e % (ncols / 4)) * 4;
-  f32x4 s = *reinterpret_cast<const f32x4*>(part + t * ncols + gc);
-  for (int z = 1; z < splits; ++z) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part + ((int64_t)z * n + t) * ncols + gc);
-    s[0] += v[0];
-    s[1] += v[1];
-    s[2] += v[2];
-    s[3] += v[3];
+  const float* src = part + t * ncols + gc;
+  const int64_t zstride = n * ncols;
+  f32x4 s = *reinterpret_cast<const f32x4*>(src);
+  // eight partials in flight at a time, added in split order
+  for (int z0 = 1; z0 < splits; z0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)(z0 + u) * zstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) {
+        s[0] += v[u][0];
+        s[1] += v[u][1];
+        s[2] += v[u][2];
+        s[3] += v[u][3];
+      }
   }
   const u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
   uint16_t* dst;
