@@ -43,14 +43,14 @@ class RowsF64:
         return mo.to_f64(self.t[idx])
 
 
-def oracle_rows_threaded(rows, q_rows, qi_rows, ki, k, v, topk, threads=16):
+def oracle_rows_threaded(rows, q_rows, qi_rows, ki, k, v, topk, threads=16, block_size=128):
     from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
     parts = np.array_split(np.arange(len(rows)), max(1, min(64, len(rows) // 16)))
     done = [0]
 
     def run(ix):
-        r = mo.prefill_rows(rows[ix], q_rows[ix], qi_rows[ix], ki, k, v, block_size=128, topk=topk)
+        r = mo.prefill_rows(rows[ix], q_rows[ix], qi_rows[ix], ki, k, v, block_size=block_size, topk=topk)
         done[0] += len(ix)
         if done[0] % 512 < len(ix):
             log(f"    oracle rows {done[0]}/{len(rows)}")
@@ -63,6 +63,7 @@ def oracle_rows_threaded(rows, q_rows, qi_rows, ki, k, v, topk, threads=16):
 
 
 def prefill_sampled(inp, topk, rows, label):
+    bk = inp.dims.block_size
     dev = "cuda"
     log(f"case {label}: N={inp.n} rows={len(rows)}")
     with timed("inputs"):
@@ -73,7 +74,7 @@ def prefill_sampled(inp, topk, rows, label):
         ki = inp.k_idx(device=dev)[None]
         torch.cuda.synchronize()
     with timed("gpu"):
-        out, sel, lse = msa.prefill(q, k, v, qi, ki, topk=topk, want_sel=True, want_lse=True)
+        out, sel, lse = msa.prefill(q, k, v, qi, ki, topk=topk, block_size=bk, want_sel=True, want_lse=True)
         torch.cuda.synchronize()
     rows = np.asarray(rows, dtype=np.int64)
     rt = torch.as_tensor(rows, device=dev)
@@ -83,7 +84,7 @@ def prefill_sampled(inp, topk, rows, label):
     del out, lse, q
     with timed("oracle"):
         ref = oracle_rows_threaded(rows, mo.to_f64(inp.q(rows)), mo.to_f64(inp.q_idx(rows)),
-                                   mo.to_f64(ki[0]), RowsF64(k[0]), RowsF64(v[0]), topk)
+                                   mo.to_f64(ki[0]), RowsF64(k[0]), RowsF64(v[0]), topk, block_size=bk)
     mism = np.argwhere(got_sel != ref["sel"])
     assert mism.size == 0, f"selection mismatch at {mism[:5].tolist()}"
     compare_out(got_out, ref["out"], f"{label} out")
@@ -108,6 +109,21 @@ def test_prefill_1m_sampled():
     bounds = [w * 65536 + o for w in range(16) for o in (0, 1, 127, 128, 65535) if w * 65536 + o < n]
     rows = np.union1d(syn.stratified_rows(n, 4096, 128, 4, topk, extra=extra), bounds)
     prefill_sampled(inp, topk, rows, "prefill 1M")
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("bk", [64, 32])
+def test_prefill_longest_at_small_blocks_sampled(bk):
+    """The longest sequence a smaller block size takes (2^20 * B_k / 128
+    positions: 8192 blocks, as at B_k = 128 and 1M), over several windows."""
+    n, topk = (1 << 20) * bk // 128, 16
+    dims = syn.Dims(block_size=bk)
+    inp = syn.PrefillInputs(n, dims, 9, "planted", n_planted=8)
+    extra = sorted({b for g in inp.planted.values() for b in g})
+    bounds = [w * 65536 + o for w in range(n // 65536 + 1) for o in (0, 1, bk - 1, bk, 65535)
+              if w * 65536 + o < n] + [n - 1]
+    rows = np.union1d(syn.stratified_rows(n, 2048, bk, 7, topk, extra=extra), bounds)
+    prefill_sampled(inp, topk, rows, f"prefill {n} at B_k={bk}")
 
 
 @pytest.mark.timeout(1200)
