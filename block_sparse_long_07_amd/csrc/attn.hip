@@ -813,8 +813,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const int32_t* __restrict__ dense_qmask, const int32_t* __restrict__ dense_slots, const uint16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t n_tokens,
     int64_t row0, int nrows, int nunits, int G, int topk, float scale_log2) {
-  // two K/V stages, then one 4 KiB partial slot per wave (160 KiB in all)
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage + kAttnWaves * 4096];
+  // two K/V stages, then 256 bytes per wave for the partials' lse
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage + kAttnWaves * 256];
   lds_char* lds = (lds_char*)lds_raw;
   const int unit = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -858,12 +858,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   }
   reset_state(qg);
 
-  // KV-outer partials of the wave's queries, in (query, slot) order. One at a
-  // time streams into the wave's slot while a dense block is computed (issued
-  // once the previous one is merged, at the start of the block) and is merged
-  // at the start of the next block; the rest go through the two larger
-  // regions after the last block (below).
-  lds_char* pslot = lds + 2 * kStage + wave * 4096;
+  // KV-outer partials of the wave's queries, in (query, slot) order, merged
+  // after the last block (below). Merging them between blocks instead costs
+  // more: the waves' partial counts differ, and every block's barrier then
+  // waits for the wave with the most.
+  lds_char* lse_side = lds + 2 * kStage + wave * 256;  // [region][partial][16 heads] fp32
   // (wave-uniform bookkeeping, kept in scalar registers; slot indices fit 32
   // bits: rows * G * topk of a window)
   int cur_n = 0;
@@ -882,28 +881,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     slot = (uint32_t)__builtin_amdgcn_readfirstlane(((i_rel0 + cur_n) * G + g) * topk + pu);
     return true;
   };
-  int pend_n = -1;       // query of the partial in the slot (-1: none)
-  float pend_lse = 0.f;  // its lse2 for the lane's head
-  int64_t pend_slot = 0;
-  // picks the next partial for the slot (pend_n, pend_slot); its loads are
-  // issued by slot_piece(0..3) and its lse with piece 0
-  auto take_slot = [&]() {
-    int pn = 0;
-    pend_n = next_pair(pn, pend_slot) ? pn : -1;
-  };
-  auto slot_piece = [&](int j) {
-    if (pend_n < 0) return;
-    lds_dma16_s(part_o + pend_slot * (kHpg * kHeadDim) + j * 512, (uint32_t)lane * 16, pslot + j * 1024);
-    if (j == 0) pend_lse = part_lse[pend_slot * kHpg + c];
-  };
-  take_slot();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) slot_piece(j);
 
   // shared older blocks (unmasked), then the unit's own block (masked)
   for (int d = 0; d + 1 < nd; ++d) {
     wait_loads();
-    __syncthreads();  // stage d&1 and the slot complete; stage (d+1)&1 free
+    __syncthreads();  // stage d&1 complete; stage (d+1)&1 free
     KHalf k0;
     if constexpr (BK == kBlock) load_k_half(k0, lds + (d & 1) * kStage);
     // block d+1 streams into the other stage, loaded by waves 0-3 only (one
@@ -914,15 +896,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     if (wave < 4)
       stage_block_bk<BK>(lds + ((d + 1) & 1) * kStage, k + e2, v + e2, rstride,
                          (int)min<int64_t>(BK, n_tokens - (int64_t)b2 * BK), wave, 4, soff);
-    // merge the slot's partial, then refill the slot right away: the load has
-    // the whole block's compute to arrive
-    if (pend_n >= 0) {
-      merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
-      wait_lgkmcnt0();  // the slot is read out before it is refilled
-    }
-    take_slot();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) slot_piece(j);
     // queries of the wave that did not select the block are masked; a wave
     // with none that did skips it
     const unsigned skip =
@@ -935,15 +908,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     }
   }
 
-  // The remaining partials stream through two 8 KiB LDS regions of the wave
-  // (two partials each, direct-to-LDS loads, their lse into the wave's slot):
+  // The partials stream through two 8 KiB LDS regions of the wave (two
+  // partials each, direct-to-LDS loads, their lse into the wave's lse_side):
   // region 0 in the stage not holding the last block, filled while the last
   // block is computed; region 1 in the last block's stage once every wave is
   // done with it. Completion is tracked with vmcnt (5 loads per partial), so
   // one region is merged while the other streams in.
   const int last = (nd - 1) & 1;
   lds_char* region[2] = {lds + (last ^ 1) * kStage + wave * 8192, lds + last * kStage + wave * 8192};
-  lds_char* lse_side = pslot;  // [region][partial][16 heads] fp32
   auto issue_round = [&](int reg, int& cnt, int& na, int& nb) {
     cnt = 0;
 #pragma unroll
@@ -980,8 +952,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
     __syncthreads();
     KHalf k0;
     if constexpr (BK == kBlock) load_k_half(k0, lds + last * kStage);
-    if (pend_n >= 0) merge_partial_into(qg, pend_n, pslot, pend_lse, scale_log2);
-    wait_lgkmcnt0();  // the slot is read out: it holds the lse of the rounds
     issue_round(0, cA, nA0, nA1);
     int lim[kAttnQN];
 #pragma unroll
