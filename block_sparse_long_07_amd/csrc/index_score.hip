@@ -17,13 +17,18 @@
 
 namespace msa {
 
-// One workgroup (4 waves) per (query block qb, chunk of kKC key blocks); it
+// One workgroup (4 waves) per (query block qb, chunk of key blocks); it
 // covers the 128*G index rows (i, g) of the query block, 32*G per wave. Each
 // 16 KiB key block is loaded once per workgroup straight into LDS
 // (global_load_lds, double-buffered) and read as MFMA operands by all waves.
 // LDS layout: 128 rows of 128 B; 16-byte chunk x of row r sits at chunk
 // position x ^ ((r >> 1) & 7), which keeps the operand reads conflict-free.
-constexpr int kKC = 8;
+// Key blocks per workgroup: two 128-key stages at B_k = 128, one stage
+// otherwise. Short workgroups spread the causal triangle's uneven work over
+// the whole chip: chunks of 4 and 8 blocks measured 1.05x and 1.3x slower at
+// B_k = 128, 16 slower still.
+template <int SUB>
+constexpr int chunk_blocks() { return SUB == 1 ? 2 : SUB; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -52,7 +57,8 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
                                                           float* __restrict__ sblk, int64_t row0,
                                                           int64_t row_end, int qb_begin, int nb) {
   constexpr int RT = 2 * G;        // 16-row tiles per wave
-  constexpr int NS = kKC / SUB;    // stages per chunk: the chunk yields kKC blocks
+  constexpr int KC = chunk_blocks<SUB>();  // blocks per chunk
+  constexpr int NS = KC / SUB;            // 128-key stages per chunk
   constexpr int TPB = 8 / SUB;     // key tiles per block
   constexpr int BKS = kBlock / SUB;
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * 16384];
@@ -85,12 +91,12 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
   }
 
   // pooled scores of the chunk: lane group qd keeps the rows of tiles rt = qd
-  // (mod 4), kKC blocks each, and writes them as one 32-byte run per row
-  float res[(RT + 3) / 4][kKC];
+  // (mod 4), KC blocks each, and writes them as one run per row
+  float res[(RT + 3) / 4][KC];
 #pragma unroll
   for (int j = 0; j < (RT + 3) / 4; ++j)
 #pragma unroll
-    for (int x = 0; x < kKC; ++x) res[j][x] = -__builtin_inff();
+    for (int x = 0; x < KC; ++x) res[j][x] = -__builtin_inff();
 
   // fully unrolled over the chunk's stages, so every pooled maximum lands in
   // a fixed register (the block position is a constant)
@@ -147,12 +153,17 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
     const int nout = SUB == 1 ? nkb : max(0, min(nkb, (int)((row / G) / BKS) - kb0 * SUB));
     float* dst = sblk + (row - flat_lo) * nb + kb0 * SUB;
     const float* rv = res[rt >> 2];
-    if (nout == kKC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-      *reinterpret_cast<f32x4*>(dst) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
-      *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){rv[4], rv[5], rv[6], rv[7]};
+    if (nout == KC && (reinterpret_cast<uintptr_t>(dst) & (4 * KC - 1)) == 0) {
+      if constexpr (KC == 2) {
+        *reinterpret_cast<f32x2*>(dst) = (f32x2){rv[0], rv[1]};
+      } else {
+#pragma unroll
+        for (int v4 = 0; v4 < KC / 4; ++v4)
+          *reinterpret_cast<f32x4*>(dst + 4 * v4) = (f32x4){rv[4 * v4], rv[4 * v4 + 1], rv[4 * v4 + 2], rv[4 * v4 + 3]};
+      }
     } else {
 #pragma unroll
-      for (int xx = 0; xx < kKC; ++xx)
+      for (int xx = 0; xx < KC; ++xx)
         if (xx < nout) dst[xx] = rv[xx];
     }
   }
@@ -236,7 +247,7 @@ template <int G, int SUB>
 static void launch_prefill_g(const LaunchIndexPrefill& a, hipStream_t st) {
   const int n_qb = a.qb_end - a.qb_begin;
   if (n_qb <= 0) return;
-  constexpr int NS = kKC / SUB;
+  constexpr int NS = chunk_blocks<SUB>() / SUB;
   const int stages = SUB > 1 ? a.qb_end : a.qb_end - 1;  // stages of the last query block
   const int chunks = (stages + NS - 1) / NS;
   if (chunks <= 0) return;
