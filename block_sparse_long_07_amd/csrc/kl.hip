@@ -13,7 +13,7 @@
 //
 // Work is organised like the KV-outer main branch: the reverse index of the
 // selections lists, per (group, block), the queries that selected it (every
-// pair, no dense split), cut into chunks of up to 1024 queries. One workgroup
+// pair, no dense split), cut into chunks of up to 512 queries. One workgroup
 // per chunk stages the block's K and k_idx (also transposed) in LDS once and
 // takes the queries 16 at a time. Pass 1 writes, per (query, slot), the max
 // and the sum of exp of the index scores over the block; a combine gives each
