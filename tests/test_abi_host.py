@@ -202,3 +202,9 @@ def test_index_project_rejects_bad_args(lib):
     assert d(ctypes.byref(p), 64, 4096, 8192, ok, ok, ok, ok, ok, ok, ok, need - 1, None) == -3
     p.index_dim = 32
     assert f(ctypes.byref(p), 64, 8192, ok, ok, ok, ok, ok, ok, need, None) == -2
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No CPU or eager fallback: loading a library that is not there raises."""
+    with pytest.raises(OSError):
+        msa.load(str(tmp_path / "libmsa.so"))

@@ -147,3 +147,15 @@ def test_projection_feeds_prefill_selection_exactly():
     assert np.array_equal(sel[0][:, rt].permute(1, 0, 2).cpu().numpy(), ref["sel"])
     err = np.abs(out[0][rt].double().cpu().numpy() - ref["out"]).max()
     assert err <= 2e-2
+
+
+def test_split_reduce_is_deterministic():
+    """The split plan sums its partials in a fixed order: two calls agree bit
+    for bit."""
+    x, wq, wk = normal_inputs(3, 64, 8192, 4)
+    xc, wqc, wkc = x.cuda(), wq.cuda(), wk.cuda()
+    a = [t.clone() for t in msa.index_project(xc, wqc, wkc)]
+    b = msa.index_project(xc, wqc, wkc)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
