@@ -189,20 +189,29 @@ __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sb
       id[t] = 0x7fffffff;
     }
     const float* row = sblk + r * (int64_t)nb;
-    for (int b = lane; b < b_loc; b += 64) {
-      float cv = row[b];
-      if (cv > v[KM1 - 1]) {
-        int ci = b;
-        bool shift = false;
+    // 16 candidates per lane are loaded before any is ranked, so their
+    // latencies overlap; they are then inserted in ascending order
+    constexpr int kBatch = 16;
+    for (int b0 = lane; b0 < b_loc; b0 += 64 * kBatch) {
+      float cand[kBatch];
 #pragma unroll
-        for (int t = 0; t < KM1; ++t) {
-          shift = shift || (cv > v[t]);
-          const float nv = shift ? cv : v[t];
-          const int ni = shift ? ci : id[t];
-          cv = shift ? v[t] : cv;
-          ci = shift ? id[t] : ci;
-          v[t] = nv;
-          id[t] = ni;
+      for (int u = 0; u < kBatch; ++u) cand[u] = b0 + 64 * u < b_loc ? row[b0 + 64 * u] : -__builtin_inff();
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        float cv = cand[u];
+        if (b0 + 64 * u < b_loc && cv > v[KM1 - 1]) {
+          int ci = b0 + 64 * u;
+          bool shift = false;
+#pragma unroll
+          for (int t = 0; t < KM1; ++t) {
+            shift = shift || (cv > v[t]);
+            const float nv = shift ? cv : v[t];
+            const int ni = shift ? ci : id[t];
+            cv = shift ? v[t] : cv;
+            ci = shift ? id[t] : ci;
+            v[t] = nv;
+            id[t] = ni;
+          }
         }
       }
     }
