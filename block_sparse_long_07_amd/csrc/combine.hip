@@ -36,21 +36,31 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
     if (u < nsel) lse_u[u] = __builtin_nontemporal_load(part_lse + (slot0 + u) * kHpg + h);
     M = fmaxf(M, lse_u[u]);
   }
+  // every slot's loads are issued before any is used, so their latencies
+  // overlap; the sum then runs in slot order
+  u32x2 pa[kMaxTopk], pb[kMaxTopk];
+#pragma unroll
+  for (int u = 0; u < kMaxTopk; ++u) {
+    pa[u] = pb[u] = (u32x2){0u, 0u};
+    if (u < nsel) {
+      const uint16_t* src = part_o + (slot0 + u) * (kHpg * kHeadDim) + dt * 256 + (16 * qd + h) * 4;
+      pa[u] = *reinterpret_cast<const u32x2*>(src);
+      pb[u] = *reinterpret_cast<const u32x2*>(src + 64);  // qd + 1
+    }
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
 #pragma unroll
   for (int u = 0; u < kMaxTopk; ++u) {
-    if (u >= nsel) break;
-    const float w = __builtin_amdgcn_exp2f(lse_u[u] - M);
-    wsum += w;
-    const uint16_t* src = part_o + (slot0 + u) * (kHpg * kHeadDim) + dt * 256 + (16 * qd + h) * 4;
-    const u32x2 a = *reinterpret_cast<const u32x2*>(src);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(src + 64);  // qd + 1
-    const uint32_t o[4] = {a[0], a[1], b[0], b[1]};
+    if (u < nsel) {
+      const float w = __builtin_amdgcn_exp2f(lse_u[u] - M);
+      wsum += w;
+      const uint32_t o[4] = {pa[u][0], pa[u][1], pb[u][0], pb[u][1]};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += w * bf2f(o[e] & 0xffffu);
-      acc[2 * e + 1] += w * bf2f(o[e] >> 16);
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += w * bf2f(o[e] & 0xffffu);
+        acc[2 * e + 1] += w * bf2f(o[e] >> 16);
+      }
     }
   }
   const float inv = 1.0f / wsum;
