@@ -139,9 +139,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "23b86bdb29621a20",
-    "k_attn_prefill (KV-outer)": 5.343e9,
-    "k_attn_dense (dense + merge)": 4.410e9,
+    "source": "3f99b0d7ba2c866b",
+    "k_attn_prefill (KV-outer)": 5.342e9,
+    "k_attn_dense (dense + merge)": 4.413e9,
 }
 
 

@@ -720,6 +720,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
   // the queue: chunk c of this workgroup's tiles (tiles kClaim*c ..) starts at
   // queue position s_t[c & 1]
   constexpr int kClaim = 4;
+  // chunk c+1 is claimed at tile kClaim*c and first read for tile kClaim*c + 2
+  // (the descriptor two tiles ahead): a barrier lies between only if the
+  // chunk is longer than two tiles
+  static_assert(kClaim >= 3, "the claim must be visible before the look-ahead reads it");
   if (tid == 0) s_t[0] = atomicAdd(&tile_info[1], kClaim);
   __syncthreads();
   auto tile_pos = [&](int jj) { return __builtin_amdgcn_readfirstlane(s_t[(jj / kClaim) & 1] + jj % kClaim); };
