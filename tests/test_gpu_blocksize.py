@@ -79,7 +79,7 @@ def test_select_exact_with_ties(bk, topk, n):
 @pytest.mark.parametrize("bk", [64, 32])
 @pytest.mark.parametrize("n,G,topk,recipe", [
     (1, 1, 4, "tiny"), (33, 1, 2, "tiny"), (129, 1, 4, "tiny"), (1000, 2, 4, "planted"),
-    (2500, 4, 16, "planted"), (1920, 1, 1, "tiny"), (4321, 3, 7, "tiny"),
+    (2500, 4, 16, "planted"), (1920, 1, 1, "tiny"), (4321, 3, 7, "tiny"), (1500, 8, 16, "planted"),
 ])
 def test_prefill_all_rows(bk, n, G, topk, recipe):
     inp = syn.PrefillInputs(n, dims(G, topk, bk), 5, recipe, n_planted=2)
@@ -138,12 +138,12 @@ def test_chunked_prefill_vs_oracle(bk, bounds):
         compare_lse(lse, ref["lse"][a:b], f"chunk [{a},{b})")
 
 
-@pytest.mark.parametrize("bk", [64, 32])
-def test_decode_ragged(bk):
-    G, topk, B, max_ctx = 4, 16, 7, 3000
+@pytest.mark.parametrize("bk,G", [(64, 4), (32, 4), (64, 1), (32, 8)])
+def test_decode_ragged(bk, G):
+    topk, B, max_ctx = 16, 7, 3000
     lens = [1, bk, bk + 1, 1500, 2048, 2999, 3000]
     dec = syn.DecodeInputs(B, max_ctx, dims(G, topk, bk), 4, ctx_lens=lens)
-    log(f"case decode B_k={bk}")
+    log(f"case decode B_k={bk} G={G}")
     q = torch.stack([dec.q(b, "cuda") for b in range(B)]).contiguous()
     qi = torch.stack([dec.q_idx(b, "cuda") for b in range(B)]).contiguous()
     kc = torch.stack([dec.k_cache(b, device="cuda") for b in range(B)]).contiguous()
