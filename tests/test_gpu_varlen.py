@@ -94,14 +94,16 @@ def test_chunks_at_multiples_of_16_equal_one_call():
         assert torch.equal(lse, full_lse[0][a:b]), f"chunk [{a},{b}) lse"
 
 
-def test_varlen_batch_vs_oracle():
+@pytest.mark.parametrize("bk", [128, 32])
+def test_varlen_batch_vs_oracle(bk):
     G, topk = 4, 16
     # (q_start, q_len): fresh prompts, continuations of a cache, one token,
     # an empty entry, an unaligned start with a ragged length
     specs = [(0, 1500), (777, 1300), (2000, 1), (3, 0), (1040, 37), (0, 2100)]
     max_ctx = 2100
     B = len(specs)
-    inps = [syn.PrefillInputs(max(s + l, 1), dims(G, topk), 50 + b, "planted", n_planted=3)
+    d = syn.Dims(num_q_heads=16 * G, num_kv_heads=G, head_dim=128, index_dim=64, block_size=bk, topk=topk)
+    inps = [syn.PrefillInputs(max(s + l, 1), d, 50 + b, "planted", n_planted=3)
             for b, (s, l) in enumerate(specs)]
     kc = torch.empty((B, max_ctx, G, 128), dtype=torch.bfloat16, device="cuda")
     vc = torch.empty_like(kc)
@@ -118,9 +120,9 @@ def test_varlen_batch_vs_oracle():
             qis.append(inp.q_idx(rows, device="cuda"))
     q = torch.cat(qs).contiguous()
     qi = torch.cat(qis).contiguous()
-    log(f"case varlen batch specs={specs}")
+    log(f"case varlen batch B_k={bk} specs={specs}")
     out, sel, lse = msa.prefill_varlen(q, qi, kc, vc, kic, [s for s, _ in specs], [l for _, l in specs],
-                                       topk=topk, want_sel=True, want_lse=True)
+                                       topk=topk, block_size=bk, want_sel=True, want_lse=True)
     torch.cuda.synchronize()
     r = 0
     for b, ((s, l), inp) in enumerate(zip(specs, inps)):
