@@ -560,10 +560,20 @@ __global__ __launch_bounds__(256) void k_kl_out(const float* __restrict__ loss_p
   const int64_t i_rel = x / G, i = row0 + i_rel;
   const int g = (int)(x % G);
   const int nsel = (int)min<int64_t>(topk, i / kBlock + 1);
+  // every slot's loads are issued before the sums, which run in slot order
+  float dv[kMaxTopk], lv[kMaxTopk];
+#pragma unroll
+  for (int u = 0; u < kMaxTopk; ++u) {
+    dv[u] = u < nsel ? dq_part[(x * topk + u) * kIndexDim + lane] : 0.f;
+    lv[u] = u < nsel ? loss_part[x * topk + u] : 0.f;
+  }
   float d = 0.f, l = 0.f;
-  for (int u = 0; u < nsel; ++u) {
-    d += dq_part[(x * topk + u) * kIndexDim + lane];
-    l += loss_part[x * topk + u];
+#pragma unroll
+  for (int u = 0; u < kMaxTopk; ++u) {
+    if (u < nsel) {
+      d += dv[u];
+      l += lv[u];
+    }
   }
   dq_idx[x * kIndexDim + lane] = d;
   if (lane == 0) loss[(int64_t)g * n_tokens + i] = l;
