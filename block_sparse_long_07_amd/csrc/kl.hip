@@ -529,7 +529,17 @@ __global__ __launch_bounds__(256) void k_kl_dk(const float* __restrict__ dk_part
     f32x4 acc = *reinterpret_cast<const f32x4*>(dk_idx + key0 * kIndexDim + x * 4);
     for (int g = 0; g < G; ++g) {
       const int t0 = tile_start[g * nbw + b], t1 = tile_start[g * nbw + b + 1];
-      for (int t = t0; t < t1; ++t) acc = acc + *reinterpret_cast<const f32x4*>(dk_part + (int64_t)t * kBlock * kIndexDim + x * 4);
+      // eight chunk partials in flight at a time, added in chunk order
+      for (int t = t0; t < t1; t += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = t + u < t1 ? *reinterpret_cast<const f32x4*>(dk_part + (int64_t)(t + u) * kBlock * kIndexDim + x * 4)
+                            : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (t + u < t1) acc = acc + v[u];
+      }
     }
     *reinterpret_cast<f32x4*>(dk_idx + key0 * kIndexDim + x * 4) = acc;
   }
