@@ -177,8 +177,10 @@ struct DecodeLayout {
   size_t sblk, sel, part_o, part_lse, total;
 };
 
+// max_ctx beyond the longest supported context has no layout (the caller
+// reports MSA_ERR_UNSUPPORTED)
 bool decode_layout(const Shape& s, int32_t B, int64_t max_ctx, DecodeLayout* L) {
-  if (B <= 0 || max_ctx <= 0) return false;
+  if (B <= 0 || max_ctx <= 0 || max_ctx > s.max_seq) return false;
   L->nb = (int)cdiv(max_ctx, s.bk);
   const size_t items = (size_t)B * s.G * s.k;
   size_t off = 0;
@@ -519,7 +521,8 @@ msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const
   Shape s;
   msa_status st = check_params(p, &s);
   if (st != MSA_OK) return st;
-  if (batch <= 0 || max_ctx <= 0 || max_ctx > (int64_t)INT32_MAX) return MSA_ERR_INVALID_ARG;
+  if (batch <= 0 || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
+  if (max_ctx > s.max_seq) return MSA_ERR_UNSUPPORTED;
   for (const void* ptr : {q, q_idx, k_cache, v_cache, k_idx_cache, (const void*)out})
     if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
   if (!ctx_lens || !aligned(ctx_lens, 4)) return MSA_ERR_INVALID_ARG;

@@ -76,7 +76,11 @@ typedef struct {
  * Returns 0 for invalid or unsupported arguments. */
 size_t msa_prefill_workspace_bytes(const msa_params* p, int32_t batch, int64_t seq_len);
 
-/* Causal MSA prefill of `batch` independent sequences of `seq_len` tokens.
+/* Causal MSA prefill of `batch` independent sequences of `seq_len` tokens: for
+ * every query row and group, the Index Branch selects the own block plus the
+ * k-1 best-scoring older blocks, and the Main Branch computes exact softmax
+ * attention over the selected blocks' tokens at or before the row [pnsm,
+ * section 2: group-specific block selection; yhxrc, 二 "MSA是怎么做的"].
  *   q      bf16 [batch, seq_len, Hq, d]       query heads; head h belongs to group h / 16
  *   k, v   bf16 [batch, seq_len, G, d]        main-branch keys / values
  *   q_idx  bf16 [batch, seq_len, G, d_idx]    one index query head per group
@@ -130,7 +134,8 @@ msa_status msa_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ct
                               void* out, int32_t* sel_out, float* lse_out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace msa_decode needs. Returns 0 on invalid arguments. */
+/* Bytes of device workspace msa_decode needs. Returns 0 on invalid arguments
+ * and for max_ctx above the longest supported context. */
 size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx);
 
 /* One decode step for `batch` sequences. Decode is prefill's last row: the new
@@ -146,7 +151,9 @@ size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t ma
  *                cache positions >= ctx_lens[b] are never read
  *   out          bf16 [batch, Hq, d]
  *   sel_out      optional int32 [batch, G, topk] (ascending, -1 padded)
- *   lse_out      optional fp32 [batch, Hq] */
+ *   lse_out      optional fp32 [batch, Hq]
+ * max_ctx above the longest supported context (2^20 * block_size / 128) is
+ * MSA_ERR_UNSUPPORTED. */
 msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx,
                       const void* q, const void* q_idx,
                       const void* k_cache, const void* v_cache, const void* k_idx_cache,

@@ -35,7 +35,7 @@ def prefill_device_inputs(inp: syn.PrefillInputs, device="cuda"):
     return q, k, v, qi, ki
 
 
-def oracle_prefill(inp: syn.PrefillInputs, rows, topk, want_scores=False, kv_host=None, threads=16):
+def oracle_prefill(inp: syn.PrefillInputs, rows, topk, want_scores=False, kv_host=None, threads=16, scale=None):
     """Oracle on the given rows; inputs regenerated on the CPU from the seed
     (kv_host: optional pre-generated (k_idx, k, v) float64 arrays)."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -52,7 +52,7 @@ def oracle_prefill(inp: syn.PrefillInputs, rows, topk, want_scores=False, kv_hos
 
     def run(ix):
         r = mo.prefill_rows(rows[ix], q[ix], qi[ix], ki, k, v, block_size=bk, topk=topk,
-                            want_scores=want_scores)
+                            want_scores=want_scores, scale=scale)
         done[0] += len(ix)
         if len(rows) >= 1024:
             log(f"    oracle rows {done[0]}/{len(rows)} ({time.time() - t0:.0f}s)")

@@ -88,6 +88,10 @@ def test_decode_rejects_bad_args(lib):
     assert lib.msa_decode(ctypes.byref(p), 2, 4096, *args, None, ok, None, None, ok, need, None) == -1
     assert lib.msa_decode(ctypes.byref(p), 2, 4096, *args, ok, ok, None, None, ok, need - 1, None) == -3
     assert lib.msa_decode(ctypes.byref(p), 0, 4096, *args, ok, ok, None, None, ok, need, None) == -1
+    # contexts beyond the longest supported one (2^20 positions at B_k = 128)
+    assert lib.msa_decode_workspace_bytes(ctypes.byref(p), 2, (1 << 20) + 1) == 0
+    assert lib.msa_decode_workspace_bytes(ctypes.byref(p), 2, 1 << 20) > 0
+    assert lib.msa_decode(ctypes.byref(p), 2, (1 << 20) + 1, *args, ok, ok, None, None, ok, 1 << 40, None) == -2
     p.topk = 20
     assert lib.msa_decode(ctypes.byref(p), 2, 4096, *args, ok, ok, None, None, ok, need, None) == -2
 
@@ -120,6 +124,9 @@ def test_block_size_limits(lib, bk):
     # decode: the workspace holds one pooled score per block of the longest context
     d = msa.decode_workspace_bytes(p, 4, 8192)
     assert d >= 4 * 4 * (8192 // bk) * 4
+    assert msa.decode_workspace_bytes(p, 4, longest) > 0
+    assert msa.decode_workspace_bytes(p, 4, longest + 1) == 0
+    assert lib.msa_decode(ctypes.byref(p), 4, longest + 1, *[ok] * 7, None, None, ok, 1 << 40, None) == -2
     kl_need = lib.msa_index_kl_workspace_bytes(ctypes.byref(p), 4096)
     if bk == 128:
         assert kl_need > 0

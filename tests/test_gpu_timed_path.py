@@ -1,0 +1,125 @@
+"""GPU parity of the call path the benchmark times: no selection or lse
+output (the selection then lives in the workspace), a workspace and output
+reused across calls, several query windows, and a softmax scale other than
+1/sqrt(d). Every output is compared with the float64 oracle on the same seeded
+inputs (exact softmax over the selected blocks [yifor, 設計核心]).
+
+Bar as in tests/_parity.py: max-abs 2e-2, relative L2 5e-3 on the outputs,
+lse within 4e-3, selection bit-exact where it is requested.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_07_amd as msa
+import msa_synth as syn
+from oracle import msa_oracle as mo
+from tests._parity import compare_lse, compare_out, log, oracle_prefill, prefill_device_inputs, timed
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    msa.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def dims(G, topk, bk=128):
+    return syn.Dims(num_q_heads=16 * G, num_kv_heads=G, head_dim=128, index_dim=64, block_size=bk, topk=topk)
+
+
+@pytest.mark.timeout(900)
+def test_bench_call_sampled():
+    """The 32K workload called exactly as the benchmark's timed step calls it
+    (preallocated workspace and output, sel_out = lse_out = NULL), twice in a
+    row on the same workspace; the second call's output is checked."""
+    n, topk = 32768, 16
+    inp = syn.PrefillInputs(n, dims(4, topk), 0, "planted", n_planted=8)
+    log(f"case bench call: N={n}")
+    pre = prefill_device_inputs(inp)
+    p = msa.params(64, 4, 128, 64, 128, topk)
+    ws = torch.empty(msa.prefill_workspace_bytes(p, 1, n), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(pre[0])
+    with timed("gpu"):
+        for _ in range(2):
+            o, s, l = msa.prefill(*pre, topk=topk, workspace=ws, out=out)
+            assert s is None and l is None and o is out
+        torch.cuda.synchronize()
+    extra = sorted({b for g in inp.planted.values() for b in g})
+    rows = syn.stratified_rows(n, 4096, 128, 10, topk, extra=extra)
+    with timed("oracle"):
+        ref = oracle_prefill(inp, rows, topk)
+    compare_out(out[0][torch.as_tensor(rows, device="cuda")], ref["out"], "bench call out")
+
+
+@pytest.mark.timeout(1200)
+def test_multiwindow_without_selection_output_sampled():
+    """70000 rows: a full 65536-row window and a ragged second one, with the
+    selection kept in the workspace (no sel_out, no lse_out)."""
+    n, topk = 70000, 16
+    inp = syn.PrefillInputs(n, dims(4, topk), 11, "planted", n_planted=8)
+    log(f"case multi-window, no sel/lse: N={n}")
+    with timed("gpu"):
+        pre = prefill_device_inputs(inp)
+        out, s, l = msa.prefill(*pre, topk=topk)
+        assert s is None and l is None
+        torch.cuda.synchronize()
+    extra = sorted({b for g in inp.planted.values() for b in g})
+    edges = [65535, 65536, 65537, 65551, 65552, 65663, 65664, 69999]
+    rows = np.union1d(syn.stratified_rows(n, 4096, 128, 11, topk, extra=extra), edges)
+    got = out[0][torch.as_tensor(rows, device="cuda")].cpu()
+    del pre, out
+    with timed("oracle"):
+        ref = oracle_prefill(inp, rows, topk)
+    compare_out(got, ref["out"], "multi-window out")
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.25])
+@pytest.mark.parametrize("bk", [128, 32])
+def test_prefill_nondefault_scale_all_rows(scale, bk):
+    """A softmax scale other than 1/sqrt(128): a flat (0.03) and a sharp
+    (0.25, logits of tens) distribution, the latter exercising the lazy
+    rescale of the running softmax state; without and with the lse output."""
+    n, topk = 1500, 4
+    inp = syn.PrefillInputs(n, dims(2, topk, bk), 12, "tiny")
+    log(f"case scale {scale} B_k={bk}: N={n}")
+    pre = prefill_device_inputs(inp)
+    out0, _, _ = msa.prefill(*pre, topk=topk, block_size=bk, softmax_scale=scale)
+    out1, sel, lse = msa.prefill(*pre, topk=topk, block_size=bk, softmax_scale=scale, want_sel=True,
+                                 want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1), "the optional outputs change the attention output"
+    rows = np.arange(n)
+    ref = oracle_prefill(inp, rows, topk, scale=scale)
+    assert np.array_equal(sel[0].permute(1, 0, 2).cpu().numpy(), ref["sel"])
+    compare_out(out1[0], ref["out"], f"scale {scale} out")
+    compare_lse(lse[0], ref["lse"], f"scale {scale}")
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.25])
+def test_decode_nondefault_scale(scale):
+    B, L, topk = 5, 4000, 16
+    dec = syn.DecodeInputs(B, L, syn.Dims(), 13, ctx_lens=[4000, 3001, 2048, 129, 1])
+    dev = "cuda"
+    q = torch.stack([dec.q(b, dev) for b in range(B)]).contiguous()
+    qi = torch.stack([dec.q_idx(b, dev) for b in range(B)]).contiguous()
+    kc = torch.stack([dec.k_cache(b, device=dev) for b in range(B)]).contiguous()
+    vc = torch.stack([dec.v_cache(b, device=dev) for b in range(B)]).contiguous()
+    kic = torch.stack([dec.k_idx_cache(b, device=dev) for b in range(B)]).contiguous()
+    lens = torch.tensor(dec.ctx_lens, dtype=torch.int32, device=dev)
+    out, _, _ = msa.decode(q, qi, kc, vc, kic, lens, topk=topk, softmax_scale=scale)
+    _, sel, lse = msa.decode(q, qi, kc, vc, kic, lens, topk=topk, softmax_scale=scale, want_sel=True,
+                             want_lse=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        Lb = dec.ctx_lens[b]
+        ref = mo.decode_seq(mo.to_f64(dec.q(b)), mo.to_f64(dec.q_idx(b)), mo.to_f64(dec.k_idx_cache(b)),
+                            mo.to_f64(dec.k_cache(b)), mo.to_f64(dec.v_cache(b)), Lb, block_size=128, topk=topk,
+                            scale=scale)
+        assert np.array_equal(sel[b].cpu().numpy(), ref["sel"]), f"seq {b}"
+        compare_out(out[b], ref["out"], f"decode scale {scale} seq{b}")
+        compare_lse(lse[b], ref["lse"], f"decode scale {scale} seq{b}")
