@@ -11,10 +11,16 @@ F_main / t_prefill, where F_main = 4 * d * hpg * sum over (query, group) of the
 attended token count and t_prefill is the whole prefill call (index branch
 included). Decode KV GB/s (algorithmic bytes / whole decode call) is reported
 alongside, with per-stage times from the profiled entry points and the
-roofline of the dominant kernel. Side measurements (not part of a step):
-chunked and variable-length prefill, the Index Branch KL-alignment
-backward, prefill / decode at B_k 64 and 32, and the Index Branch
-projections from hidden states.
+roofline of the dominant kernel. The timed calls' own outputs (no selection
+or lse output, reused workspace) are checked against the float64 oracle on
+sampled prefill rows and 8 decode sequences (`parity`; the run exits with
+status 3 on a miss); the same oracle rows, timed on the host cores, are the
+`cpu_baseline`. Side measurements (not part of a step): cold-cache timings
+(after a 512 MiB write), measured ceilings (bf16 matmul, device copy), the
+top-k kernel beside torch.topk, chunked and variable-length prefill, the
+Index Branch KL-alignment backward, prefill / decode at B_k 64 and 32, the
+Index Branch projections from hidden states, and the long configurations
+(`configs`: 128K prefill with hot blocks, 1M prefill, 8 x 1M decode).
 """
 from __future__ import annotations
 
@@ -96,7 +102,7 @@ def decode_bytes(ctx_lens, topk=TOPK, bk=BK):
 DENSE_MIN = 7
 
 
-def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
+def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G, window=65536):
     """Split the selected (query, group, block) pairs of a prefill into the
     two attention passes, as the library does: a pair is "dense" when at least
     min(DENSE_MIN, rows of the unit) rows of its 16-row unit selected the block,
@@ -104,33 +110,42 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G):
     flops (4*d*hpg per attended key), the number of distinct (group, block) K/V
     blocks each pass touches, and the dense pass's (unit, block) count (it
     computes all 16 rows of a unit against each, masking those that did not
-    select it). sel: [G, n, k] int32 on the device (-1 = no selection)."""
+    select it). sel: [G, n, k] int32 on the device (-1 = no selection). Rows
+    are taken `window` at a time (a multiple of 16) to bound the memory."""
     ng, _, k = sel.shape
     dev = sel.device
     nb = (n + bk - 1) // bk
-    nunits = (n + 15) // 16
-    rows = torch.arange(n, device=dev)
-    unit_rows = torch.clamp(n - torch.arange(nunits, device=dev) * 16, max=16)
     st = {"dense_pairs": 0, "sparse_pairs": 0, "F_dense": 0.0, "F_sparse": 0.0, "kv_dense": 0, "kv_sparse": 0,
           "dense_unit_blocks": 0}
     for g in range(ng):
-        s = sel[g].long()
-        valid = s >= 0
-        rr = rows[:, None].expand(n, k)[valid]
-        bb = s[valid]
-        key = (rr // 16) * nb + bb
-        cnt = torch.bincount(key, minlength=nunits * nb).view(nunits, nb)
-        dense_ub = cnt >= torch.clamp(unit_rows, max=DENSE_MIN)[:, None]
-        dense = dense_ub.view(-1)[key]
-        st["dense_unit_blocks"] += int((dense_ub & (cnt > 0)).sum())
-        keys = torch.where(bb == rr // bk, rr % bk + 1, torch.full_like(rr, bk)).double()
-        fl = 4.0 * d * hpg * keys
-        st["F_dense"] += float(fl[dense].sum())
-        st["F_sparse"] += float(fl[~dense].sum())
-        st["dense_pairs"] += int(dense.sum())
-        st["sparse_pairs"] += int((~dense).sum())
-        st["kv_dense"] += int(torch.unique(bb[dense]).numel())
-        st["kv_sparse"] += int(torch.unique(bb[~dense]).numel())
+        used_d = torch.zeros(nb, dtype=torch.bool, device=dev)
+        used_s = torch.zeros(nb, dtype=torch.bool, device=dev)
+        for r0 in range(0, n, window):
+            r1 = min(n, r0 + window)
+            w = r1 - r0
+            nunits = (w + 15) // 16
+            rows = torch.arange(r0, r1, device=dev)
+            unit_rows = torch.clamp(w - torch.arange(nunits, device=dev) * 16, max=16)
+            s = sel[g, r0:r1].long()
+            valid = s >= 0
+            rr = rows[:, None].expand(w, k)[valid]
+            bb = s[valid]
+            key = ((rr - r0) // 16) * nb + bb
+            cnt = torch.bincount(key, minlength=nunits * nb).view(nunits, nb)
+            dense_ub = cnt >= torch.clamp(unit_rows, max=DENSE_MIN)[:, None]
+            dense = dense_ub.view(-1)[key]
+            st["dense_unit_blocks"] += int((dense_ub & (cnt > 0)).sum())
+            keys = torch.where(bb == rr // bk, rr % bk + 1, torch.full_like(rr, bk)).double()
+            fl = 4.0 * d * hpg * keys
+            st["F_dense"] += float(fl[dense].sum())
+            st["F_sparse"] += float(fl[~dense].sum())
+            st["dense_pairs"] += int(dense.sum())
+            st["sparse_pairs"] += int((~dense).sum())
+            used_d[bb[dense]] = True
+            used_s[bb[~dense]] = True
+            del s, valid, rr, bb, key, cnt, dense_ub, dense, keys, fl
+        st["kv_dense"] += int(used_d.sum())
+        st["kv_sparse"] += int(used_s.sum())
     return st
 
 
@@ -331,36 +346,296 @@ def make_inputs(torch, dev):
     return pin, pre, (q, qi, kc, vc, kic, lens), dec
 
 
-# ---- CPU baseline (the oracle) -------------------------------------------------
+# ---- CPU baseline (the oracle) and parity of the timed calls -----------------------
 
-def cpu_baseline(pin, budget_s=15.0):
-    from oracle import msa_oracle as mo
-    import msa_synth as syn
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas_threads = 1
+        return 1
+
+
+def _row_cost(rows, bk=BK, topk=TOPK):
+    """Per-row oracle work model: index scoring over b_loc(i) older blocks
+    plus attention over |T(i)| keys (both as flops)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    b_loc = rows // bk
+    t = bk * (np.minimum(topk, b_loc + 1) - 1) + rows % bk + 1
+    return 2.0 * DI * G * bk * b_loc + 4.0 * D * HQ * t
+
+
+def cpu_oracle(pin, rows, budget_s=15.0):
+    """The float64 oracle on as many of `rows` (in the given order) as fit in
+    the budget: half of it in one process with the default BLAS threads, half
+    in a pool of one-BLAS-thread workers over all host cores. Returns the
+    timing record and the oracle results of the rows done (for parity)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import msa_oracle as mo
+    cores = len(os.sched_getaffinity(0))
+    blas = _blas_threads()
     f = mo.to_f64
     t0 = time.time()
     ki, k, v = f(pin.k_idx()), f(pin.k()), f(pin.v())
     log(f"cpu_baseline: host inputs {time.time() - t0:.1f}s")
-    rows_all = syn.stratified_rows(N_PREFILL, 4096, BK, 0, TOPK)
-    rng = np.random.default_rng(1)
-    rng.shuffle(rows_all)
-    done, flops, spent = 0, 0.0, 0.0
     chunk = 16
-    while spent < budget_s and done < len(rows_all):
-        rows = np.sort(rows_all[done:done + chunk])
-        q, qi = f(pin.q(rows)), f(pin.q_idx(rows))
+    done_rows, sel, out = [], [], []
+
+    def run(rr):
+        q, qi = f(pin.q(rr)), f(pin.q_idx(rr))
+        return mo.prefill_rows(rr, q, qi, ki, k, v, block_size=BK, topk=TOPK)
+
+    # one process, default BLAS threads
+    single_flops, single_s, pos = 0.0, 0.0, 0
+    while single_s < budget_s / 2 and pos < len(rows):
+        rr = np.sort(rows[pos:pos + chunk])
         t = time.time()
-        mo.prefill_rows(rows, q, qi, ki, k, v, block_size=BK, topk=TOPK)
-        spent += time.time() - t
-        flops += prefill_flops(rows)
-        done += len(rows)
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{done} random rows of the 32768-token prefill workload (selection + attention, "
-                      f"float64 numpy), {spent:.1f}s of oracle time"}
+        r = run(rr)
+        single_s += time.time() - t
+        single_flops += prefill_flops(rr)
+        done_rows.append(rr), sel.append(r["sel"]), out.append(r["out"])
+        pos += len(rr)
+    # pool over all cores, one BLAS thread each
+    pool_flops, pool_s = 0.0, 0.0
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limit = None
+    try:
+        with ThreadPoolExecutor(cores) as ex:
+            while pool_s < budget_s / 2 and pos < len(rows):
+                batch = [np.sort(rows[p:p + chunk]) for p in range(pos, min(len(rows), pos + chunk * cores), chunk)]
+                t = time.time()
+                res = list(ex.map(run, batch))
+                pool_s += time.time() - t
+                for rr, r in zip(batch, res):
+                    pool_flops += prefill_flops(rr)
+                    done_rows.append(rr), sel.append(r["sel"]), out.append(r["out"])
+                pos += sum(len(rr) for rr in batch)
+    finally:
+        if limit is not None:
+            limit.unregister()
+    rows_done = np.concatenate(done_rows)
+    # extrapolation of the full 32K prefill from the per-row work model
+    all_rows = np.arange(N_PREFILL)
+    scale = _row_cost(all_rows).sum() / _row_cost(rows_done).sum()
+    pool_rate = pool_flops / pool_s if pool_s > 0 else 0.0
+    rec = {"value": (pool_rate or single_flops / max(single_s, 1e-9)) / 1e12, "unit": "TFLOP/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"{len(rows_done)} stratified random rows of the 32768-token prefill workload (selection + "
+                     f"attention, float64 numpy); value from the pool leg",
+           "blas_threads": blas,
+           "single_process": {"s": round(single_s, 2), "tflops": round(single_flops / max(single_s, 1e-9) / 1e12, 5)},
+           "pool": {"workers": cores, "s": round(pool_s, 2), "tflops": round(pool_rate / 1e12, 5)},
+           "extrapolated_full_prefill_s": round((single_s + pool_s) * scale, 1),
+           "extrapolated_note": "extrapolated: sample time x (work model of all 32768 rows / of the sampled rows)"}
+    return rec, rows_done, np.concatenate(sel), np.concatenate(out)
+
+
+def prefill_parity(torch, got_sel, got_out, ref_sel, ref_out):
+    """Bit-exact selection and max-abs / relative-L2 output error against the
+    oracle on the same rows (bar: 2e-2 / 5e-3)."""
+    g = got_out.astype(np.float64)
+    diff = g - ref_out
+    max_abs = float(np.abs(diff).max())
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref_out), 1e-30))
+    sel_exact = bool(np.array_equal(got_sel, ref_sel))
+    return {"rows": int(ref_out.shape[0]), "sel_exact": sel_exact, "max_abs": max_abs, "rel_l2": rel,
+            "ok": sel_exact and max_abs <= 2e-2 and rel <= 5e-3}
+
+
+def decode_parity(torch, dec, dec_in, out_d, seqs):
+    """The timed decode call's outputs for `seqs` against the oracle (caches
+    read row-wise from the device; q, q_idx regenerated on the host)."""
+    from oracle import msa_oracle as mo
+    q, qi, kc, vc, kic, lens = dec_in
+
+    class Rows:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, idx):
+            if isinstance(idx, tuple):
+                idx = tuple(torch.as_tensor(np.asarray(i), device=self.t.device)
+                            if not isinstance(i, (int, slice)) else i for i in idx)
+            elif not isinstance(idx, (int, slice)):
+                idx = torch.as_tensor(np.asarray(idx), device=self.t.device)
+            return mo.to_f64(self.t[idx])
+
+    import block_sparse_long_07_amd as msa
+    _, sel_all, _ = msa.decode(q, qi, kc, vc, kic, lens, topk=TOPK, want_sel=True)
+    max_abs, num, den, sel_exact = 0.0, 0.0, 0.0, True
+    for b in seqs:
+        L = dec.ctx_lens[b]
+        ref = mo.decode_seq(mo.to_f64(dec.q(b)), mo.to_f64(dec.q_idx(b)), mo.to_f64(kic[b, :L]), Rows(kc[b]),
+                            Rows(vc[b]), L, block_size=BK, topk=TOPK)
+        got = out_d[b].double().cpu().numpy()
+        d = got - ref["out"]
+        max_abs = max(max_abs, float(np.abs(d).max()))
+        num += float((d ** 2).sum())
+        den += float((ref["out"] ** 2).sum())
+        sel_exact &= bool(np.array_equal(sel_all[b].cpu().numpy(), ref["sel"]))
+    rel = (num / max(den, 1e-30)) ** 0.5
+    return {"seqs": len(seqs), "sel_exact": sel_exact, "max_abs": max_abs, "rel_l2": rel,
+            "ok": sel_exact and max_abs <= 2e-2 and rel <= 5e-3}
+
+
+# ---- context measurements ------------------------------------------------------
+
+def ceilings(torch, reps=10):
+    """Measured ceilings on this GPU: a bf16 torch.matmul (8192^3) and a 1 GiB
+    device copy (1 GiB read + 1 GiB written)."""
+    dev = torch.device("cuda:0")
+    a = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev).to(torch.bfloat16).t().contiguous()
+    ms = _time_calls(torch, lambda: torch.matmul(a, b), reps)
+    mm = 2.0 * 8192 ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    src = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    ms = _time_calls(torch, lambda: dst.copy_(src), reps)
+    cp = 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
+    del src, dst
+    return {"matmul_bf16_tflops": round(mm, 1), "matmul_frac_of_peak": round(mm / MFMA_PEAK_TFLOPS, 3),
+            "copy_GB/s": round(cp, 1), "copy_frac_of_peak": round(cp / HBM_PEAK_GBS, 3)}
+
+
+def topk_context(torch, msa, pre, reps):
+    """The pages compare their top-k kernel with a generic top-k (3-5x). Here:
+    msa_select_blocks against torch.topk (k-1 of the older blocks, the others
+    masked to -inf beforehand, untimed) on the same pooled scores of the bench
+    prefill. Context only: torch.topk neither forces the own block nor fixes
+    the order of ties."""
+    q, k, v, qi, ki = (t[0] for t in pre)
+    n = qi.shape[0]
+    sc = msa.index_scores(qi, ki, topk=TOPK)
+    nb = sc.shape[-1]
+    rows = torch.arange(n, device=sc.device)
+    valid = torch.arange(nb, device=sc.device)[None, :] < (rows // BK)[:, None]
+    masked = torch.where(valid[:, None, :], sc, torch.full_like(sc, float("-inf")))
+    sel = torch.empty((G, n, TOPK), dtype=torch.int32, device=sc.device)
+    ms_msa = _time_calls(torch, lambda: msa.select_blocks(sc, topk=TOPK, sel=sel), reps)
+    ms_t = _time_calls(torch, lambda: torch.topk(masked, TOPK - 1, dim=-1), reps)
+    del sc, masked, sel, valid
+    return {"msa_topk_ms": round(ms_msa, 4), "torch_topk_ms": round(ms_t, 4),
+            "torch_over_msa": round(ms_t / ms_msa, 2), "rows": n * G, "candidates_max": nb}
+
+
+def _flush(torch, buf):
+    buf.zero_()
+
+
+def time_cold(torch, fn, reps, flush_bytes=512 << 20):
+    """Mean time of fn after writing a 512 MiB buffer (evicts the 256 MB
+    last-level cache and the L2s), events around fn only."""
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    ts = []
+    for _ in range(reps):
+        _flush(torch, buf)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del buf
+    return float(np.mean(ts))
+
+
+# ---- the longer configurations ------------------------------------------------------
+
+def config_prefill(torch, msa, label, inp, reps):
+    """One prefill configuration: warm (mean of reps) and cold timings, the
+    per-stage times, the attention kernels' roofline positions from the actual
+    selection, and the index stage's rate."""
+    dev = torch.device("cuda:0")
+    n = inp.n
+    t0 = time.time()
+    pre = [fn(device=dev)[None].contiguous() for fn in (inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx)]
+    torch.cuda.synchronize()
+    log(f"{label}: inputs ready in {time.time() - t0:.1f}s")
+    p = msa.params(HQ, G, D, DI, BK, TOPK)
+    ws = torch.empty(msa.prefill_workspace_bytes(p, 1, n), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(pre[0])
+    run = lambda: msa.prefill(*pre, topk=TOPK, workspace=ws, out=out)
+    ms = _time_calls(torch, run, reps)
+    ms_cold = time_cold(torch, run, max(2, reps // 2))
+    x = []
+    msa.prefill(*pre, topk=TOPK, workspace=ws, out=out, stage_ms=x)
+    stage = dict(zip(msa.PREFILL_STAGES, (float(v) for v in x)))
+    _, sel, _ = msa.prefill(*pre, topk=TOPK, workspace=ws, out=out, want_sel=True)
+    del ws, out, pre
+    torch.cuda.empty_cache()
+    ps, kernels = attention_rooflines(torch, sel[0], n, stage, measured=False)
+    del sel
+    torch.cuda.empty_cache()
+    f_main, f_idx = prefill_flops_full(n), index_flops_full(n)
+    dom = max(kernels, key=lambda r: r["ms"])
+    log(f"{label}: {ms:.2f} ms warm, {ms_cold:.2f} ms cold")
+    return {"workload": label, "ms": round(ms, 3), "ms_cold": round(ms_cold, 3),
+            "F_main_tflop": round(f_main / 1e12, 3), "F_idx_tflop": round(f_idx / 1e12, 3),
+            "tflops": round(f_main / (ms * 1e-3) / 1e12, 2),
+            "end_to_end_tflops": round((f_main + f_idx) / (ms * 1e-3) / 1e12, 2),
+            "index_tflops": round(f_idx / (stage["index_score"] * 1e-3) / 1e12, 2),
+            "stage_ms": {k: round(v, 3) for k, v in stage.items()},
+            "roofline": {k: dom[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "traffic")},
+            "kernels": kernels,
+            "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse",
+                                         "dense_unit_blocks")}}
+
+
+def config_decode(torch, msa, label, B, L, seed, reps):
+    dev = torch.device("cuda:0")
+    import msa_synth as syn
+    dims = syn.Dims()
+    t0 = time.time()
+    dec = syn.DecodeInputs(B, L, dims, seed)
+    q = torch.stack([dec.q(b, dev) for b in range(B)]).contiguous()
+    qi = torch.stack([dec.q_idx(b, dev) for b in range(B)]).contiguous()
+    kc = torch.empty((B, L, G, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    kic = torch.empty((B, L, DI), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        kc[b] = dec.k_cache(b, device=dev)
+        vc[b] = dec.v_cache(b, device=dev)
+        kic[b] = dec.k_idx_cache(b, device=dev)
+    lens = torch.tensor(dec.ctx_lens, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"{label}: inputs ready in {time.time() - t0:.1f}s")
+    p = msa.params(HQ, G, D, DI, BK, TOPK)
+    ws = torch.empty(msa.decode_workspace_bytes(p, B, L), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    run = lambda: msa.decode(q, qi, kc, vc, kic, lens, topk=TOPK, workspace=ws, out=out)
+    ms = _time_calls(torch, run, reps)
+    ms_cold = time_cold(torch, run, max(2, reps // 2))
+    x = []
+    msa.decode(q, qi, kc, vc, kic, lens, topk=TOPK, workspace=ws, out=out, stage_ms=x)
+    db = decode_bytes(dec.ctx_lens)
+    gbs = db / (ms * 1e-3) / 1e9
+    del q, qi, kc, vc, kic, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": label, "ms": round(ms, 4), "ms_cold": round(ms_cold, 4), "bytes_gb": round(db / 1e9, 4),
+            "GB/s": round(gbs, 1), "GB/s_cold": round(db / (ms_cold * 1e-3) / 1e9, 1),
+            "roofline": {"kernel": "decode (index + select + attention + combine)", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "stage_ms": {k: round(float(v), 4) for k, v in zip(msa.DECODE_STAGES, x)}}
+
+
+def long_configs(torch, msa, reps):
+    """The long-context configurations: the 128K prefill with hot blocks
+    shared by most queries, the 1M-token prefill, and decode of 8 sequences
+    with 1M-token caches."""
+    import msa_synth as syn
+    res = []
+    inp = syn.PrefillInputs(131072, syn.Dims(), 3, "skewed", n_planted=4, n_hot=4)
+    res.append(config_prefill(torch, msa, "prefill N=131072, skewed (4 hot blocks shared by all groups)", inp, reps))
+    inp = syn.PrefillInputs(1 << 20, syn.Dims(), 4, "planted", n_planted=8)
+    res.append(config_prefill(torch, msa, "prefill N=1048576", inp, max(2, reps // 4)))
+    res.append(config_decode(torch, msa, "decode 8 x 1048576", 8, 1 << 20, 5, reps))
+    return res
 
 
 # ---- serving shapes (msa_prefill_varlen) --------------------------------------
@@ -466,6 +741,11 @@ def main():
                     help="skip the chunked / variable-length prefill, KL-backward, B_k 64 / 32 and projection "
                          "measurements "
                          "(profiling runs use this so that per-kernel averages cover the headline workload only)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the long configurations (128K skewed prefill, 1M prefill, 8 x 1M decode) and the "
+                         "context measurements (ceilings, top-k comparison)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle check of the timed calls' outputs (profiling runs)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
@@ -519,6 +799,14 @@ def main():
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     step_ms = wall * 1e3 / args.steps
 
+    # the timed calls' own outputs, kept for the oracle comparison below
+    import msa_synth as syn
+    planted = sorted({b for g in pin.planted.values() for b in g})
+    par_rows = syn.stratified_rows(N_PREFILL, 4096, BK, 0, TOPK, extra=planted)
+    np.random.default_rng(1).shuffle(par_rows)
+    timed_out_rows = out_p[0][torch.as_tensor(par_rows, device=dev)].float().cpu().numpy()
+    timed_out_d = out_d.clone()
+
     # per-stage times (profiled entry points: HIP events on the launch stream)
     pst, dst = [], []
     for _ in range(args.profile_reps):
@@ -543,15 +831,33 @@ def main():
     # roofline of the two attention kernels from the actual selection
     _, sel, _ = msa.prefill(*pre, topk=TOPK, workspace=ws_p, out=out_p, want_sel=True)
     ps, kernels = attention_rooflines(torch, sel[0], N_PREFILL, stage)
+    par_sel = sel[0][:, torch.as_tensor(par_rows, device=dev)].permute(1, 0, 2).cpu().numpy()
     del sel
     assert abs(ps["F_dense"] + ps["F_sparse"] - f_main) <= 1e-9 * f_main, "pair split does not cover F_main"
     dom = max(kernels, key=lambda r: r["ms"])
+
+    cold = {"prefill_ms": round(time_cold(torch, lambda: msa.prefill(*pre, topk=TOPK, workspace=ws_p, out=out_p),
+                                          args.profile_reps), 4),
+            "decode_ms": round(time_cold(torch, lambda: msa.decode(*dec_in, topk=TOPK, workspace=ws_d, out=out_d),
+                                         args.profile_reps), 4)}
+    cold["prefill_tflops"] = round(prefill_flops_full(N_PREFILL) / (cold["prefill_ms"] * 1e-3) / 1e12, 2)
+    cold["decode_GB/s"] = round(decode_bytes(dec.ctx_lens) / (cold["decode_ms"] * 1e-3) / 1e9, 1)
+    context = None
+    if not args.no_configs:
+        context = {"ceilings": ceilings(torch), "topk": topk_context(torch, msa, pre, args.steps)}
 
     chunked, varlen = (None, None) if args.no_serving else serving_shapes(torch, msa, pre, TOPK, args.steps)
     kl = None if args.no_serving else kl_backward_measure(torch, msa, pre, TOPK, args.steps)
     variants = (None if args.no_serving else
                 block_size_variants(torch, msa, pre, dec_in, dec.ctx_lens, TOPK, args.steps))
     proj = None if args.no_serving else projection_measure(torch, msa, N_PREFILL, DEC_B, args.steps)
+
+    parity = None
+    if not args.no_parity:
+        dpar = decode_parity(torch, dec, dec_in, timed_out_d, [0, 9, 18, 27, 36, 45, 54, 63])
+    del ws_p, ws_d, out_p, out_d, timed_out_d, pre, dec_in
+    torch.cuda.empty_cache()
+    configs = None if args.no_configs else long_configs(torch, msa, args.steps)
 
     res = {
         "metric": METRIC,
@@ -591,12 +897,27 @@ def main():
         "index_kl_backward": kl,
         "block_size_variants": variants,
         "index_projection": proj,
+        "cold_cache": cold,
+        "context": context,
+        "configs": configs,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(pin, args.cpu_budget)
+    if not (args.no_parity and args.no_cpu_baseline):
+        rec, rows_done, ref_sel, ref_out = cpu_oracle(pin, par_rows, args.cpu_budget)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = rec
+        if not args.no_parity:
+            pos = {int(r): i for i, r in enumerate(par_rows)}
+            ix = np.array([pos[int(r)] for r in rows_done])
+            ppar = prefill_parity(torch, par_sel[ix], timed_out_rows[ix], ref_sel, ref_out)
+            parity = {"prefill": ppar, "decode": dpar,
+                      "bar": "selection bit-exact; max-abs <= 2e-2, rel-L2 <= 5e-3 vs the float64 oracle",
+                      "what": "outputs of the timed calls themselves (no selection / lse output, reused workspace)"}
+            res["parity"] = parity
     print(json.dumps(res), flush=True)
+    if parity is not None and not (parity["prefill"]["ok"] and parity["decode"]["ok"]):
+        print("parity check of the timed calls failed", file=sys.stderr)
+        sys.exit(3)
     if args.calibration_copy:
-        del ws_p, ws_d
         src = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
         dst = torch.neg(src)
         torch.cuda.synchronize()
