@@ -23,12 +23,24 @@ namespace msa {
 // (global_load_lds, double-buffered) and read as MFMA operands by all waves.
 // LDS layout: 128 rows of 128 B; 16-byte chunk x of row r sits at chunk
 // position x ^ ((r >> 1) & 7), which keeps the operand reads conflict-free.
-// Key blocks per workgroup: two 128-key stages at B_k = 128, one stage
-// otherwise. Short workgroups spread the causal triangle's uneven work over
-// the whole chip: chunks of 4 and 8 blocks measured 1.05x and 1.3x slower at
-// B_k = 128, 16 slower still.
-template <int SUB>
-constexpr int chunk_blocks() { return SUB == 1 ? 2 : SUB; }
+// Key blocks per workgroup (NSTG 128-key stages at B_k = 128, one stage
+// otherwise): short workgroups spread the causal triangle's uneven work over
+// the chip when there are few query blocks (at 32K, chunks of 4 and 8 blocks
+// measured 1.05x and 1.3x slower than 2); long sequences have work for
+// millions of workgroups, and longer chunks load each workgroup's 64 KiB of
+// index queries once for more key blocks.
+//
+// Workgroups form a 1-D grid over the causal triangle only: query block q
+// holds st(q) = q (+1 when B_k < 128: its own stage) stages, cut into
+// ceil(st(q) / NS) chunks, and workgroup w finds its (q, chunk) from the
+// closed-form count of the chunks before q.
+__host__ __device__ __forceinline__ int64_t chunks_before(int64_t x, int ns) {
+  // sum over q < x of ceil(q / ns)
+  const int64_t a = x / ns, r = x % ns;
+  int64_t s = ns * a * (a - 1) / 2 + a * (ns - 1);
+  if (r > 0) s += a + (r - 1) * (a + 1);
+  return s;
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -51,21 +63,32 @@ __device__ __forceinline__ void stage_kidx(lds_char* dst, const uint16_t* src_ro
 // pooled scores per row, from its key tiles s*8/SUB .. (s+1)*8/SUB - 1. With
 // SUB > 1 a query block's own stage also holds blocks older than some of its
 // rows, so it is scored too; every row writes only its blocks b < b_loc.
-template <int G, int SUB>
+template <int G, int SUB, int NSTG>
 __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __restrict__ q_idx,
                                                           const uint16_t* __restrict__ k_idx,
                                                           float* __restrict__ sblk, int64_t row0,
-                                                          int64_t row_end, int qb_begin, int nb) {
+                                                          int64_t row_end, int qb_begin, int qb_end, int nb) {
   constexpr int RT = 2 * G;        // 16-row tiles per wave
-  constexpr int KC = chunk_blocks<SUB>();  // blocks per chunk
-  constexpr int NS = KC / SUB;            // 128-key stages per chunk
+  constexpr int NS = SUB == 1 ? NSTG : 1;  // 128-key stages per chunk
+  constexpr int KC = NS * SUB;             // blocks per chunk
   constexpr int TPB = 8 / SUB;     // key tiles per block
   constexpr int BKS = kBlock / SUB;
+  constexpr int ADD = SUB > 1 ? 1 : 0;     // st(q) = q + ADD
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * 16384];
   lds_char* lds = (lds_char*)lds_raw;
-  const int qb = qb_begin + (int)blockIdx.y;
+  // (query block, chunk) of this workgroup: the largest qb with
+  // chunks_before(qb + ADD) - chunks_before(qb_begin + ADD) <= w
+  const int64_t w = (int64_t)blockIdx.x;
+  const int64_t base = chunks_before(qb_begin + ADD, NS);
+  int lo = qb_begin, hi = qb_end - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunks_before(mid + ADD, NS) - base <= w) lo = mid; else hi = mid - 1;
+  }
+  const int qb = __builtin_amdgcn_readfirstlane(lo);
+  const int chunk = (int)__builtin_amdgcn_readfirstlane((int)(w - (chunks_before(qb + ADD, NS) - base)));
   const int last = SUB > 1 ? qb : qb - 1;  // last stage holding a block older than some row
-  const int kb0 = (int)blockIdx.x * NS;
+  const int kb0 = chunk * NS;
   if (kb0 > last) return;
   const int kb1 = min(kb0 + NS, last + 1);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -243,17 +266,34 @@ __global__ __launch_bounds__(256) void k_index_decode(const uint16_t* __restrict
   }
 }
 
+template <int G, int SUB, int NSTG>
+static void launch_prefill_ns(const LaunchIndexPrefill& a, hipStream_t st) {
+  constexpr int NS = SUB == 1 ? NSTG : 1;
+  constexpr int ADD = SUB > 1 ? 1 : 0;
+  const int64_t wgs = chunks_before(a.qb_end + ADD, NS) - chunks_before(a.qb_begin + ADD, NS);
+  if (wgs <= 0) return;
+  hipLaunchKernelGGL((k_index_prefill<G, SUB, NSTG>), dim3((unsigned)wgs), dim3(256), 0, st, a.q_idx, a.k_idx,
+                     a.sblk, a.row0, a.row_end, a.qb_begin, a.qb_end, a.nb);
+}
+
+// Chunk length: two stages unless that makes more than kManyChunks
+// workgroups, then 8 or 16.
+constexpr int64_t kManyChunks = 1 << 16;
+
 template <int G, int SUB>
 static void launch_prefill_g(const LaunchIndexPrefill& a, hipStream_t st) {
-  const int n_qb = a.qb_end - a.qb_begin;
-  if (n_qb <= 0) return;
-  constexpr int NS = chunk_blocks<SUB>() / SUB;
-  const int stages = SUB > 1 ? a.qb_end : a.qb_end - 1;  // stages of the last query block
-  const int chunks = (stages + NS - 1) / NS;
-  if (chunks <= 0) return;
-  dim3 grid(chunks, n_qb);
-  hipLaunchKernelGGL((k_index_prefill<G, SUB>), grid, dim3(256), 0, st, a.q_idx, a.k_idx, a.sblk, a.row0,
-                     a.row_end, a.qb_begin, a.nb);
+  if (a.qb_end <= a.qb_begin) return;
+  if constexpr (SUB > 1) {
+    launch_prefill_ns<G, SUB, 1>(a, st);
+  } else {
+    const int64_t w2 = chunks_before(a.qb_end, 2) - chunks_before(a.qb_begin, 2);
+    if (w2 <= kManyChunks)
+      launch_prefill_ns<G, SUB, 2>(a, st);
+    else if (w2 <= 8 * kManyChunks)
+      launch_prefill_ns<G, SUB, 8>(a, st);
+    else
+      launch_prefill_ns<G, SUB, 16>(a, st);
+  }
 }
 
 template <int SUB>
