@@ -24,7 +24,7 @@ EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_prefill_varlen_wo
             "msa_prefill_varlen", "msa_decode_workspace_bytes", "msa_decode", "msa_prefill_profiled",
             "msa_decode_profiled", "msa_index_kl_workspace_bytes", "msa_index_kl_backward", "msa_index_scores",
             "msa_select_blocks", "msa_status_string", "msa_index_project_workspace_bytes", "msa_index_project",
-            "msa_index_project_decode")
+            "msa_index_project_decode", "msa_decode_noalloc")
 PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
 DECODE_STAGES = ("index_score", "select", "attn", "combine")
 
@@ -68,6 +68,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_decode_workspace_bytes.restype = sz
     lib.msa_decode.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode.restype = ctypes.c_int
+    lib.msa_decode_noalloc.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.msa_decode_noalloc.restype = ctypes.c_int
     fp = ctypes.POINTER(ctypes.c_float)
     lib.msa_prefill_profiled.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, fp]
     lib.msa_prefill_profiled.restype = ctypes.c_int
@@ -245,6 +247,30 @@ def decode(q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, *, topk=16, block_
         ms = (ctypes.c_float * len(DECODE_STAGES))()
         _check(lib.msa_decode_profiled(*args, ms), "msa_decode_profiled")
         stage_ms.extend(float(x) for x in ms)
+    return out, sel, lse
+
+
+def decode_noalloc(q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, *, topk=16, block_size=128,
+                   softmax_scale=None, want_sel=False, want_lse=False, out: Optional[torch.Tensor] = None):
+    """msa_decode_noalloc: one decode step with the library's own fixed device
+    workspace (no workspace argument; the library allocates nothing). Same
+    arguments and results as decode()."""
+    lib = load()
+    B, Hq, d = q.shape
+    max_ctx, G = k_cache.shape[1], k_cache.shape[2]
+    for t, name in ((q, "q"), (q_idx, "q_idx"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                    (k_idx_cache, "k_idx_cache")):
+        _need(t, torch.bfloat16, name)
+    _need(ctx_lens, torch.int32, "ctx_lens")
+    p = params(Hq, G, d, q_idx.shape[-1], block_size, topk, softmax_scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    sel = torch.empty((B, G, topk), dtype=torch.int32, device=dev) if want_sel else None
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    _check(lib.msa_decode_noalloc(ctypes.byref(p), B, max_ctx, _ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(k_idx_cache), _ptr(ctx_lens), _ptr(out), _ptr(sel), _ptr(lse),
+                                  _stream(dev)), "msa_decode_noalloc")
     return out, sel, lse
 
 

@@ -17,6 +17,7 @@
 #include <cstdint>
 #include <vector>
 
+#include "api_internal.h"
 #include "msa.h"
 #include "msa_launch.h"
 
@@ -512,25 +513,46 @@ size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t ma
 
 }  // extern "C"
 
+namespace msa {
+
+// Host-side checks of a decode call, everything but the workspace; *need gets
+// the workspace bytes the call takes.
+msa_status decode_check(const msa_params* p, int32_t batch, int64_t max_ctx, const void* q, const void* q_idx,
+                        const void* k_cache, const void* v_cache, const void* k_idx_cache, const int32_t* ctx_lens,
+                        const void* out, const int32_t* sel_out, const float* lse_out, size_t* need) {
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  if (batch <= 0 || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
+  if (max_ctx > s.max_seq) return MSA_ERR_UNSUPPORTED;
+  for (const void* ptr : {q, q_idx, k_cache, v_cache, k_idx_cache, out})
+    if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
+  if (!ctx_lens || !aligned(ctx_lens, 4)) return MSA_ERR_INVALID_ARG;
+  if ((sel_out && !aligned(sel_out, 4)) || (lse_out && !aligned(lse_out, 4))) return MSA_ERR_INVALID_ARG;
+  DecodeLayout L;
+  if (!decode_layout(s, batch, max_ctx, &L)) return MSA_ERR_INVALID_ARG;
+  *need = L.total;
+  return MSA_OK;
+}
+
+}  // namespace msa
+
 namespace {
 
 msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const void* q, const void* q_idx,
                       const void* k_cache, const void* v_cache, const void* k_idx_cache,
                       const int32_t* ctx_lens, void* out, int32_t* sel_out, float* lse_out, void* workspace,
                       size_t workspace_bytes, void* stream, std::vector<hipEvent_t>* ev) {
-  Shape s;
-  msa_status st = check_params(p, &s);
+  size_t need = 0;
+  msa_status st = msa::decode_check(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out,
+                               lse_out, &need);
   if (st != MSA_OK) return st;
-  if (batch <= 0 || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
-  if (max_ctx > s.max_seq) return MSA_ERR_UNSUPPORTED;
-  for (const void* ptr : {q, q_idx, k_cache, v_cache, k_idx_cache, (const void*)out})
-    if (!ptr || !aligned(ptr, 16)) return MSA_ERR_INVALID_ARG;
-  if (!ctx_lens || !aligned(ctx_lens, 4)) return MSA_ERR_INVALID_ARG;
-  if ((sel_out && !aligned(sel_out, 4)) || (lse_out && !aligned(lse_out, 4))) return MSA_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  Shape s;
+  check_params(p, &s);
   DecodeLayout L;
-  if (!decode_layout(s, batch, max_ctx, &L)) return MSA_ERR_INVALID_ARG;
-  if (workspace_bytes < L.total) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  decode_layout(s, batch, max_ctx, &L);
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();

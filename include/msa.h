@@ -161,6 +161,24 @@ msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx,
                       void* out, int32_t* sel_out, float* lse_out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Decode without allocation -------------------------------------------
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): msa_decode with
+ * the same arguments minus the workspace, which comes from a fixed device
+ * array of MSA_DECODE_NOALLOC_WORKSPACE_BYTES that the library holds on each
+ * device it runs on (from the first call there until the process ends). A
+ * call whose msa_decode_workspace_bytes exceeds it returns
+ * MSA_ERR_UNSUPPORTED (64 sequences at 128K positions take 17.3 MiB, 8 at
+ * 1M 3.3 MiB). Calls on one device share the array: calls that overlap in
+ * time on one device race (serialise them on one stream). The results are
+ * those of msa_decode: the same kernels run. */
+#define MSA_DECODE_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+msa_status msa_decode_noalloc(const msa_params* p, int32_t batch, int64_t max_ctx,
+                              const void* q, const void* q_idx,
+                              const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                              const int32_t* ctx_lens,
+                              void* out, int32_t* sel_out, float* lse_out, void* stream);
+
 /* ---- Profiling variants -------------------------------------------------
  * Same work and arguments as msa_prefill / msa_decode, plus HIP events recorded
  * on `stream` at every stage boundary. They synchronise on the last event and

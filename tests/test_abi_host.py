@@ -96,6 +96,23 @@ def test_decode_rejects_bad_args(lib):
     assert lib.msa_decode(ctypes.byref(p), 2, 4096, *args, ok, ok, None, None, ok, need, None) == -2
 
 
+def test_decode_noalloc_rejects_before_touching_the_device(lib):
+    """The allocation-free decode validates on the host like msa_decode and
+    refuses calls whose workspace exceeds its fixed array; none of these
+    reaches the device."""
+    p = msa.params()
+    ok = ctypes.c_void_p(1 << 20)
+    f = lib.msa_decode_noalloc
+    assert f(ctypes.byref(p), 2, 4096, None, *[ok] * 6, None, None, None) == -1        # no q
+    assert f(ctypes.byref(p), 0, 4096, *[ok] * 7, None, None, None) == -1              # no sequences
+    assert f(ctypes.byref(p), 2, (1 << 20) + 1, *[ok] * 7, None, None, None) == -2     # context too long
+    need = lib.msa_decode_workspace_bytes(ctypes.byref(p), 256, 131072)
+    assert need > (32 << 20)
+    assert f(ctypes.byref(p), 256, 131072, *[ok] * 7, None, None, None) == -2          # beyond the array
+    p.topk = 20
+    assert f(ctypes.byref(p), 2, 4096, *[ok] * 7, None, None, None) == -2
+
+
 def test_stage_entry_points_reject_bad_args(lib):
     p = msa.params()
     ok = ctypes.c_void_p(1 << 20)

@@ -1,0 +1,68 @@
+"""msa_decode_noalloc (the decode step with the library's fixed device
+workspace, for callers that cannot allocate) against msa_decode on the same
+inputs, through the C ABI: two calls in a row, the second with a smaller
+input (it runs on what the first left in the shared array). The same kernels
+run, so outputs, selections and lse must be identical."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_07_amd as msa
+import msa_synth as syn
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    msa.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _inputs(B, L, seed, lens):
+    dec = syn.DecodeInputs(B, L, syn.Dims(), seed, ctx_lens=lens)
+    dev = "cuda"
+    q = torch.stack([dec.q(b, dev) for b in range(B)]).contiguous()
+    qi = torch.stack([dec.q_idx(b, dev) for b in range(B)]).contiguous()
+    kc = torch.stack([dec.k_cache(b, device=dev) for b in range(B)]).contiguous()
+    vc = torch.stack([dec.v_cache(b, device=dev) for b in range(B)]).contiguous()
+    kic = torch.stack([dec.k_idx_cache(b, device=dev) for b in range(B)]).contiguous()
+    ctx = torch.tensor(dec.ctx_lens, dtype=torch.int32, device=dev)
+    return q, qi, kc, vc, kic, ctx
+
+
+def test_noalloc_decode_matches_decode_twice():
+    cases = [(16, 20000, 21, [20000, 19999, 12345, 8193, 4096, 4095, 2048, 2047, 1920, 1919, 300, 129, 128, 17, 2, 1]),
+             (3, 5000, 22, [5000, 2049, 640])]
+    for B, L, seed, lens in cases:
+        print(f"case noalloc decode B={B} L={L}", flush=True)
+        args = _inputs(B, L, seed, lens)
+        ref_out, ref_sel, ref_lse = msa.decode(*args, topk=16, want_sel=True, want_lse=True)
+        out, sel, lse = msa.decode_noalloc(*args, topk=16, want_sel=True, want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, ref_sel)
+        assert torch.equal(out, ref_out)
+        assert torch.equal(lse, ref_lse)
+        # (implies the parity bar: max-abs 2e-2, rel-L2 5e-3 against the same reference)
+        d = (out.double() - ref_out.double()).abs().max().item()
+        assert d <= 2e-2
+
+
+def test_noalloc_rejects_workspace_beyond_its_array():
+    p = msa.params()
+    need = msa.decode_workspace_bytes(p, 256, 131072)
+    assert need > (32 << 20)
+    q = torch.empty((256, 64, 128), dtype=torch.bfloat16, device="cuda")
+    qi = torch.empty((256, 4, 64), dtype=torch.bfloat16, device="cuda")
+    kc = torch.empty((256, 1, 4, 128), dtype=torch.bfloat16, device="cuda")  # never read: rejected on the host
+    ctx = torch.ones(256, dtype=torch.int32, device="cuda")
+    lib = msa.load()
+    import ctypes
+    st = lib.msa_decode_noalloc(ctypes.byref(p), 256, 131072, ctypes.c_void_p(q.data_ptr()),
+                                ctypes.c_void_p(qi.data_ptr()), ctypes.c_void_p(kc.data_ptr()),
+                                ctypes.c_void_p(kc.data_ptr()), ctypes.c_void_p(kc.data_ptr()),
+                                ctypes.c_void_p(ctx.data_ptr()), ctypes.c_void_p(q.data_ptr()), None, None, None)
+    assert st == -2
