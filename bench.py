@@ -618,7 +618,7 @@ def config_decode(torch, msa, label, B, L, seed, reps):
     torch.cuda.empty_cache()
     return {"workload": label, "ms": round(ms, 4), "ms_cold": round(ms_cold, 4), "bytes_gb": round(db / 1e9, 4),
             "GB/s": round(gbs, 1), "GB/s_cold": round(db / (ms_cold * 1e-3) / 1e9, 1),
-            "roofline": {"kernel": "decode (index + select + attention + combine)", "bound": "hbm",
+            "roofline": {"kernel": "decode (index + select + attention)", "bound": "hbm",
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "stage_ms": {k: round(float(v), 4) for k, v in zip(msa.DECODE_STAGES, x)}}

@@ -8,8 +8,8 @@
 //   (combine).
 // Windows bound the workspace (block scores and partials grow with the rows of
 // a window, not with the sequence), which is what makes 1M-token prefill fit.
-// Decode: index scores -> selection -> per-(sequence, group, slot) attention ->
-// combine.
+// Decode: index scores -> selection -> per-(sequence, group) attention over the
+// selected blocks (online softmax across them; no partials).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -175,7 +175,7 @@ bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
 
 struct DecodeLayout {
   int nb;
-  size_t sblk, sel, part_o, part_lse, total;
+  size_t sblk, sel, total;
 };
 
 // max_ctx beyond the longest supported context has no layout (the caller
@@ -187,8 +187,6 @@ bool decode_layout(const Shape& s, int32_t B, int64_t max_ctx, DecodeLayout* L) 
   size_t off = 0;
   L->sblk = off;     off += up((size_t)B * s.G * L->nb * sizeof(float));
   L->sel = off;      off += up(items * sizeof(int32_t));
-  L->part_o = off;   off += up(items * kHpg * kHeadDim * sizeof(uint16_t));
-  L->part_lse = off; off += up(items * kHpg * sizeof(float));
   L->total = off;
   return true;
 }
@@ -568,13 +566,9 @@ msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const
   launch_select(sa, hs);
   clk.mark();
   LaunchAttnDecode aa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                      static_cast<const uint16_t*>(v_cache), ctx_lens, sel, at<uint16_t>(workspace, L.part_o),
-                      at<float>(workspace, L.part_lse), max_ctx, batch, s.G, s.k, s.scale_log2, s.bk};
+                      static_cast<const uint16_t*>(v_cache), ctx_lens, sel, static_cast<uint16_t*>(out), lse_out,
+                      max_ctx, batch, s.G, s.k, s.scale_log2, s.bk};
   launch_attn_decode(aa, hs);
-  clk.mark();
-  LaunchCombine cb{at<uint16_t>(workspace, L.part_o), at<float>(workspace, L.part_lse),
-                   static_cast<uint16_t*>(out), lse_out, batch, s.G, s.k, ctx_lens, s.bk_shift};
-  launch_combine(cb, hs);
   clk.mark();
   return finish();
 }
@@ -600,7 +594,7 @@ msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_c
   std::vector<hipEvent_t> ev;
   msa_status st = run_decode(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out,
                              lse_out, workspace, workspace_bytes, stream, &ev);
-  return collect(ev, 4, stage_ms, st);
+  return collect(ev, 3, stage_ms, st);
 }
 
 size_t msa_index_kl_workspace_bytes(const msa_params* p, int64_t seq_len) {

@@ -31,8 +31,8 @@
 // swizzles of the 16-byte (K) and 32-byte (V) chunks keep the operand reads
 // free of bank conflicts.
 //
-// Decode: one workgroup per (sequence, group, selected slot); four waves stage
-// the block, one computes the 16 heads.
+// Decode: one workgroup per (sequence, group) streams the selected blocks
+// through LDS; one wave keeps the 16 heads' online softmax across them.
 #include <type_traits>
 
 #include "msa_device.h"
@@ -1000,45 +1000,85 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   }
 }
 
-// Decode: one workgroup per (sequence, group, selected slot). All four waves
-// stage the block; wave 0 computes the 16 heads.
+// Decode: one workgroup per (sequence, group). Its selected blocks stream
+// through two LDS stages (all four waves issue the direct-to-LDS loads of the
+// next block while wave 0 computes the current one), and wave 0 keeps the
+// group's 16 heads in one online-softmax state across the blocks (the own
+// block, the last in ascending order, with the causal mask), so the output
+// and lse are written at the end with no partials and no separate combine.
+// Only cache rows below ctx_len are staged (later rows may hold anything).
 template <int BK>
 __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      const uint16_t* __restrict__ v,
                                                      const int32_t* __restrict__ ctx_lens,
-                                                     const int32_t* __restrict__ sel,
-                                                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-                                                     int64_t max_ctx, int G, int topk, float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kStage];
+                                                     const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
+                                                     float* __restrict__ lse_out, int64_t max_ctx, int G, int topk,
+                                                     float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
   lds_char* lds = (lds_char*)lds_raw;
-  const int item = blockIdx.x;
-  const int sq = item / (G * topk), g = (item / topk) % G;
-  const int b = sel[item];
-  if (b < 0) return;
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 15, qd = (tid >> 4) & 3;
+  const int item = blockIdx.x;  // sq * G + g
+  const int sq = item / G, g = item % G;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int c = lane & 15, qd = lane >> 4;
   const int64_t i = ctx_lens[sq] - 1;
-  const int64_t key0 = (int64_t)b * BK;
+  const int b_loc = (int)(i / BK);
+  const int nsel = min(topk, b_loc + 1);
   const int Hq = G * kHpg;
-  const int64_t base = ((int64_t)sq * max_ctx * G + key0 * G + g) * kHeadDim;
-  // only positions < ctx_len are read: later cache rows may hold anything
-  stage_block_bk<BK>(lds, k + base, v + base, (int64_t)G * kHeadDim, (int)min<int64_t>(BK, i + 1 - key0), wave, 4,
-                     stage_offsets((int64_t)G * kHeadDim, wave));
+  const int64_t rstride = (int64_t)G * kHeadDim;
+  const int64_t seq0 = (int64_t)sq * max_ctx * G * kHeadDim + (int64_t)g * kHeadDim;
+  // lane u holds slot u of the selection (ascending; the first nsel are valid)
+  const int lane_blk = lane < topk ? sel[(int64_t)item * topk + lane] : 0;
+  const StageOffsets soff = stage_offsets(rstride, wave);
+  auto stage = [&](int u, lds_char* dst) {
+    const int b = __builtin_amdgcn_readlane(lane_blk, u);
+    const int64_t key0 = (int64_t)b * BK;
+    const int64_t base = seq0 + key0 * rstride;
+    stage_block_bk<BK>(dst, k + base, v + base, rstride, (int)min<int64_t>(BK, i + 1 - key0), wave, 4, soff);
+  };
+  stage(0, lds);
   QueryGroup<1> qg;
-  if (wave == 0) load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
-  wait_loads();
-  __syncthreads();
-  if (wave != 0) return;
-  int lim[1] = {(i / BK == b) ? (int)(i - key0) : BK - 1};
-  if constexpr (BK == kBlock) {
-    KHalf k0;
-    load_k_half(k0, lds);
-    attend_block<true, true>(qg, lds, k0, lim, scale_log2, 0u, [](int) {});
-  } else {
-    attend_short<true, true, BK / 16>(qg, lds, lim, scale_log2, 0u, [](int) {});
+  if (wave == 0) {
+    load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
+    reset_state(qg);
   }
-  store_partial(qg.o[0], qg.m[0], scale_log2, part_o + (int64_t)item * kHpg * kHeadDim,
-                part_lse + (int64_t)item * kHpg);
+  for (int u = 0; u < nsel; ++u) {
+    wait_loads();
+    __syncthreads();  // stage u&1 complete; stage (u+1)&1 free
+    if (u + 1 < nsel) stage(u + 1, lds + ((u + 1) & 1) * kStage);
+    if (wave != 0) continue;
+    const lds_char* st = lds + (u & 1) * kStage;
+    if (u + 1 < nsel) {  // an older block: every key is before the query
+      if constexpr (BK == kBlock) {
+        KHalf k0;
+        load_k_half(k0, st);
+        attend_block<false, false>(qg, st, k0, nullptr, scale_log2, 0u, [](int) {});
+      } else {
+        attend_short<false, false, BK / 16>(qg, st, nullptr, scale_log2, 0u, [](int) {});
+      }
+    } else {  // the own block, keys up to the query
+      int lim[1] = {(int)(i - (int64_t)b_loc * BK)};
+      if constexpr (BK == kBlock) {
+        KHalf k0;
+        load_k_half(k0, st);
+        attend_block<false, true>(qg, st, k0, lim, scale_log2, 0u, [](int) {});
+      } else {
+        attend_short<false, true, BK / 16>(qg, st, lim, scale_log2, 0u, [](int) {});
+      }
+    }
+  }
+  if (wave != 0) return;
+  const float l = qg.o[0][8][0];
+  const float inv = 1.0f / l;
+  uint16_t* dst = out + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    u32x2 w = {pack_bf16x2(qg.o[0][dt][0] * inv, qg.o[0][dt][1] * inv),
+               pack_bf16x2(qg.o[0][dt][2] * inv, qg.o[0][dt][3] * inv)};
+    *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+  }
+  if (lse_out && qd == 0)
+    lse_out[(int64_t)sq * Hq + g * kHpg + c] = (qg.m[0] * scale_log2 + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
 }
 
 template <int BK>
@@ -1075,12 +1115,12 @@ void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {
 
 template <int BK>
 static void launch_attn_decode_bk(const LaunchAttnDecode& a, hipStream_t st, int items) {
-  hipLaunchKernelGGL(k_attn_decode<BK>, dim3(items), dim3(256), 0, st, a.q, a.k, a.v, a.ctx_lens, a.sel, a.part_o,
-                     a.part_lse, a.max_ctx, a.G, a.topk, a.scale_log2);
+  hipLaunchKernelGGL(k_attn_decode<BK>, dim3(items), dim3(256), 0, st, a.q, a.k, a.v, a.ctx_lens, a.sel, a.out,
+                     a.lse_out, a.max_ctx, a.G, a.topk, a.scale_log2);
 }
 
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st) {
-  const int items = a.batch * a.G * a.topk;
+  const int items = a.batch * a.G;
   if (items <= 0) return;
   switch (a.bk) {
     case 128: launch_attn_decode_bk<128>(a, st, items); break;

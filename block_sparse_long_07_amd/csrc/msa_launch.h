@@ -129,8 +129,8 @@ struct LaunchAttnDecode {
   const uint16_t* v;
   const int32_t* ctx_lens;
   const int32_t* sel;     // [(s*G + g)*topk + u]
-  uint16_t* part_o;
-  float* part_lse;
+  uint16_t* out;          // [batch, Hq, 128]
+  float* lse_out;         // optional [batch, Hq]
   int64_t max_ctx;
   int batch, G, topk;
   float scale_log2;
@@ -190,16 +190,5 @@ struct ProjectPlan {
 ProjectPlan plan_index_project(int64_t n, int d_model, int G);
 void launch_index_project(const LaunchProject& a, hipStream_t st);
 
-struct LaunchCombine {   // decode
-  const uint16_t* part_o;  // [(s*G + g)*topk + u][2048] bf16, fragment order
-  const float* part_lse;
-  uint16_t* out;           // row s at out + s*Hq*128
-  float* lse_out;          // optional, row s at lse_out + s*Hq
-  int64_t nrows;
-  int G, topk;
-  const int32_t* ctx_lens;
-  int bk_shift;            // log2 B_k
-};
-void launch_combine(const LaunchCombine& a, hipStream_t st);
 
 }  // namespace msa

@@ -17,6 +17,8 @@
 // butterfly inside the 16-lane row; ties to the lower index), the winning lane
 // popping its head. The chosen indices are sorted ascending and written with
 // b_loc last and -1 padding.
+#include <utility>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -253,20 +255,143 @@ __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sb
   }
 }
 
+// Few rows with very many candidates (long decode contexts): NW waves per
+// row. Wave w ranks the candidates b = 64w + lane + 64*NW*j like
+// k_select_wave and reduces its 64 lane lists to its own best k-1 (by k-1
+// wave arg-max rounds), which go to LDS; wave 0 then ranks the NW*(k-1)
+// survivors (the row's best k-1 are among them: each wave kept its subset's
+// best under the same total order) and writes the selection. The survivors
+// do not arrive in index order, so this second ranking compares (score
+// descending, index ascending) in full.
+__device__ __forceinline__ bool before(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+template <int KM1, int NW>
+__global__ __launch_bounds__(64 * NW) void k_select_multi(const float* __restrict__ sblk, int nb,
+                                                          int32_t* __restrict__ sel, int64_t sel_gstride,
+                                                          int64_t sel_rstride, int G, int64_t row0,
+                                                          const int32_t* __restrict__ ctx_lens, int bk_shift) {
+  static_assert(KM1 > 0, "k >= 2");
+  __shared__ float sv[NW * KM1];
+  __shared__ int si[NW * KM1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = blockIdx.x;
+  const int64_t rr = r / G;
+  const int g = (int)(r % G);
+  const int b_loc = ctx_lens ? (ctx_lens[rr] - 1) >> bk_shift : (int)((row0 + rr) >> bk_shift);
+  int32_t* out = sel + (int64_t)g * sel_gstride + rr * sel_rstride;
+  if (b_loc <= KM1) {  // every block 0..b_loc is selected (uniform over the workgroup)
+    if (wave == 0 && lane <= KM1) out[lane] = (lane <= b_loc) ? lane : -1;
+    return;
+  }
+  float v[KM1];
+  int id[KM1];
+#pragma unroll
+  for (int t = 0; t < KM1; ++t) {
+    v[t] = -__builtin_inff();
+    id[t] = 0x7fffffff;
+  }
+  auto insert = [&](float cv, int ci) {
+    if (!before(cv, ci, v[KM1 - 1], id[KM1 - 1])) return;
+    bool shift = false;
+#pragma unroll
+    for (int t = 0; t < KM1; ++t) {
+      shift = shift || before(cv, ci, v[t], id[t]);
+      const float nv = shift ? cv : v[t];
+      const int ni = shift ? ci : id[t];
+      cv = shift ? v[t] : cv;
+      ci = shift ? id[t] : ci;
+      v[t] = nv;
+      id[t] = ni;
+    }
+  };
+  auto pop_best = [&]() {  // wave-wide arg-max of the list heads; the winner pops
+    float bv = v[0];
+    int bi = id[0];
+    argmax_row16(bv, bi);
+    argmax_rows(bv, bi);
+    if (id[0] == bi) {
+#pragma unroll
+      for (int t = 0; t + 1 < KM1; ++t) {
+        v[t] = v[t + 1];
+        id[t] = id[t + 1];
+      }
+      v[KM1 - 1] = -__builtin_inff();
+      id[KM1 - 1] = 0x7fffffff;
+    }
+    return std::pair<float, int>(bv, bi);
+  };
+  const float* row = sblk + r * (int64_t)nb;
+  constexpr int kBatch = 16;
+  constexpr int kStride = 64 * NW;
+  for (int b0 = wave * 64 + lane; b0 < b_loc; b0 += kStride * kBatch) {
+    float cand[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) cand[u] = b0 + kStride * u < b_loc ? row[b0 + kStride * u] : -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (b0 + kStride * u < b_loc) insert(cand[u], b0 + kStride * u);
+  }
+#pragma unroll
+  for (int rd = 0; rd < KM1; ++rd) {
+    const auto best = pop_best();
+    if (lane == 0) {
+      sv[wave * KM1 + rd] = best.first;
+      si[wave * KM1 + rd] = best.second;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < KM1; ++t) {
+    v[t] = -__builtin_inff();
+    id[t] = 0x7fffffff;
+  }
+  for (int j = lane; j < NW * KM1; j += 64) insert(sv[j], si[j]);
+  int chosen[KM1];
+#pragma unroll
+  for (int rd = 0; rd < KM1; ++rd) chosen[rd] = pop_best().second;
+#pragma unroll
+  for (int a = 0; a < KM1; ++a) {
+#pragma unroll
+    for (int t = 0; t + 1 < KM1 - a; ++t) {
+      const int lo = min(chosen[t], chosen[t + 1]);
+      const int hi = max(chosen[t], chosen[t + 1]);
+      chosen[t] = lo;
+      chosen[t + 1] = hi;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int u = 0; u < KM1; ++u) out[u] = chosen[u];
+    out[KM1] = b_loc;
+  }
+}
+
 void launch_select(const LaunchSelect& a, hipStream_t st) {
   const int64_t rows = a.nrows * a.G;
   if (rows <= 0) return;
-  // few rows: a wave per row; many rows: 16 lanes per row (4 rows per wave)
+  // few rows: a wave per row (16 waves per row when the rows are long: at
+  // 8 x 1M decode 53 -> ~10 us; 4 waves at 1024 candidates measured a few us
+  // slower than one); many rows: 16 lanes per row (4 rows per wave)
   const bool per_wave = rows <= kWaveRowsMax;
+  const int nw = !per_wave || a.topk < 2 ? 1 : a.nb >= 4096 ? 16 : 1;
   dim3 grid((unsigned)(per_wave ? rows : (rows + 15) / 16));
+#define MSA_SEL_MULTI(K)                                                                                \
+  hipLaunchKernelGGL((k_select_multi<K - 1, 16>), grid, dim3(1024), 0, st, a.sblk, a.nb, a.sel,         \
+                     a.sel_gstride, a.sel_rstride, a.G, a.row0, a.ctx_lens, a.bk_shift);
 #define MSA_SEL_CASE(K)                                                                                 \
   case K:                                                                                               \
-    if (per_wave)                                                                                       \
+    if (per_wave && nw > 1) {                                                                           \
+      if constexpr (K > 1) { MSA_SEL_MULTI(K) }                                                         \
+    } else if (per_wave) {                                                                              \
       hipLaunchKernelGGL(k_select_wave<K - 1>, grid, dim3(64), 0, st, a.sblk, a.nb, a.sel,              \
                          a.sel_gstride, a.sel_rstride, a.G, a.row0, a.ctx_lens, a.bk_shift);            \
-    else                                                                                                \
+    } else {                                                                                            \
       hipLaunchKernelGGL(k_select<K - 1>, grid, dim3(256), 0, st, a.sblk, a.nb, a.sel, a.sel_gstride,   \
                          a.sel_rstride, a.nrows, a.G, a.row0, a.ctx_lens, a.bk_shift);                  \
+    }                                                                                                   \
     break;
   switch (a.topk) {
     MSA_SEL_CASE(1)
@@ -288,6 +413,7 @@ void launch_select(const LaunchSelect& a, hipStream_t st) {
     default: break;
   }
 #undef MSA_SEL_CASE
+#undef MSA_SEL_MULTI
 }
 
 }  // namespace msa

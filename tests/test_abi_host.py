@@ -106,9 +106,9 @@ def test_decode_noalloc_rejects_before_touching_the_device(lib):
     assert f(ctypes.byref(p), 2, 4096, None, *[ok] * 6, None, None, None) == -1        # no q
     assert f(ctypes.byref(p), 0, 4096, *[ok] * 7, None, None, None) == -1              # no sequences
     assert f(ctypes.byref(p), 2, (1 << 20) + 1, *[ok] * 7, None, None, None) == -2     # context too long
-    need = lib.msa_decode_workspace_bytes(ctypes.byref(p), 256, 131072)
-    assert need > (32 << 20)
-    assert f(ctypes.byref(p), 256, 131072, *[ok] * 7, None, None, None) == -2          # beyond the array
+    need = lib.msa_decode_workspace_bytes(ctypes.byref(p), 1024, 131072)
+    assert need > (8 << 20)
+    assert f(ctypes.byref(p), 1024, 131072, *[ok] * 7, None, None, None) == -2         # beyond the array
     p.topk = 20
     assert f(ctypes.byref(p), 2, 4096, *[ok] * 7, None, None, None) == -2
 

@@ -53,16 +53,14 @@ def test_noalloc_decode_matches_decode_twice():
 
 def test_noalloc_rejects_workspace_beyond_its_array():
     p = msa.params()
-    need = msa.decode_workspace_bytes(p, 256, 131072)
-    assert need > (32 << 20)
-    q = torch.empty((256, 64, 128), dtype=torch.bfloat16, device="cuda")
-    qi = torch.empty((256, 4, 64), dtype=torch.bfloat16, device="cuda")
-    kc = torch.empty((256, 1, 4, 128), dtype=torch.bfloat16, device="cuda")  # never read: rejected on the host
-    ctx = torch.ones(256, dtype=torch.int32, device="cuda")
+    B = 1024
+    need = msa.decode_workspace_bytes(p, B, 131072)
+    assert need > (8 << 20)
+    t = torch.empty((64, 64, 128), dtype=torch.bfloat16, device="cuda")  # never read: rejected on the host
+    ctx = torch.ones(64, dtype=torch.int32, device="cuda")
     lib = msa.load()
     import ctypes
-    st = lib.msa_decode_noalloc(ctypes.byref(p), 256, 131072, ctypes.c_void_p(q.data_ptr()),
-                                ctypes.c_void_p(qi.data_ptr()), ctypes.c_void_p(kc.data_ptr()),
-                                ctypes.c_void_p(kc.data_ptr()), ctypes.c_void_p(kc.data_ptr()),
-                                ctypes.c_void_p(ctx.data_ptr()), ctypes.c_void_p(q.data_ptr()), None, None, None)
+    ptr = ctypes.c_void_p(t.data_ptr())
+    st = lib.msa_decode_noalloc(ctypes.byref(p), B, 131072, ptr, ptr, ptr, ptr, ptr,
+                                ctypes.c_void_p(ctx.data_ptr()), ptr, None, None, None)
     assert st == -2
