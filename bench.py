@@ -546,6 +546,31 @@ def time_cold(torch, fn, reps, flush_bytes=512 << 20):
 
 # ---- the longer configurations ------------------------------------------------------
 
+def queue_spread(torch, msa, ws, p, n):
+    """Balance of the persistent KV-outer pass over the last window of the
+    latest prefill on `ws`: per-workgroup busy time (its own wall clock from
+    start to exit) and tiles drained, and how many compute units held one."""
+    torch.cuda.synchronize()
+    m = msa.prefill_schedule_layout(p, n, n)
+    sc = msa.read_prefill_schedule(ws, m, G)
+    wg = sc["wg_trace"].numpy().astype(np.int64)
+    info = sc["tile_info"].numpy()
+    if len(wg) == 0 or m.wall_clock_khz <= 0:
+        return None
+    us = 1e3 / m.wall_clock_khz
+    busy = (wg[:, 3] - wg[:, 2]) * us
+    tiles = wg[:, 1]
+    return {"window_rows": int(info[5]), "first_row": int(info[6]), "tiles": int(info[0]),
+            "workgroups": int(len(wg)), "compute_units_used": int(len(np.unique(wg[:, 0]))),
+            "visits_all_one": bool((sc["tile_visits"].numpy() == 1).all()),
+            "busy_us": {"min": round(float(busy.min()), 1), "median": round(float(np.median(busy)), 1),
+                        "max": round(float(busy.max()), 1), "max_over_mean": round(float(busy.max() / busy.mean()), 3)},
+            "tiles_per_wg": {"min": int(tiles.min()), "median": float(np.median(tiles)), "max": int(tiles.max())},
+            "first_exit_to_last_exit_us": round(float((wg[:, 3].max() - wg[:, 3].min()) * us), 1),
+            "span_us": round(float((wg[:, 3].max() - wg[:, 2].min()) * us), 1),
+            "clock_khz": int(m.wall_clock_khz)}
+
+
 def config_prefill(torch, msa, label, inp, reps):
     """One prefill configuration: warm (mean of reps) and cold timings, the
     per-stage times, the attention kernels' roofline positions from the actual
@@ -566,6 +591,7 @@ def config_prefill(torch, msa, label, inp, reps):
     msa.prefill(*pre, topk=TOPK, workspace=ws, out=out, stage_ms=x)
     stage = dict(zip(msa.PREFILL_STAGES, (float(v) for v in x)))
     _, sel, _ = msa.prefill(*pre, topk=TOPK, workspace=ws, out=out, want_sel=True)
+    queue = queue_spread(torch, msa, ws, p, n)
     del ws, out, pre
     torch.cuda.empty_cache()
     ps, kernels = attention_rooflines(torch, sel[0], n, stage, measured=False)
@@ -583,7 +609,8 @@ def config_prefill(torch, msa, label, inp, reps):
             "roofline": {k: dom[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "traffic")},
             "kernels": kernels,
             "pairs": {k: ps[k] for k in ("dense_pairs", "sparse_pairs", "kv_dense", "kv_sparse",
-                                         "dense_unit_blocks")}}
+                                         "dense_unit_blocks")},
+            "kv_outer_queue": queue}
 
 
 def config_decode(torch, msa, label, B, L, seed, reps):
@@ -833,6 +860,7 @@ def main():
     ps, kernels = attention_rooflines(torch, sel[0], N_PREFILL, stage)
     par_sel = sel[0][:, torch.as_tensor(par_rows, device=dev)].permute(1, 0, 2).cpu().numpy()
     del sel
+    queue = queue_spread(torch, msa, ws_p, p, N_PREFILL)
     assert abs(ps["F_dense"] + ps["F_sparse"] - f_main) <= 1e-9 * f_main, "pair split does not cover F_main"
     dom = max(kernels, key=lambda r: r["ms"])
 
@@ -898,6 +926,7 @@ def main():
         "block_size_variants": variants,
         "index_projection": proj,
         "cold_cache": cold,
+        "kv_outer_queue": queue,
         "context": context,
         "configs": configs,
     }

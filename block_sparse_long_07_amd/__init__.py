@@ -24,7 +24,7 @@ EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_prefill_varlen_wo
             "msa_prefill_varlen", "msa_decode_workspace_bytes", "msa_decode", "msa_prefill_profiled",
             "msa_decode_profiled", "msa_index_kl_workspace_bytes", "msa_index_kl_backward", "msa_index_scores",
             "msa_select_blocks", "msa_status_string", "msa_index_project_workspace_bytes", "msa_index_project",
-            "msa_index_project_decode", "msa_decode_noalloc")
+            "msa_index_project_decode", "msa_decode_noalloc", "msa_prefill_schedule_layout")
 PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
 DECODE_STAGES = ("index_score", "select", "attn")
 
@@ -34,6 +34,16 @@ class MsaParams(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float)]
+
+
+_SCHED_OFFSETS = ("tile_info", "chunk_off", "entries", "tiles", "tile_visits", "wg_trace", "dense_cnt",
+                  "dense_list", "dense_qmask", "dense_slots")
+
+
+class MsaScheduleMap(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in _SCHED_OFFSETS] + [
+        ("dense_max", ctypes.c_int32), ("tile_queries", ctypes.c_int32), ("claim", ctypes.c_int32),
+        ("dense_min", ctypes.c_int32), ("wall_clock_khz", ctypes.c_int64)]
 
 
 class MsaError(RuntimeError):
@@ -89,6 +99,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_index_project.restype = ctypes.c_int
     lib.msa_index_project_decode.argtypes = [P, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_index_project_decode.restype = ctypes.c_int
+    lib.msa_prefill_schedule_layout.argtypes = [P, i64, i64, ctypes.POINTER(MsaScheduleMap)]
+    lib.msa_prefill_schedule_layout.restype = ctypes.c_int
     lib.msa_status_string.argtypes = [ctypes.c_int]
     lib.msa_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -160,6 +172,39 @@ def prefill(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale=Non
         _check(lib.msa_prefill_profiled(*args, ms), "msa_prefill_profiled")
         stage_ms.extend(float(x) for x in ms)
     return out, sel, lse
+
+
+def prefill_schedule_layout(p: MsaParams, max_q_len: int, max_ctx: int) -> MsaScheduleMap:
+    """Where a prefill workspace keeps the KV-outer schedule of its last window."""
+    m = MsaScheduleMap()
+    _check(load().msa_prefill_schedule_layout(ctypes.byref(p), max_q_len, max_ctx, ctypes.byref(m)),
+           "msa_prefill_schedule_layout")
+    return m
+
+
+def read_prefill_schedule(workspace: torch.Tensor, m: MsaScheduleMap, num_kv_heads: int) -> dict:
+    """Copies the schedule of the last window a completed prefill left in
+    `workspace` (laid out as `m` says) to host tensors: tile_info, chunk_off,
+    entries, tiles [T,4], tile_visits [T], wg_trace [workgroups,4],
+    dense_cnt [G,units], dense_list / dense_qmask [G,units,dense_max],
+    dense_slots [G,rows]."""
+    def part(name, count, dtype=torch.int32):
+        off = getattr(m, name)
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return workspace[off:off + nbytes].view(dtype).cpu()
+
+    info = part("tile_info", 8)
+    T, lists, nch, nwg, n = (int(info[i]) for i in (0, 2, 3, 4, 5))
+    G, units = num_kv_heads, (n + 15) // 16
+    chunk_off = part("chunk_off", lists * nch + 1)
+    return dict(
+        tile_info=info, chunk_off=chunk_off, entries=part("entries", int(chunk_off[-1])),
+        tiles=part("tiles", 4 * T).view(T, 4), tile_visits=part("tile_visits", T),
+        wg_trace=part("wg_trace", 4 * nwg, torch.int64).view(nwg, 4),
+        dense_cnt=part("dense_cnt", G * units).view(G, units),
+        dense_list=part("dense_list", G * units * m.dense_max).view(G, units, m.dense_max),
+        dense_qmask=part("dense_qmask", G * units * m.dense_max).view(G, units, m.dense_max),
+        dense_slots=part("dense_slots", G * n).view(G, n))
 
 
 def prefill_varlen_workspace_bytes(p: MsaParams, max_q_len: int, max_ctx: int) -> int:

@@ -94,8 +94,8 @@ struct PrefillLayout {
   int nbs;    // row stride of the pooled scores (nb rounded up to 4: 16-byte aligned rows)
   int64_t nch, Lc, nblk, e_cap, tile_cap, slots;
   int64_t nunits;
-  size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, part_o, part_lse, dense_cnt,
-      dense_list, dense_qmask, dense_slots, total;
+  size_t sblk, sel, chunkcnt, chunkoff, bsum, entries, tile_start, tiles, tile_info, tile_visits, wg_trace, part_o,
+      part_lse, dense_cnt, dense_list, dense_qmask, dense_slots, total;
 };
 
 // n_ctx: positions of the longest context; max_rows: most query rows of one
@@ -121,7 +121,9 @@ bool prefill_layout(const Shape& s, int64_t n_ctx, int64_t max_rows, PrefillLayo
   L->entries = off;    off += up((size_t)L->e_cap * sizeof(int32_t));
   L->tile_start = off; off += up((size_t)((int64_t)s.G * L->nb + 1) * sizeof(int32_t));
   L->tiles = off;      off += up((size_t)L->tile_cap * 4 * sizeof(int32_t));
-  L->tile_info = off;  off += up(4 * sizeof(int32_t));
+  L->tile_info = off;  off += up(8 * sizeof(int32_t));
+  L->tile_visits = off; off += up((size_t)L->tile_cap * sizeof(int32_t));
+  L->wg_trace = off;   off += up((size_t)kMaxPersistent * 4 * sizeof(int64_t));
   L->part_o = off;     off += up((size_t)L->slots * kHpg * kHeadDim * sizeof(uint16_t));
   L->part_lse = off;   off += up((size_t)L->slots * kHpg * sizeof(float));
   L->nunits = cdiv(L->W, 16);
@@ -162,7 +164,7 @@ bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
   L->entries = off;    off += up((size_t)L->e_cap * sizeof(int32_t));
   L->tile_start = off; off += up((size_t)((int64_t)s.G * L->nb + 1) * sizeof(int32_t));
   L->chunks = off;     off += up((size_t)L->chunk_cap * 4 * sizeof(int32_t));
-  L->chunk_info = off; off += up(4 * sizeof(int32_t));
+  L->chunk_info = off; off += up(8 * sizeof(int32_t));
   L->part_m = off;     off += up((size_t)L->slots * sizeof(float));
   L->part_l = off;     off += up((size_t)L->slots * sizeof(float));
   L->loss_part = off;  off += up((size_t)L->slots * sizeof(float));
@@ -311,14 +313,15 @@ void prefill_window(const Shape& s, const PrefillLayout& L, const SeqIO& io, int
                at<int32_t>(workspace, L.tile_start), at<int32_t>(workspace, L.tiles),
                at<int32_t>(workspace, L.tile_info), kTileQ, tile_cap, dcnt, dlist,
                at<int32_t>(workspace, L.dense_qmask), at<int32_t>(workspace, L.dense_slots), nunits, true,
-               s.bk_shift};
+               s.bk_shift, at<int32_t>(workspace, L.tile_visits)};
   launch_csr_and_tiles(ca, hs);
   clk.mark();
   // 4. KV-outer attention over the pairs not shared by a whole unit
   LaunchAttnPrefill aa{qw, io.k, io.v, at<int32_t>(workspace, L.entries), at<int32_t>(workspace, L.tiles),
                        at<int32_t>(workspace, L.tile_info), at<uint16_t>(workspace, L.part_o),
                        at<float>(workspace, L.part_lse), n_ctx, G, nbw, K, s.scale_log2,
-                       (int)std::min<int64_t>(cu_count(), tile_cap), s.bk};
+                       (int)std::min<int64_t>({(int64_t)cu_count(), tile_cap, (int64_t)kMaxPersistent}), s.bk,
+                       at<int32_t>(workspace, L.tile_visits), at<int64_t>(workspace, L.wg_trace)};
   launch_attn_prefill(aa, hs);
   clk.mark();
   // 5. query-stationary attention over the units' shared blocks + merge
@@ -492,6 +495,36 @@ size_t msa_prefill_varlen_workspace_bytes(const msa_params* p, int64_t max_q_len
   PrefillLayout L;
   if (check_params(p, &s) != MSA_OK || !prefill_layout(s, max_ctx, std::min(max_q_len, max_ctx), &L)) return 0;
   return L.total;
+}
+
+msa_status msa_prefill_schedule_layout(const msa_params* p, int64_t max_q_len, int64_t max_ctx,
+                                       msa_prefill_schedule_map* m) {
+  if (!m || max_q_len <= 0 || max_ctx <= 0) return MSA_ERR_INVALID_ARG;
+  Shape s;
+  msa_status st = check_params(p, &s);
+  if (st != MSA_OK) return st;
+  PrefillLayout L;
+  if (!prefill_layout(s, max_ctx, std::min(max_q_len, max_ctx), &L)) return MSA_ERR_UNSUPPORTED;
+  *m = msa_prefill_schedule_map{};
+  m->tile_info = (int64_t)L.tile_info;
+  m->chunk_off = (int64_t)L.chunkoff;
+  m->entries = (int64_t)L.entries;
+  m->tiles = (int64_t)L.tiles;
+  m->tile_visits = (int64_t)L.tile_visits;
+  m->wg_trace = (int64_t)L.wg_trace;
+  m->dense_cnt = (int64_t)L.dense_cnt;
+  m->dense_list = (int64_t)L.dense_list;
+  m->dense_qmask = (int64_t)L.dense_qmask;
+  m->dense_slots = (int64_t)L.dense_slots;
+  m->dense_max = kDenseMax;
+  m->tile_queries = kTileQ;
+  m->claim = kTileClaim;
+  m->dense_min = kDenseMin;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+    m->wall_clock_khz = khz;
+  return MSA_OK;
 }
 
 msa_status msa_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ctx, const int64_t* q_start,

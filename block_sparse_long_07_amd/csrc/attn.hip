@@ -674,7 +674,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ tiles, int32_t* __restrict__ tile_info,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, int64_t n_tokens, int G,
-    int nbw, int topk, float scale_log2) {
+    int nbw, int topk, float scale_log2, int32_t* __restrict__ tile_visits, int64_t* __restrict__ wg_trace) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
   __shared__ int s_t[4];
   lds_char* lds = (lds_char*)lds_raw;
@@ -719,12 +719,16 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
 
   // the queue: chunk c of this workgroup's tiles (tiles kClaim*c ..) starts at
   // queue position s_t[c & 1]
-  constexpr int kClaim = 4;
+  constexpr int kClaim = kTileClaim;
   // chunk c+1 is claimed at tile kClaim*c and first read for tile kClaim*c + 2
   // (the descriptor two tiles ahead): a barrier lies between only if the
   // chunk is longer than two tiles
   static_assert(kClaim >= 3, "the claim must be visible before the look-ahead reads it");
-  if (tid == 0) s_t[0] = atomicAdd(&tile_info[1], kClaim);
+  const int64_t t_start = wall_clock64();
+  if (tid == 0) {
+    if (blockIdx.x == 0) tile_info[4] = gridDim.x;
+    s_t[0] = atomicAdd(&tile_info[1], kClaim);
+  }
   __syncthreads();
   auto tile_pos = [&](int jj) { return __builtin_amdgcn_readfirstlane(s_t[(jj / kClaim) & 1] + jj % kClaim); };
   Tile cur = read_tile(tile_pos(0));
@@ -738,6 +742,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     }
   }
   int after_dma = 0;  // vector memory operations issued after the last stage load
+  int drained = 0;    // tiles this workgroup computed
   for (int j = 0; cur.t < T; ++j) {
     wait_vmcnt_upto(after_dma);  // the stage of tile j is in
     wait_lgkmcnt0();
@@ -748,8 +753,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     KHalf k0;
     if (BK == kBlock && e0 < cur.len) load_k_half(k0, stage);
     // chunk c+1 is claimed when chunk c starts; it is first read two tiles
-    // later (for tile kClaim*(c+1)), after at least one more barrier
-    if (tid == 0 && j % kClaim == 0) s_t[(j / kClaim + 1) & 1] = atomicAdd(&tile_info[1], kClaim);
+    // later (for tile kClaim*(c+1)), after at least one more barrier. Both
+    // atomics are issued before the next stage's loads, so the vmcnt budget
+    // of those loads (after_dma) does not count them.
+    if (tid == 0) {
+      atomicAdd(&tile_visits[cur.t], 1);
+      if (j % kClaim == 0) s_t[(j / kClaim + 1) & 1] = atomicAdd(&tile_info[1], kClaim);
+    }
     const int t2 = tile_pos(j + 2);
     int d2[4] = {0, 0, 0, 0};
     if (t2 < T) {
@@ -794,6 +804,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     nxt.len = d2[2];
     nxt.g = d2[0];
     nxt.b = d2[3];
+    if (tid == 0) ++drained;
+  }
+  if (tid == 0) {
+    int64_t* r = wg_trace + 4 * blockIdx.x;
+    r[0] = __smid();
+    r[1] = drained;
+    r[2] = t_start;
+    r[3] = wall_clock64();
   }
 }
 
@@ -1084,7 +1102,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
 template <int BK>
 static void launch_attn_prefill_bk(const LaunchAttnPrefill& a, hipStream_t st) {
   hipLaunchKernelGGL(k_attn_prefill<BK>, dim3(a.grid), dim3(512), 0, st, a.q, a.k, a.v, a.entries, a.tiles,
-                     a.tile_info, a.part_o, a.part_lse, a.n_tokens, a.G, a.nbw, a.topk, a.scale_log2);
+                     a.tile_info, a.part_o, a.part_lse, a.n_tokens, a.G, a.nbw, a.topk, a.scale_log2,
+                     a.tile_visits, a.wg_trace);
 }
 
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {

@@ -240,10 +240,11 @@ __global__ __launch_bounds__(256) void k_scan_final(const int32_t* __restrict__ 
 // ---- tiles --------------------------------------------------------------------
 
 // One workgroup: per list l = g*nbw + b, tiles = ceil(count / tile_q); exclusive
-// scan into tile_start; tile_info[0] = total tiles, tile_info[1] = 0 (queue).
+// scan into tile_start; tile_info[0] = total tiles, tile_info[1] = 0 (queue),
+// [2] = lists, [3] = chunks per list, [5] = window rows, [6] = first row.
 __global__ __launch_bounds__(1024) void k_tiles_count(const int32_t* __restrict__ chunkoff, int nch, int L,
                                                       int tile_q, int32_t* __restrict__ tile_start,
-                                                      int32_t* __restrict__ tile_info) {
+                                                      int32_t* __restrict__ tile_info, int nrows, int row0) {
   const int per = (L + 1023) / 1024;
   const int l0 = threadIdx.x * per;
   int s = 0;
@@ -268,16 +269,22 @@ __global__ __launch_bounds__(1024) void k_tiles_count(const int32_t* __restrict_
     tile_start[L] = tot;
     tile_info[0] = tot;
     tile_info[1] = 0;
+    tile_info[2] = L;
+    tile_info[3] = nch;
+    tile_info[5] = nrows;
+    tile_info[6] = row0;
   }
 }
 
 __global__ __launch_bounds__(256) void k_tiles_fill(const int32_t* __restrict__ tile_start,
                                                     const int32_t* __restrict__ chunkoff, int nch, int L, int nbw,
                                                     int tile_q, const int32_t* __restrict__ tile_info,
-                                                    int64_t tile_cap, int32_t* __restrict__ tiles) {
+                                                    int64_t tile_cap, int32_t* __restrict__ tiles,
+                                                    int32_t* __restrict__ tile_visits) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int T = tile_info[0];
   if (t >= T || t >= tile_cap) return;
+  if (tile_visits) tile_visits[t] = 0;
   // largest l with tile_start[l] <= t
   int lo = 0, hi = L - 1;
   while (lo < hi) {
@@ -313,10 +320,10 @@ void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st) {
                      a.nbw, nch, a.chunkoff, a.entries, a.dense, a.bk_shift);
   const int L = a.G * a.nbw;
   hipLaunchKernelGGL(k_tiles_count, dim3(1), dim3(1024), 0, st, a.chunkoff, nch, L, a.tile_q, a.tile_start,
-                     a.tile_info);
+                     a.tile_info, a.nrows, (int)a.row0);
   const int fill_blocks = (int)((a.tile_cap + 255) / 256);
   hipLaunchKernelGGL(k_tiles_fill, dim3(fill_blocks), dim3(256), 0, st, a.tile_start, a.chunkoff, nch, L, a.nbw,
-                     a.tile_q, a.tile_info, a.tile_cap, a.tiles);
+                     a.tile_q, a.tile_info, a.tile_cap, a.tiles, a.tile_visits);
 }
 
 }  // namespace msa

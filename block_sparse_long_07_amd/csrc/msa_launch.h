@@ -17,6 +17,8 @@ constexpr int kMaxTopk = 16;
 // their KV-outer partials would. At most 16*16/kDenseMin blocks qualify.
 constexpr int kDenseMin = 7;
 constexpr int kDenseMax = 64;
+constexpr int kMaxPersistent = 1024;  // workgroups of the persistent KV-outer pass, at most
+constexpr int kTileClaim = 4;         // tiles a KV-outer workgroup claims from the queue at a time
 
 // Per-query arrays of a prefill window (q, q_idx, out, lse, selection) start
 // at the window's first row row0; key-side arrays (k, v, k_idx) at position 0.
@@ -74,7 +76,8 @@ struct LaunchCsr {
   int32_t* entries;
   int32_t* tile_start;    // [G*nbw + 1]
   int32_t* tiles;         // [T_cap][4] = (group, begin, len, block)
-  int32_t* tile_info;     // [0] tiles, [1] queue counter
+  int32_t* tile_info;     // [8]: [0] tiles, [1] queue counter, [2] lists (G*nbw), [3] chunks per list,
+                          // [4] workgroups of the KV-outer pass (written by it), [5] rows, [6] row0
   int tile_q;             // queries per tile
   int64_t tile_cap;
   int32_t* dense_cnt;     // [G][nunits]: blocks a 16-row unit computes in the dense pass
@@ -84,6 +87,7 @@ struct LaunchCsr {
   int nunits;             // ceil(nrows / 16)
   bool dense;             // split off the dense pass's pairs (else list every pair; dense_* unused)
   int bk_shift;           // log2 B_k
+  int32_t* tile_visits;   // [T_cap] (optional): zeroed for the tiles scheduled
 };
 void launch_csr_and_tiles(const LaunchCsr& a, hipStream_t st);
 
@@ -99,8 +103,10 @@ struct LaunchAttnPrefill {
   int64_t n_tokens;       // keys that exist (positions < n_tokens)
   int G, nbw, topk;
   float scale_log2;
-  int grid;               // persistent workgroups
+  int grid;               // persistent workgroups (<= kMaxPersistent)
   int bk;                 // B_k: 128, 64 or 32
+  int32_t* tile_visits;   // [T]: +1 for every claim of a tile
+  int64_t* wg_trace;      // [grid][4]: hardware id, tiles drained, wall clock at start and end
 };
 void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st);
 

@@ -134,6 +134,52 @@ msa_status msa_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ct
                               void* out, int32_t* sel_out, float* lse_out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Schedule inspection ---------------------------------------------------
+ * Where a prefill workspace keeps the reverse index and the tile schedule of
+ * the KV-outer pass [pnsm, section 7 "outer gather Q" and section 9: reverse
+ * index, pre-scheduled tile chunking, persistent work queue], for checks and
+ * load-balance diagnostics. Once a msa_prefill / msa_prefill_varlen call has
+ * completed on its stream, these arrays describe the LAST window it processed
+ * (a window is a run of at most 65536 query rows of one sequence; a call of one
+ * sequence of up to 65536 rows starting at a multiple of 16 has exactly one).
+ * All offsets are bytes from the start of the workspace; n is the window's rows,
+ * nbw the blocks its rows can see, nch = ceil(n / 64), units = ceil(n / 16).
+ * Nothing here is read by the library after the call: writing it is harmless. */
+typedef struct {
+  int64_t tile_info;   /* int32 [8]: [0] tiles T, [1] the queue counter after the pass
+                          (claims * claim), [2] lists = G * nbw, [3] nch,
+                          [4] workgroups of the KV-outer pass, [5] n, [6] first row */
+  int64_t chunk_off;   /* int32 [lists * nch + 1]: exclusive scan of the KV-outer pair
+                          counts of each (group g, block b, chunk of 64 rows), list
+                          l = g * nbw + b first; list l holds entries
+                          [chunk_off[l * nch], chunk_off[(l + 1) * nch]) */
+  int64_t entries;     /* int32: row in the window << 4 | slot u, rows ascending in a list */
+  int64_t tiles;       /* int32 [T][4]: group, first entry, entry count (<= tile_queries), block */
+  int64_t tile_visits; /* int32 [T]: how many times the KV-outer pass computed each tile */
+  int64_t wg_trace;    /* int64 [workgroups][4] of the KV-outer pass: hardware id
+                          (xcc << 6 | shader engine << 4 | compute unit), tiles it
+                          computed, wall clock at its start and at its end */
+  int64_t dense_cnt;   /* int32 [G][units]: blocks the 16-row unit computes in the
+                          query-stationary (dense) pass */
+  int64_t dense_list;  /* int32 [G][units][dense_max]: those blocks, ascending */
+  int64_t dense_qmask; /* int32 [G][units][dense_max]: bit r = row r of the unit selected it */
+  int64_t dense_slots; /* int32 [G][n]: bit u = slot u of the row is computed in the dense pass */
+  int32_t dense_max;
+  int32_t tile_queries;
+  int32_t claim;       /* tiles per claim from the queue */
+  int32_t dense_min;   /* a unit's block goes to the dense pass when at least
+                          min(dense_min, rows of the unit) of its rows selected it */
+  int64_t wall_clock_khz; /* rate of the wg_trace clock (0 if the device does not report it) */
+} msa_prefill_schedule_map;
+
+/* Fills *m for the workspace of a prefill whose longest sequence has max_q_len
+ * query rows and whose longest context is max_ctx positions (msa_prefill:
+ * max_q_len = max_ctx = seq_len). MSA_ERR_INVALID_ARG for a NULL m or
+ * non-positive sizes, MSA_ERR_UNSUPPORTED where the workspace-size functions
+ * return 0. Host only; wall_clock_khz is queried from the current device. */
+msa_status msa_prefill_schedule_layout(const msa_params* p, int64_t max_q_len, int64_t max_ctx,
+                                       msa_prefill_schedule_map* m);
+
 /* Bytes of device workspace msa_decode needs. Returns 0 on invalid arguments
  * and for max_ctx above the longest supported context. */
 size_t msa_decode_workspace_bytes(const msa_params* p, int32_t batch, int64_t max_ctx);

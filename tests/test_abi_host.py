@@ -51,6 +51,26 @@ def test_workspace_sizes(lib):
     assert msa.prefill_workspace_bytes(p, 1, (1 << 20) + 1) == 0
 
 
+def test_schedule_layout_within_the_workspace(lib):
+    for bk, n, rows in [(128, 4096, 4096), (128, 1 << 20, 1 << 20), (32, 5000, 5000), (64, 200000, 3000)]:
+        p = msa.params(block_size=bk)
+        m = msa.prefill_schedule_layout(p, rows, n)
+        total = msa.prefill_varlen_workspace_bytes(p, rows, n)
+        if rows == n:
+            assert total == msa.prefill_workspace_bytes(p, 1, n)
+        offs = sorted(getattr(m, f) for f in msa._SCHED_OFFSETS)
+        assert len(set(offs)) == len(offs)
+        assert all(0 <= o < total and o % 256 == 0 for o in offs)
+        assert (m.dense_max, m.tile_queries, m.claim, m.dense_min) == (64, 16, 4, 7)
+    m = msa.MsaScheduleMap()
+    p = msa.params()
+    assert lib.msa_prefill_schedule_layout(ctypes.byref(p), 64, 64, None) == -1
+    assert lib.msa_prefill_schedule_layout(ctypes.byref(p), 0, 64, ctypes.byref(m)) == -1
+    assert lib.msa_prefill_schedule_layout(ctypes.byref(p), 64, -1, ctypes.byref(m)) == -1
+    assert lib.msa_prefill_schedule_layout(ctypes.byref(p), 64, (1 << 20) + 1, ctypes.byref(m)) == -2
+    assert lib.msa_prefill_schedule_layout(None, 64, 64, ctypes.byref(m)) == -1
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, -2), ("index_dim", 32, -2), ("block_size", 96, -2), ("block_size", 256, -2),
     ("block_size", 16, -2), ("topk", 17, -2),

@@ -1,0 +1,154 @@
+"""The reverse index and tile queue of the KV-outer pass, read back from the
+prefill workspace after a call [pnsm, section 7: KV-outer "outer gather Q";
+section 9: reverse index, pre-scheduled tile chunking, persistent queue].
+
+For the selection the call made (its sel_out), every valid (group, row, slot)
+pair must be computed exactly once: either listed in the reverse index of its
+(group, block) or covered by its 16-row unit's dense list. The sum of the
+reverse-index counts plus the dense pairs equals the number of selected pairs;
+the tiles cut every list into consecutive runs of at most 16 queries; the
+persistent pass computed every tile exactly once (its visit counts) and its
+workgroups together drained all tiles.
+
+All of this is integer bookkeeping: it is checked exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_07_amd as msa
+import msa_synth as syn
+from tests._parity import log, prefill_device_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    msa.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def check_schedule(sel: np.ndarray, sc: dict, m, bk: int) -> dict:
+    """sel: [G, n, topk] selection of a one-window call (rows 0..n-1)."""
+    G, n, topk = sel.shape
+    info = sc["tile_info"].numpy()
+    T, counter, lists, nch, nwg, rows, row0 = (int(x) for x in info[:7])
+    nbw = (n - 1) // bk + 1
+    assert (rows, row0) == (n, 0)
+    assert lists == G * nbw and nch == (n + 63) // 64
+    valid = sel >= 0
+    slot_bits = 1 << np.arange(topk)
+
+    # dense pass: per row, the slots it computes; per unit, the list of blocks
+    dslots = sc["dense_slots"].numpy()
+    dense = ((dslots[:, :, None] & slot_bits) != 0)
+    assert not (dense & ~valid).any(), "a dense slot without a selection"
+    own = sel == (np.arange(n) // bk)[None, :, None]
+    assert (own.sum(-1) == 1).all(), "every row selects its own block once"
+    assert (dense[own]).all(), "the own block is always computed in the dense pass"
+    cnt, dl, dq = sc["dense_cnt"].numpy(), sc["dense_list"].numpy(), sc["dense_qmask"].numpy()
+    units = (n + 15) // 16
+    for g in range(G):
+        for un in range(units):
+            r0, r1 = 16 * un, min(16 * un + 16, n)
+            s = sel[g, r0:r1]
+            blocks, hits = np.unique(s[s >= 0], return_counts=True)
+            want = blocks[hits >= min(m.dense_min, r1 - r0)]
+            c = int(cnt[g, un])
+            assert np.array_equal(dl[g, un, :c], want), (g, un)
+            for j, b in enumerate(want):
+                rowmask = (s == b).any(-1)
+                assert dq[g, un, j] == int((rowmask.astype(np.int64) << np.arange(r1 - r0)).sum()), (g, un, b)
+                # exactly the slots holding a dense block are dense
+            dense_blocks = np.isin(s, want)
+            assert np.array_equal(dense[g, r0:r1], dense_blocks & (s >= 0)), (g, un)
+
+    # KV-outer reverse index: list l = g*nbw + b holds (row << 4 | slot)
+    chunk_off = sc["chunk_off"].numpy().astype(np.int64)
+    entries = sc["entries"].numpy()
+    assert len(chunk_off) == lists * nch + 1 and chunk_off[0] == 0
+    assert (np.diff(chunk_off) >= 0).all()
+    kv = np.zeros_like(valid)
+    want_tiles = []
+    for l in range(lists):
+        g, b = divmod(l, nbw)
+        s0, s1 = int(chunk_off[l * nch]), int(chunk_off[(l + 1) * nch])
+        e = entries[s0:s1]
+        r, u = e >> 4, e & 15
+        assert ((r >= 0) & (r < n) & (u < topk)).all()
+        assert (sel[g, r, u] == b).all(), f"list ({g}, {b}) holds a pair that did not select it"
+        assert (np.diff(r) > 0).all(), f"list ({g}, {b}) not ascending in rows"
+        # each chunk of 64 rows lands in its own counted range
+        for c in range(nch):
+            cs0, cs1 = int(chunk_off[l * nch + c]), int(chunk_off[l * nch + c + 1])
+            assert ((entries[cs0:cs1] >> 4) // 64 == c).all()
+        assert not kv[g, r, u].any()
+        kv[g, r, u] = True
+        for j in range(0, s1 - s0, m.tile_queries):
+            want_tiles.append((g, s0 + j, min(m.tile_queries, s1 - s0 - j), b))
+    assert not (kv & dense).any(), "a pair computed by both passes"
+    assert np.array_equal(kv | dense, valid), "a selected pair computed by neither pass"
+    assert int(chunk_off[-1]) + int(dense.sum()) == int(valid.sum())
+
+    # tiles, visits, queue, workgroups
+    tiles = sc["tiles"].numpy()
+    want_tiles = np.array(want_tiles, dtype=np.int64).reshape(-1, 4)
+    assert T == len(want_tiles)
+    assert np.array_equal(tiles.astype(np.int64), want_tiles)
+    visits = sc["tile_visits"].numpy()
+    assert (visits == 1).all(), f"tiles visited {np.unique(visits, return_counts=True)}"
+    assert counter % m.claim == 0 and T <= counter <= T + 2 * m.claim * nwg
+    wg = sc["wg_trace"].numpy()
+    assert nwg >= 1 and len(wg) == nwg
+    assert int(wg[:, 1].sum()) == T
+    assert (wg[:, 3] >= wg[:, 2]).all()
+    return dict(tiles=T, kv_pairs=int(chunk_off[-1]), dense_pairs=int(dense.sum()), selected=int(valid.sum()),
+                workgroups=nwg)
+
+
+CASES = [
+    # n, block size, topk, recipe, seed
+    (16384, 128, 16, "skewed", 11),
+    (5000, 32, 16, "planted", 12),
+    (9000, 64, 7, "tiny", 13),
+    (3000, 128, 1, "tiny", 14),   # own block only: every pair dense, no tiles
+]
+
+
+@pytest.mark.parametrize("n,bk,topk,recipe,seed", CASES)
+def test_reverse_index_and_tile_queue(n, bk, topk, recipe, seed):
+    log(f"schedule n={n} B_k={bk} k={topk} {recipe} seed={seed}")
+    dims = syn.Dims(block_size=bk, topk=topk)
+    kw = dict(n_planted=4, n_hot=4) if recipe == "skewed" else {}
+    inp = syn.PrefillInputs(n, dims, seed, recipe, **kw)
+    q, k, v, qi, ki = prefill_device_inputs(inp)
+    p = msa.params(dims.num_q_heads, dims.num_kv_heads, dims.head_dim, dims.index_dim, bk, topk)
+    ws = torch.empty(msa.prefill_workspace_bytes(p, 1, n), dtype=torch.uint8, device="cuda")
+    _, sel, _ = msa.prefill(q, k, v, qi, ki, topk=topk, block_size=bk, want_sel=True, workspace=ws)
+    torch.cuda.synchronize()
+    m = msa.prefill_schedule_layout(p, n, n)
+    sc = msa.read_prefill_schedule(ws, m, dims.num_kv_heads)
+    stats = check_schedule(sel[0].cpu().numpy(), sc, m, bk)
+    log(f"  {stats}")
+    if topk == 1:
+        assert stats["tiles"] == 0 and stats["kv_pairs"] == 0
+
+
+def test_visits_reset_between_calls():
+    """A second call on the same workspace starts its visit counts from zero."""
+    n, bk, topk = 4096, 128, 16
+    dims = syn.Dims(block_size=bk, topk=topk)
+    inp = syn.PrefillInputs(n, dims, 15, "tiny")
+    q, k, v, qi, ki = prefill_device_inputs(inp)
+    p = msa.params(block_size=bk, topk=topk)
+    ws = torch.empty(msa.prefill_workspace_bytes(p, 1, n), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        _, sel, _ = msa.prefill(q, k, v, qi, ki, topk=topk, block_size=bk, want_sel=True, workspace=ws)
+    torch.cuda.synchronize()
+    m = msa.prefill_schedule_layout(p, n, n)
+    sc = msa.read_prefill_schedule(ws, m, dims.num_kv_heads)
+    check_schedule(sel[0].cpu().numpy(), sc, m, bk)
