@@ -154,9 +154,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G, window=65536):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "3f99b0d7ba2c866b",
-    "k_attn_prefill (KV-outer)": 5.342e9,
-    "k_attn_dense (dense + merge)": 4.413e9,
+    "source": "7c2f075f2c929902",
+    "k_attn_prefill (KV-outer)": 5.344e9,
+    "k_attn_dense (dense + merge)": 4.410e9,
 }
 
 
@@ -312,6 +312,19 @@ def summarize_rocprof(d):
                     lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                                  f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                                  f"{float(r['TotalDurationNs']) / 1e6:10.3f}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        # the same kernel runs at several shapes in one process: split by grid
+        lines.append(f"## dispatches by grid ({os.path.basename(f)})")
+        lines.append(f"{'kernel':60s} {'grid':>18s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+        by = defaultdict(list)
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if keep(r["Kernel_Name"]):
+                    grid = "x".join(r.get(k, "?") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"))
+                    by[(r["Kernel_Name"][:60], grid)].append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for (name, grid), us in sorted(by.items()):
+            lines.append(f"{name:60s} {grid:>18s} {len(us):6d} {np.mean(us):10.2f} {min(us):10.2f} {max(us):10.2f}")
     for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         lines.append(f"## counters per dispatch ({os.path.basename(f)})")
         agg = defaultdict(list)
@@ -773,6 +786,8 @@ def main():
                          "context measurements (ceilings, top-k comparison)")
     ap.add_argument("--no-parity", action="store_true",
                     help="skip the oracle check of the timed calls' outputs (profiling runs)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="run only the long configurations and print their JSON (profiling runs of those shapes)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
@@ -790,6 +805,9 @@ def main():
         sys.exit(1)
     msa.load()
     dev = torch.device("cuda:0")
+    if args.configs_only:
+        print(json.dumps({"configs": long_configs(torch, msa, args.steps)}), flush=True)
+        return
     t0 = time.time()
     pin, pre, dec_in, dec = make_inputs(torch, dev)
     torch.cuda.synchronize()
