@@ -93,19 +93,6 @@ __device__ __forceinline__ uint64_t block_elems(int b, int bk, int G, int g) {
   return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(b * bk * G + g) * kHeadDim;
 }
 
-// Load i (0 .. 8*nwaves/4 - 1) of the fast path below: K (even i) or V (odd
-// i) of row group i/2; for spreading a full block's loads over compute.
-__device__ __forceinline__ void stage_piece(lds_char* stage, const uint16_t* kr0, const uint16_t* vr0,
-                                            int64_t rstride, int wave, int nwaves, const StageOffsets& off, int i) {
-  const int it = i >> 1;
-  const int s0 = wave * 64 + it * nwaves * 64;
-  const int64_t e = (int64_t)it * 4 * nwaves * rstride;
-  if (i & 1)
-    lds_dma16_s(vr0 + e, off.v, stage + kVOff + s0 * 16);
-  else
-    lds_dma16_s(kr0 + e, off.k, stage + s0 * 16);
-}
-
 // A whole block (128 keys) per stage. A full block is loaded from uniform
 // bases and the precomputed offsets (nwaves a multiple of 4); a partial one
 // (the sequence's last) clamps its rows.
@@ -838,7 +825,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   // two K/V stages, then 256 bytes per wave for the partials' lse
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage + kAttnWaves * 256];
   lds_char* lds = (lds_char*)lds_raw;
-  const int unit = blockIdx.x, g = blockIdx.y;
+  // (group, unit) in group-major order, contiguous per XCD
+  const int item = xcd_item(blockIdx.x, nunits * G);
+  const int g = item / nunits, unit = item - g * nunits;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
@@ -1117,7 +1106,7 @@ void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
 
 template <int BK>
 static void launch_attn_dense_bk(const LaunchAttnDense& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_dense<BK>, dim3(a.nunits, a.G), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v,
+  hipLaunchKernelGGL(k_attn_dense<BK>, dim3(a.nunits * a.G), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v,
                      a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.part_o, a.part_lse, a.out,
                      a.lse_out, a.n_tokens, a.row0, a.nrows, a.nunits, a.G, a.topk, a.scale_log2);
 }

@@ -125,6 +125,19 @@ __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(
 // Cross-lane exchange within a wave (ds_bpermute based).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Work item of workgroup w in a one-dimensional grid of n workgroups, so that
+// each XCD runs a contiguous run of items: the dispatcher hands workgroups to
+// the kXcd XCDs in turn (w mod kXcd), and XCD x is given the items after those
+// of XCDs 0 .. x-1 (each holds n/kXcd of them, the first n mod kXcd one more).
+// Neighbouring items, which read the same K/V blocks, then share one L2.
+// A bijection of [0, n) for any n.
+constexpr int kXcd = 8;
+__device__ __forceinline__ int xcd_item(int w, int n) {
+  const int x = w % kXcd, k = w / kXcd;
+  const int q = n / kXcd, r = n % kXcd;
+  return x * q + min(x, r) + k;
+}
+
 // max over the four lanes l ^ {0, 16, 32, 48} (the four lane groups of an
 // MFMA 16x16 fragment column): v_permlane32_swap then v_permlane16_swap with
 // both operands x return x of the partner half / row in one of the two
