@@ -26,7 +26,7 @@ EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_prefill_varlen_wo
             "msa_select_blocks", "msa_status_string", "msa_index_project_workspace_bytes", "msa_index_project",
             "msa_index_project_decode", "msa_decode_noalloc", "msa_prefill_schedule_layout")
 PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
-DECODE_STAGES = ("index_score", "select", "attn")
+DECODE_STAGES = ("index_score", "select_attn")
 
 
 class MsaParams(ctypes.Structure):

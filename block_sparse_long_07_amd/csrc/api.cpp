@@ -8,8 +8,8 @@
 //   (combine).
 // Windows bound the workspace (block scores and partials grow with the rows of
 // a window, not with the sequence), which is what makes 1M-token prefill fit.
-// Decode: index scores -> selection -> per-(sequence, group) attention over the
-// selected blocks (online softmax across them; no partials).
+// Decode: index scores -> per-(sequence, group) selection and attention over
+// the selected blocks in one kernel (online softmax across them; no partials).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -177,7 +177,7 @@ bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
 
 struct DecodeLayout {
   int nb;
-  size_t sblk, sel, total;
+  size_t sblk, total;
 };
 
 // max_ctx beyond the longest supported context has no layout (the caller
@@ -185,10 +185,8 @@ struct DecodeLayout {
 bool decode_layout(const Shape& s, int32_t B, int64_t max_ctx, DecodeLayout* L) {
   if (B <= 0 || max_ctx <= 0 || max_ctx > s.max_seq) return false;
   L->nb = (int)cdiv(max_ctx, s.bk);
-  const size_t items = (size_t)B * s.G * s.k;
   size_t off = 0;
   L->sblk = off;     off += up((size_t)B * s.G * L->nb * sizeof(float));
-  L->sel = off;      off += up(items * sizeof(int32_t));
   L->total = off;
   return true;
 }
@@ -589,18 +587,14 @@ msa_status run_decode(const msa_params* p, int32_t batch, int64_t max_ctx, const
   (void)hipGetLastError();
   StageClock clk{ev, hs};
   clk.mark();
-  int32_t* sel = sel_out ? sel_out : at<int32_t>(workspace, L.sel);
   LaunchIndexDecode ia{static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx_cache), ctx_lens,
                        at<float>(workspace, L.sblk), max_ctx, L.nb, batch, s.G, s.k, s.bk};
   launch_index_decode(ia, hs);
   clk.mark();
-  LaunchSelect sa{at<float>(workspace, L.sblk), L.nb, sel, s.k, (int64_t)s.G * s.k, batch, s.G, s.k, 0, ctx_lens,
-                  s.bk_shift};
-  launch_select(sa, hs);
-  clk.mark();
+  // selection and attention in one kernel
   LaunchAttnDecode aa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                      static_cast<const uint16_t*>(v_cache), ctx_lens, sel, static_cast<uint16_t*>(out), lse_out,
-                      max_ctx, batch, s.G, s.k, s.scale_log2, s.bk};
+                      static_cast<const uint16_t*>(v_cache), ctx_lens, at<float>(workspace, L.sblk), L.nb, sel_out,
+                      static_cast<uint16_t*>(out), lse_out, max_ctx, batch, s.G, s.k, s.scale_log2, s.bk};
   launch_attn_decode(aa, hs);
   clk.mark();
   return finish();
@@ -627,7 +621,7 @@ msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_c
   std::vector<hipEvent_t> ev;
   msa_status st = run_decode(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out,
                              lse_out, workspace, workspace_bytes, stream, &ev);
-  return collect(ev, 3, stage_ms, st);
+  return collect(ev, 2, stage_ms, st);
 }
 
 size_t msa_index_kl_workspace_bytes(const msa_params* p, int64_t seq_len) {

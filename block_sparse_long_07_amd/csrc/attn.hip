@@ -37,6 +37,7 @@
 
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "topk_row.h"
 
 namespace msa {
 
@@ -1007,22 +1008,26 @@ __global__ __launch_bounds__(512, 1) void k_attn_dense(
   }
 }
 
-// Decode: one workgroup per (sequence, group). Its selected blocks stream
-// through two LDS stages (all four waves issue the direct-to-LDS loads of the
-// next block while wave 0 computes the current one), and wave 0 keeps the
-// group's 16 heads in one online-softmax state across the blocks (the own
-// block, the last in ascending order, with the causal mask), so the output
-// and lse are written at the end with no partials and no separate combine.
-// Only cache rows below ctx_len are staged (later rows may hold anything).
+// Decode: one workgroup per (sequence, group). It first selects its row's
+// blocks from the pooled index scores (the own block plus the k-1 best older
+// ones, ranked by its four waves; written to sel_out when given), then the
+// selected blocks stream through two LDS stages (all four waves issue the
+// direct-to-LDS loads of the next block while wave 0 computes the current
+// one), and wave 0 keeps the group's 16 heads in one online-softmax state
+// across the blocks (the own block, the last in ascending order, with the
+// causal mask), so the output and lse are written at the end with no partials
+// and no separate combine. Only cache rows below ctx_len are staged (later
+// rows may hold anything).
+constexpr int kDecWaves = 4;
 template <int BK>
-__global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k,
-                                                     const uint16_t* __restrict__ v,
-                                                     const int32_t* __restrict__ ctx_lens,
-                                                     const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
-                                                     float* __restrict__ lse_out, int64_t max_ctx, int G, int topk,
-                                                     float scale_log2) {
+__global__ __launch_bounds__(kDecWaves * 64) void k_attn_decode(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ ctx_lens, const float* __restrict__ sblk, int nb, int32_t* __restrict__ sel_out,
+    uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t max_ctx, int G, int topk, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
+  __shared__ float s_sv[kDecWaves * (kMaxTopk - 1)];
+  __shared__ int s_si[kDecWaves * (kMaxTopk - 1)];
+  __shared__ int s_sel[kMaxTopk];
   lds_char* lds = (lds_char*)lds_raw;
   const int item = blockIdx.x;  // sq * G + g
   const int sq = item / G, g = item % G;
@@ -1034,14 +1039,25 @@ __global__ __launch_bounds__(256) void k_attn_decode(const uint16_t* __restrict_
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
   const int64_t seq0 = (int64_t)sq * max_ctx * G * kHeadDim + (int64_t)g * kHeadDim;
+  // the selection: every block when there are at most k, else the k-1 best
+  // older blocks (ascending) and the own block
+  if (b_loc < topk) {
+    if (wave == 0 && lane < topk) s_sel[lane] = lane <= b_loc ? lane : -1;
+  } else {
+    select_row_rt<kDecWaves>(sblk + (int64_t)item * nb, b_loc, topk - 1, s_sv, s_si, s_sel);
+    if (wave == 0 && lane == 0) s_sel[topk - 1] = b_loc;
+  }
+  __syncthreads();
   // lane u holds slot u of the selection (ascending; the first nsel are valid)
-  const int lane_blk = lane < topk ? sel[(int64_t)item * topk + lane] : 0;
+  const int lane_blk = lane < topk ? s_sel[lane] : 0;
+  if (sel_out && wave == 0 && lane < topk) sel_out[(int64_t)item * topk + lane] = lane_blk;
   const StageOffsets soff = stage_offsets(rstride, wave);
   auto stage = [&](int u, lds_char* dst) {
     const int b = __builtin_amdgcn_readlane(lane_blk, u);
     const int64_t key0 = (int64_t)b * BK;
     const int64_t base = seq0 + key0 * rstride;
-    stage_block_bk<BK>(dst, k + base, v + base, rstride, (int)min<int64_t>(BK, i + 1 - key0), wave, 4, soff);
+    stage_block_bk<BK>(dst, k + base, v + base, rstride, (int)min<int64_t>(BK, i + 1 - key0), wave, kDecWaves,
+                       soff);
   };
   stage(0, lds);
   QueryGroup<1> qg;
@@ -1123,8 +1139,8 @@ void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {
 
 template <int BK>
 static void launch_attn_decode_bk(const LaunchAttnDecode& a, hipStream_t st, int items) {
-  hipLaunchKernelGGL(k_attn_decode<BK>, dim3(items), dim3(256), 0, st, a.q, a.k, a.v, a.ctx_lens, a.sel, a.out,
-                     a.lse_out, a.max_ctx, a.G, a.topk, a.scale_log2);
+  hipLaunchKernelGGL(k_attn_decode<BK>, dim3(items), dim3(kDecWaves * 64), 0, st, a.q, a.k, a.v, a.ctx_lens,
+                     a.sblk, a.nb, a.sel_out, a.out, a.lse_out, a.max_ctx, a.G, a.topk, a.scale_log2);
 }
 
 void launch_attn_decode(const LaunchAttnDecode& a, hipStream_t st) {

@@ -134,7 +134,9 @@ struct LaunchAttnDecode {
   const uint16_t* k;      // [batch, max_ctx, G, 128]
   const uint16_t* v;
   const int32_t* ctx_lens;
-  const int32_t* sel;     // [(s*G + g)*topk + u]
+  const float* sblk;      // pooled index scores, row s*G + g of nb
+  int nb;
+  int32_t* sel_out;       // optional [(s*G + g)*topk + u]
   uint16_t* out;          // [batch, Hq, 128]
   float* lse_out;         // optional [batch, Hq]
   int64_t max_ctx;

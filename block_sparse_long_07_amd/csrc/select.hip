@@ -21,46 +21,11 @@
 
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "topk_row.h"
 
 namespace msa {
 
 constexpr int64_t kWaveRowsMax = 16384;
-
-// One step of a symmetric arg-max butterfly inside 16-lane rows: lane i meets
-// lane xor 1 (step 0), xor 2 (1), 7-i within its 8-lane half (2), 15-i (3),
-// all DPP moves; after the four steps every lane of the row holds the row's
-// best (score desc, index asc).
-template <int STEP>
-__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
-  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), ctrl, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_update_dpp(bi, bi, ctrl, 0xF, 0xF, false);
-  const bool take = ov > bv || (ov == bv && oi < bi);
-  bv = take ? ov : bv;
-  bi = take ? oi : bi;
-}
-__device__ __forceinline__ void argmax_row16(float& bv, int& bi) {
-  argmax_step<0>(bv, bi);
-  argmax_step<1>(bv, bi);
-  argmax_step<2>(bv, bi);
-  argmax_step<3>(bv, bi);
-}
-// across the four rows of a wave: v_permlane16_swap / v_permlane32_swap hand
-// each lane its partner's pair (lane xor 16, then xor 32)
-__device__ __forceinline__ void argmax_rows(float& bv, int& bi) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const auto sv = h ? __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false)
-                      : __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-    const auto si = h ? __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false)
-                      : __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
-    const float v0 = __uint_as_float(sv[0]), v1 = __uint_as_float(sv[1]);
-    const int i0 = (int)si[0], i1 = (int)si[1];
-    const bool take1 = v1 > v0 || (v1 == v0 && i1 < i0);
-    bv = take1 ? v1 : v0;
-    bi = take1 ? i1 : i0;
-  }
-}
 
 template <int KM1>
 __global__ __launch_bounds__(256) void k_select(const float* __restrict__ sblk, int nb,
@@ -102,7 +67,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ sblk, 
           bool shift = false;
 #pragma unroll
           for (int t = 0; t < KM1; ++t) {
-            shift = shift || (cv > v[t]);
+            shift |= cv > v[t];
             const float nv = shift ? cv : v[t];
             const int ni = shift ? ci : id[t];
             cv = shift ? v[t] : cv;
@@ -206,7 +171,7 @@ __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sb
           bool shift = false;
 #pragma unroll
           for (int t = 0; t < KM1; ++t) {
-            shift = shift || (cv > v[t]);
+            shift |= cv > v[t];
             const float nv = shift ? cv : v[t];
             const int ni = shift ? ci : id[t];
             cv = shift ? v[t] : cv;
@@ -255,26 +220,19 @@ __global__ __launch_bounds__(64) void k_select_wave(const float* __restrict__ sb
   }
 }
 
-// Few rows with very many candidates (long decode contexts): NW waves per
-// row. Wave w ranks the candidates b = 64w + lane + 64*NW*j like
-// k_select_wave and reduces its 64 lane lists to its own best k-1 (by k-1
-// wave arg-max rounds), which go to LDS; wave 0 then ranks the NW*(k-1)
-// survivors (the row's best k-1 are among them: each wave kept its subset's
-// best under the same total order) and writes the selection. The survivors
-// do not arrive in index order, so this second ranking compares (score
-// descending, index ascending) in full.
-__device__ __forceinline__ bool before(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
-}
-
+// Few rows with very many candidates (long contexts): NW waves per row,
+// ranked by select_row_rt (each wave's best k-1, then the row's best k-1
+// among the NW*(k-1) survivors, which do not arrive in index order and are
+// therefore compared by score and index in full).
 template <int KM1, int NW>
 __global__ __launch_bounds__(64 * NW) void k_select_multi(const float* __restrict__ sblk, int nb,
                                                           int32_t* __restrict__ sel, int64_t sel_gstride,
                                                           int64_t sel_rstride, int G, int64_t row0,
                                                           const int32_t* __restrict__ ctx_lens, int bk_shift) {
   static_assert(KM1 > 0, "k >= 2");
-  __shared__ float sv[NW * KM1];
-  __shared__ int si[NW * KM1];
+  __shared__ float sv[NW * (kMaxTopk - 1)];
+  __shared__ int si[NW * (kMaxTopk - 1)];
+  __shared__ int picks[kMaxTopk];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r = blockIdx.x;
   const int64_t rr = r / G;
@@ -285,88 +243,12 @@ __global__ __launch_bounds__(64 * NW) void k_select_multi(const float* __restric
     if (wave == 0 && lane <= KM1) out[lane] = (lane <= b_loc) ? lane : -1;
     return;
   }
-  float v[KM1];
-  int id[KM1];
-#pragma unroll
-  for (int t = 0; t < KM1; ++t) {
-    v[t] = -__builtin_inff();
-    id[t] = 0x7fffffff;
-  }
-  auto insert = [&](float cv, int ci) {
-    if (!before(cv, ci, v[KM1 - 1], id[KM1 - 1])) return;
-    bool shift = false;
-#pragma unroll
-    for (int t = 0; t < KM1; ++t) {
-      shift = shift || before(cv, ci, v[t], id[t]);
-      const float nv = shift ? cv : v[t];
-      const int ni = shift ? ci : id[t];
-      cv = shift ? v[t] : cv;
-      ci = shift ? id[t] : ci;
-      v[t] = nv;
-      id[t] = ni;
-    }
-  };
-  auto pop_best = [&]() {  // wave-wide arg-max of the list heads; the winner pops
-    float bv = v[0];
-    int bi = id[0];
-    argmax_row16(bv, bi);
-    argmax_rows(bv, bi);
-    if (id[0] == bi) {
-#pragma unroll
-      for (int t = 0; t + 1 < KM1; ++t) {
-        v[t] = v[t + 1];
-        id[t] = id[t + 1];
-      }
-      v[KM1 - 1] = -__builtin_inff();
-      id[KM1 - 1] = 0x7fffffff;
-    }
-    return std::pair<float, int>(bv, bi);
-  };
-  const float* row = sblk + r * (int64_t)nb;
-  constexpr int kBatch = 16;
-  constexpr int kStride = 64 * NW;
-  for (int b0 = wave * 64 + lane; b0 < b_loc; b0 += kStride * kBatch) {
-    float cand[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) cand[u] = b0 + kStride * u < b_loc ? row[b0 + kStride * u] : -__builtin_inff();
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (b0 + kStride * u < b_loc) insert(cand[u], b0 + kStride * u);
-  }
-#pragma unroll
-  for (int rd = 0; rd < KM1; ++rd) {
-    const auto best = pop_best();
-    if (lane == 0) {
-      sv[wave * KM1 + rd] = best.first;
-      si[wave * KM1 + rd] = best.second;
-    }
-  }
-  __syncthreads();
+  select_row_rt<NW>(sblk + r * (int64_t)nb, b_loc, KM1, sv, si, picks);
   if (wave != 0) return;
-#pragma unroll
-  for (int t = 0; t < KM1; ++t) {
-    v[t] = -__builtin_inff();
-    id[t] = 0x7fffffff;
-  }
-  for (int j = lane; j < NW * KM1; j += 64) insert(sv[j], si[j]);
-  int chosen[KM1];
-#pragma unroll
-  for (int rd = 0; rd < KM1; ++rd) chosen[rd] = pop_best().second;
-#pragma unroll
-  for (int a = 0; a < KM1; ++a) {
-#pragma unroll
-    for (int t = 0; t + 1 < KM1 - a; ++t) {
-      const int lo = min(chosen[t], chosen[t + 1]);
-      const int hi = max(chosen[t], chosen[t + 1]);
-      chosen[t] = lo;
-      chosen[t + 1] = hi;
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int u = 0; u < KM1; ++u) out[u] = chosen[u];
-    out[KM1] = b_loc;
-  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's picks are in LDS
+  __builtin_amdgcn_wave_barrier();
+  if (lane < KM1) out[lane] = picks[lane];
+  if (lane == 0) out[KM1] = b_loc;
 }
 
 void launch_select(const LaunchSelect& a, hipStream_t st) {

@@ -214,11 +214,11 @@ msa_status msa_decode(const msa_params* p, int32_t batch, int64_t max_ctx,
  * array of MSA_DECODE_NOALLOC_WORKSPACE_BYTES that the library holds on each
  * device it runs on (from the first call there until the process ends). A
  * call whose msa_decode_workspace_bytes exceeds it returns
- * MSA_ERR_UNSUPPORTED (64 sequences at 128K positions take 1.1 MiB, 8 at
- * 1M 1.1 MiB: pooled block scores and the selection; at most about 500
- * sequences of 128K fit). Calls on one device share the array: calls that overlap in
- * time on one device race (serialise them on one stream). The results are
- * those of msa_decode: the same kernels run. */
+ * MSA_ERR_UNSUPPORTED (the pooled block scores: 64 sequences at 128K
+ * positions take 1 MiB, 8 at 1M 1 MiB; at most 512 sequences of 128K fit).
+ * Calls on one device share the array: calls that overlap in time on one
+ * device race (serialise them on one stream). The results are those of
+ * msa_decode: the same kernels run. */
 #define MSA_DECODE_NOALLOC_WORKSPACE_BYTES ((size_t)8 << 20)
 msa_status msa_decode_noalloc(const msa_params* p, int32_t batch, int64_t max_ctx,
                               const void* q, const void* q_idx,
@@ -234,8 +234,10 @@ msa_status msa_decode_noalloc(const msa_params* p, int32_t batch, int64_t max_ct
  *   prefill (5): index scores, top-k selection, reverse index + tile schedule,
  *                KV-outer attention, attention over the blocks each 16-row
  *                unit shares with the merge of the KV-outer partials (combine)
- *   decode  (3): index scores, top-k selection, attention (over the selected
- *                blocks of each sequence and group, merged as they stream)
+ *   decode  (2): index scores; top-k selection with the attention over the
+ *                selected blocks of each sequence and group (one kernel:
+ *                each workgroup ranks its own row, then merges the blocks
+ *                as they stream)
  * stage_ms must not be NULL (MSA_ERR_INVALID_ARG). */
 msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len,
                                 const void* q, const void* k, const void* v,
