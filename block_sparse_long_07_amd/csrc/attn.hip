@@ -1027,6 +1027,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_attn_decode(
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
   __shared__ float s_sv[kDecWaves * (kMaxTopk - 1)];
   __shared__ int s_si[kDecWaves * (kMaxTopk - 1)];
+  __shared__ int s_cnt[2 * kDecWaves];
+  __shared__ int s_tmp[kMaxTopk];
+  __shared__ int s_ctr;
   __shared__ int s_sel[kMaxTopk];
   lds_char* lds = (lds_char*)lds_raw;
   const int item = blockIdx.x;  // sq * G + g
@@ -1041,37 +1044,53 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_attn_decode(
   const int64_t seq0 = (int64_t)sq * max_ctx * G * kHeadDim + (int64_t)g * kHeadDim;
   // the selection: every block when there are at most k, else the k-1 best
   // older blocks (ascending) and the own block
-  if (b_loc < topk) {
-    if (wave == 0 && lane < topk) s_sel[lane] = lane <= b_loc ? lane : -1;
-  } else {
-    select_row_rt<kDecWaves>(sblk + (int64_t)item * nb, b_loc, topk - 1, s_sv, s_si, s_sel);
-    if (wave == 0 && lane == 0) s_sel[topk - 1] = b_loc;
-  }
-  __syncthreads();
-  // lane u holds slot u of the selection (ascending; the first nsel are valid)
-  const int lane_blk = lane < topk ? s_sel[lane] : 0;
-  if (sel_out && wave == 0 && lane < topk) sel_out[(int64_t)item * topk + lane] = lane_blk;
   const StageOffsets soff = stage_offsets(rstride, wave);
-  auto stage = [&](int u, lds_char* dst) {
-    const int b = __builtin_amdgcn_readlane(lane_blk, u);
+  auto stage_blk = [&](int b, lds_char* dst) {
     const int64_t key0 = (int64_t)b * BK;
     const int64_t base = seq0 + key0 * rstride;
     stage_block_bk<BK>(dst, k + base, v + base, rstride, (int)min<int64_t>(BK, i + 1 - key0), wave, kDecWaves,
                        soff);
   };
-  stage(0, lds);
+  // the own block is known before the ranking: it is staged (and attended)
+  // first, its loads issued once the ranking has read its candidates, so
+  // they overlap the ranking
+  auto stage_own = [&] { stage_blk(b_loc, lds); };
   QueryGroup<1> qg;
   if (wave == 0) {
     load_q(qg, 0, q + ((int64_t)sq * Hq + g * kHpg + c) * kHeadDim + 8 * qd);
     reset_state(qg);
   }
+  if (b_loc < topk) {
+    stage_own();
+    if (wave == 0 && lane < topk) s_sel[lane] = lane <= b_loc ? lane : -1;
+  } else {
+    const float* row = sblk + (int64_t)item * nb;
+    // up to 2048 candidates: a threshold search over the four waves (at 1024,
+    // 9 us against 13 us for k-1 wave-wide pops; wave 0 alone took 19 us);
+    // beyond, where the search's per-step barriers and counts cost more than
+    // the pops, k-1 rounds over per-lane sorted lists
+    if (b_loc <= 4 * 64 * kDecWaves)
+      select_row_thr<kDecWaves, 4>(row, b_loc, topk - 1, s_cnt, s_tmp, &s_ctr, s_sel, stage_own);
+    else if (b_loc <= 8 * 64 * kDecWaves)
+      select_row_thr<kDecWaves, 8>(row, b_loc, topk - 1, s_cnt, s_tmp, &s_ctr, s_sel, stage_own);
+    else
+      select_row_rt<kDecWaves>(row, b_loc, topk - 1, s_sv, s_si, s_sel, stage_own);
+    if (wave == 0 && lane == 0) s_sel[topk - 1] = b_loc;
+  }
+  lds_barrier();  // (the own block's loads stay in flight)
+  // lane u holds slot u of the selection (ascending; the first nsel are valid,
+  // the own block last)
+  const int lane_blk = lane < topk ? s_sel[lane] : 0;
+  if (sel_out && wave == 0 && lane < topk) sel_out[(int64_t)item * topk + lane] = lane_blk;
+  // visit order: the own block, then the older blocks ascending
+  auto block_at = [&](int u) { return u == 0 ? b_loc : __builtin_amdgcn_readlane(lane_blk, u - 1); };
   for (int u = 0; u < nsel; ++u) {
     wait_loads();
     __syncthreads();  // stage u&1 complete; stage (u+1)&1 free
-    if (u + 1 < nsel) stage(u + 1, lds + ((u + 1) & 1) * kStage);
+    if (u + 1 < nsel) stage_blk(block_at(u + 1), lds + ((u + 1) & 1) * kStage);
     if (wave != 0) continue;
     const lds_char* st = lds + (u & 1) * kStage;
-    if (u + 1 < nsel) {  // an older block: every key is before the query
+    if (u > 0) {  // an older block: every key is before the query
       if constexpr (BK == kBlock) {
         KHalf k0;
         load_k_half(k0, st);

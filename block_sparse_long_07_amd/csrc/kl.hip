@@ -62,16 +62,6 @@ __device__ __forceinline__ void kl_sched_region() {
   }
 }
 
-// Workgroup barrier for LDS data: this wave's LDS operations complete, then
-// s_barrier. Unlike __syncthreads it does not wait for outstanding global
-// loads, so data prefetched into registers stays in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // f(integral_constant<int, I>) for I = B .. E-1, in order.
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {

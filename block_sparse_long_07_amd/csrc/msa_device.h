@@ -71,6 +71,17 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
   }
 }
 
+// Workgroup barrier for LDS data: this wave's LDS operations complete, then
+// s_barrier. Unlike __syncthreads it does not wait for outstanding global
+// loads, so loads in flight (into registers or direct to LDS) stay in flight
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void lds_dma16(const void* src, const lds_char* lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :

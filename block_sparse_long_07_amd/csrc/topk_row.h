@@ -117,11 +117,12 @@ __device__ __forceinline__ void list_clear(float (&v)[L], int (&id)[L]) {
 // entries); wave 0 then ranks the NW*km1 survivors the same way (the row's
 // best km1 are among them: each wave kept its subset's best) and pops the
 // row's best km1, writing their block ids to out[0 .. km1-1] (LDS) in
-// ascending order. One workgroup barrier inside; out is complete for wave 0
-// on return (other waves read it after a barrier of their own).
-template <int NW>
+// ascending order. One workgroup barrier (LDS only) inside; out is complete for wave 0
+// on return (other waves read it after a barrier of their own). after_loads()
+// runs in every wave once the candidates are read.
+template <int NW, class F = void (*)()>
 __device__ __forceinline__ void select_row_rt(const float* __restrict__ row, int b_loc, int km1, float* sv,
-                                              int* si, int* out) {
+                                              int* si, int* out, F after_loads = [] {}) {
   constexpr int L = kMaxTopk - 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float v[L];
@@ -137,6 +138,7 @@ __device__ __forceinline__ void select_row_rt(const float* __restrict__ row, int
     for (int u = 0; u < kBatch; ++u)
       if (b0 + kStride * u < b_loc) list_insert_asc(v, id, cand[u], b0 + kStride * u);
   }
+  after_loads();
   for (int rd = 0; rd < km1; ++rd) {
     float bv = v[0];
     int bi = id[0];
@@ -148,7 +150,7 @@ __device__ __forceinline__ void select_row_rt(const float* __restrict__ row, int
     }
     list_pop_if(v, id, bi);
   }
-  __syncthreads();
+  lds_barrier();
   if (wave != 0) return;
   // the survivors (wave w's rd-th best at w*L + rd, rd < km1) into wave 0's
   // lane lists, then km1 rounds over the list heads
@@ -168,6 +170,92 @@ __device__ __forceinline__ void select_row_rt(const float* __restrict__ row, int
   int rank = 0;
   for (int j = 0; j < km1; ++j) rank += __builtin_amdgcn_readlane(pick, j) < pick;
   if (lane < km1) out[rank] = pick;
+}
+
+// Exact top km1 of the candidates row[0 .. b_loc-1] (score descending, index
+// ascending) by a threshold search over the workgroup's NW waves, C
+// candidates per lane (b_loc <= 64*NW*C): candidate b = (j*NW + w)*64 + l
+// sits in slot j of lane l of wave w, as the order-preserving image of its
+// score (-0 folded onto +0; 0 for no candidate, below every score). T, the
+// km1-th largest image, is found bit by bit from the top (the largest t with
+// at least km1 images >= t), each count a sum of ballot popcounts over the
+// slots and, across waves, through LDS (cnt: 2*NW ints). Every image above T
+// is taken; if more than km1 images reach T, the ties at T go by index: X,
+// the (km1 - #above)-th tie in index order, is found the same way over the
+// index bits. The picks are gathered in LDS (tmp: kMaxTopk ints, ctr: one
+// int) and wave 0 writes them to out[0 .. km1-1] in ascending order. Every
+// thread of the workgroup calls (NW is 1 or the workgroup's wave count; with
+// NW = 1 the search has no barrier); out is complete for wave 0 on return.
+// after_loads() runs in every wave once the candidates are read (for the
+// caller's own memory traffic, which then overlaps the ranking).
+template <int NW, int C, class F = void (*)()>
+__device__ __forceinline__ void select_row_thr(const float* __restrict__ row, int b_loc, int km1, int* cnt,
+                                               int* tmp, int* ctr, int* out, F after_loads = [] {}) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave >= NW) {  // (NW = 1: wave 0 ranks alone, the others wait)
+    after_loads();
+    lds_barrier();
+    return;
+  }
+  uint32_t key[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int b = (j * NW + wave) * 64 + lane;
+    key[j] = b < b_loc ? ord_f32(row[b] + 0.0f) : 0u;
+  }
+  after_loads();
+  if (threadIdx.x == 0) *ctr = 0;
+  int it = 0;
+  // number of candidates over the workgroup whose slot passes `pred`
+  auto total = [&](auto pred) -> int {
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) c += __builtin_popcountll(__ballot(pred(j)));
+    if constexpr (NW == 1) return c;
+    int* slot = cnt + (it++ & 1) * NW;
+    if (lane == 0) slot[wave] = c;
+    lds_barrier();  // (the other half of cnt is free: every wave has read it before this barrier)
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += slot[w];
+    return sum;
+  };
+  uint32_t T = 0;
+  int n_ge = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = T | (1u << bit);
+    const int n = total([&](int j) { return key[j] >= t; });
+    if (n >= km1) {
+      T = t;
+      n_ge = n;
+    }
+  }
+  // ties at T: the first (km1 - #above) by index
+  int X = 0x7fffffff;
+  if (n_ge > km1) {
+    const int n_gt = total([&](int j) { return key[j] > T; });
+    const int need = km1 - n_gt;
+    X = 0;  // the largest X with fewer than `need` ties below index X
+    for (int bit = 20; bit >= 0; --bit) {
+      const int x = X | (1 << bit);
+      const int n = total([&](int j) { return key[j] == T && (j * NW + wave) * 64 + lane < x; });
+      if (n < need) X = x;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int b = (j * NW + wave) * 64 + lane;
+    if (key[j] > T || (key[j] == T && b <= X)) tmp[atomicAdd(ctr, 1)] = b;
+  }
+  lds_barrier();
+  if (wave != 0) return;
+  // ascending: lane r < km1 ranks pick r among the picks
+  if (lane < km1) {
+    const int x = tmp[lane];
+    int rank = 0;
+    for (int j = 0; j < km1; ++j) rank += tmp[j] < x;
+    out[rank] = x;
+  }
 }
 
 }  // namespace msa

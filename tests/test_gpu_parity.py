@@ -205,6 +205,38 @@ def test_decode_128k_bench_config():
     decode_case(64, 131072, None, 16, 0, "decode 64x128K")
 
 
+@pytest.mark.parametrize("zero_blocks", [False, True])
+def test_decode_selection_ties(zero_blocks):
+    """Integer index projections make every pooled score exact in fp32, with
+    many equal scores (all zero outside a few blocks when zero_blocks): the
+    selection must equal the oracle's (ties to the lower block index) for
+    contexts whose candidate counts span every size class of the ranking."""
+    G, topk = 4, 16
+    lens = [1000, 130000, 200000, 400000, 600000, 1000000]
+    B, max_ctx = len(lens), max(lens)
+    g = torch.Generator(device="cuda").manual_seed(7 + zero_blocks)
+    qi = torch.randint(-1, 2, (B, G, 64), generator=g, device="cuda").to(torch.bfloat16)
+    kic = torch.randint(-1, 2, (B, max_ctx, 64), generator=g, device="cuda").to(torch.bfloat16)
+    if zero_blocks:
+        keep = torch.zeros(max_ctx // 128 + 1, dtype=torch.bool, device="cuda")
+        keep[torch.randint(0, keep.numel(), (40,), generator=g, device="cuda")] = True
+        kic = kic * keep.repeat_interleave(128)[:max_ctx][None, :, None].to(kic.dtype)
+    q = torch.randn((B, G * 16, 128), generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.randn((B, max_ctx, G, 128), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((B, max_ctx, G, 128), generator=g, device="cuda").to(torch.bfloat16)
+    q, qi, kc, vc, kic = (t.contiguous() for t in (q, qi, kc, vc, kic))
+    lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, sel, lse = msa.decode(q, qi, kc, vc, kic, lens_d, topk=topk, want_sel=True, want_lse=True)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        ref = mo.decode_seq(mo.to_f64(q[b]), mo.to_f64(qi[b]), mo.to_f64(kic[b, :L]), _RowsF64(kc[b]),
+                            _RowsF64(vc[b]), L, block_size=128, topk=topk)
+        got = sel[b].cpu().numpy()
+        assert np.array_equal(got, ref["sel"]), f"seq {b} (ctx {L}): {got} vs {ref['sel']}"
+        compare_out(out[b], ref["out"], f"ties seq{b}")
+        compare_lse(lse[b], ref["lse"], f"ties seq{b}")
+
+
 # ---- bench-size prefill (sampled rows) ---------------------------------------
 
 @pytest.mark.timeout(900)
