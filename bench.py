@@ -154,9 +154,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G, window=65536):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "7c2f075f2c929902",
+    "source": "376b1a26f4e828c9",
     "k_attn_prefill (KV-outer)": 5.344e9,
-    "k_attn_dense (dense + merge)": 4.410e9,
+    "k_attn_dense (dense + merge)": 3.937e9,
 }
 
 
