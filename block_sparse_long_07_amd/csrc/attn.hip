@@ -162,10 +162,14 @@ struct QueryGroup {
   float m[QN];
 };
 
+// Vector memory instructions load_q issues (one 16-byte load per d-step, at
+// per-lane addresses: always vector loads), for callers that wait on a
+// counted vmcnt.
+constexpr int kLoadQOps = 4;
 template <class QG>
 __device__ __forceinline__ void load_q(QG& qg, int n, const uint16_t* qrow) {
 #pragma unroll
-  for (int st = 0; st < 4; ++st) qg.qop[n][st] = as_bf16x8(ld16(qrow + 32 * st));
+  for (int st = 0; st < kLoadQOps; ++st) qg.qop[n][st] = as_bf16x8(ld16(qrow + 32 * st));
 }
 
 // Running state before the first block: reference max -inf, zero accumulators.
@@ -557,7 +561,10 @@ __device__ __forceinline__ void attend_short(QG& qg, const lds_char* stage, cons
 // Softmax partial of one query, normalised, in fragment order: element (head
 // c, dim 16dt + 4qd + r) sits at dt*256 + (16qd + c)*4 + r of the 2048-element
 // slot, so each of the eight stores of a wave writes 512 contiguous bytes.
-// lse2 = m*c + log2(l) per head (c = scale * log2 e).
+// lse2 = m*c + log2(l) per head (c = scale * log2 e). It issues
+// kStorePartialOps vector memory instructions: the 8 fragment stores (512 B
+// apart per lane, never merged) and the lse store.
+constexpr int kStorePartialOps = 9;
 __device__ __forceinline__ void store_partial(const f32x4 (&o)[9], float m, float scale_log2, uint16_t* dst,
                                               float* lse16) {
   const int lane = threadIdx.x & 63, c = lane & 15, qd = lane >> 4;
@@ -729,7 +736,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
       fetch_q(ent, cur.g);
     }
   }
-  int after_dma = 0;  // vector memory operations issued after the last stage load
+  // vector memory operations issued after the last stage load, counted from
+  // the operations they certainly are (an over-count would let the wait pass
+  // with stage loads still in flight)
+  int after_dma = 0;
   int drained = 0;    // tiles this workgroup computed
   for (int j = 0; cur.t < T; ++j) {
     wait_vmcnt_upto(after_dma);  // the stage of tile j is in
@@ -762,7 +772,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     int nent[kAttnQN] = {0, 0};
     if (next_work) {
       read_entries(nxt, nent);
-      after_dma += kAttnQN + 4 * kAttnQN;  // entries, then their Q below
+      // their Q, below (the entries are not counted: their address is
+      // wave-uniform, so they may be scalar loads, which vmcnt does not
+      // track; left out, a vector load only makes the wait stronger)
+      after_dma += kAttnQN * kLoadQOps;
     }
     if (e0 < cur.len) {
       // once the scores no longer need Q, the next tile's is loaded
@@ -778,7 +791,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
         if (e0 + n < cur.len) {
           const int64_t slot = ((int64_t)(ent[n] >> 4) * G + cur.g) * topk + (ent[n] & 15);
           store_partial(qg.o[n], qg.m[n], scale_log2, part_o + slot * kHpg * kHeadDim, part_lse + slot * kHpg);
-          after_dma += 9;  // 8 partial stores + the lse store
+          after_dma += kStorePartialOps;
         }
       }
     } else if (next_work) {
