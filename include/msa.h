@@ -73,7 +73,13 @@ typedef struct {
 
 /* Bytes of device workspace msa_prefill needs for `batch` sequences of
  * `seq_len` tokens (the same for any batch: sequences are processed in turn).
- * Returns 0 for invalid or unsupported arguments. */
+ * Returns 0 for invalid or unsupported arguments. Query rows are processed in
+ * windows of at most 65536; the workspace is dominated by the KV-outer
+ * partials, sized for every (row, group, slot) of one window (4160 bytes
+ * each: 16 heads x 128 bf16 plus 16 fp32 lse), and by the pooled block scores
+ * of a window, which grow with the sequence. At 4 groups and k = 16: 1.0 GiB
+ * at 4K tokens, 8.3 GiB at 32K, 16.8 GiB at 64K, 17.3 GiB at 128K, 24.5 GiB
+ * at 1M. */
 size_t msa_prefill_workspace_bytes(const msa_params* p, int32_t batch, int64_t seq_len);
 
 /* Causal MSA prefill of `batch` independent sequences of `seq_len` tokens: for
