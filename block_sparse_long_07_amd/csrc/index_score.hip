@@ -276,8 +276,10 @@ static void launch_prefill_ns(const LaunchIndexPrefill& a, hipStream_t st) {
                      a.sblk, a.row0, a.row_end, a.qb_begin, a.qb_end, a.nb);
 }
 
-// Chunk length: two stages unless that makes more than kManyChunks
-// workgroups, then 8 or 16.
+// Chunk length: two stages for small calls (up to kFewChunks workgroups of
+// two), else 8, or 16 beyond 8 * kManyChunks (32K prefill: 2, 4, 8 stages
+// measured 0.238, 0.223, 0.213 ms).
+constexpr int64_t kFewChunks = 1 << 12;
 constexpr int64_t kManyChunks = 1 << 16;
 
 template <int G, int SUB>
@@ -287,7 +289,7 @@ static void launch_prefill_g(const LaunchIndexPrefill& a, hipStream_t st) {
     launch_prefill_ns<G, SUB, 1>(a, st);
   } else {
     const int64_t w2 = chunks_before(a.qb_end, 2) - chunks_before(a.qb_begin, 2);
-    if (w2 <= kManyChunks)
+    if (w2 <= kFewChunks)
       launch_prefill_ns<G, SUB, 2>(a, st);
     else if (w2 <= 8 * kManyChunks)
       launch_prefill_ns<G, SUB, 8>(a, st);
