@@ -24,7 +24,8 @@ EXPORTED = ("msa_prefill_workspace_bytes", "msa_prefill", "msa_prefill_varlen_wo
             "msa_prefill_varlen", "msa_decode_workspace_bytes", "msa_decode", "msa_prefill_profiled",
             "msa_decode_profiled", "msa_index_kl_workspace_bytes", "msa_index_kl_backward", "msa_index_scores",
             "msa_select_blocks", "msa_status_string", "msa_index_project_workspace_bytes", "msa_index_project",
-            "msa_index_project_decode", "msa_decode_noalloc", "msa_prefill_schedule_layout")
+            "msa_index_project_decode", "msa_decode_noalloc", "msa_prefill_schedule_layout",
+            "msa_prefill_timed", "msa_decode_timed", "msa_stage_timer_read")
 PREFILL_STAGES = ("index_score", "select", "reverse_index", "kv_outer_attn", "dense_attn_merge")
 DECODE_STAGES = ("index_score", "select_attn")
 
@@ -99,6 +100,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_index_project.restype = ctypes.c_int
     lib.msa_index_project_decode.argtypes = [P, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_index_project_decode.restype = ctypes.c_int
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    lib.msa_prefill_timed.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vpp]
+    lib.msa_prefill_timed.restype = ctypes.c_int
+    lib.msa_decode_timed.argtypes = [P, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vpp]
+    lib.msa_decode_timed.restype = ctypes.c_int
+    lib.msa_stage_timer_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
+    lib.msa_stage_timer_read.restype = ctypes.c_int
     lib.msa_prefill_schedule_layout.argtypes = [P, i64, i64, ctypes.POINTER(MsaScheduleMap)]
     lib.msa_prefill_schedule_layout.restype = ctypes.c_int
     lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -142,10 +150,13 @@ def prefill_workspace_bytes(p: MsaParams, batch: int, seq_len: int) -> int:
 
 def prefill(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale=None,
             want_sel=False, want_lse=False, workspace: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None, stage_ms: Optional[list] = None):
+            out: Optional[torch.Tensor] = None, stage_ms: Optional[list] = None,
+            stage_timers: Optional[list] = None):
     """Causal MSA prefill. q [B,N,Hq,d], k/v [B,N,G,d], q_idx [B,N,G,d_idx],
     k_idx [B,N,d_idx], all bf16 on one device. Returns (out, sel or None, lse or None).
-    With stage_ms (a list) the profiled entry point runs, synchronises, and the
+    With stage_timers (a list) the timed entry point runs without synchronising
+    and a handle is appended; read_stage_timers() later gives the per-stage
+    milliseconds. With stage_ms (a list) the profiled entry point runs, synchronises, and the
     per-stage milliseconds (PREFILL_STAGES order) are appended to it."""
     lib = load()
     B, N, Hq, d = q.shape
@@ -165,7 +176,11 @@ def prefill(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale=Non
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     args = (ctypes.byref(p), B, N, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
             _ptr(out), _ptr(sel), _ptr(lse), _ptr(workspace), nbytes, _stream(dev))
-    if stage_ms is None:
+    if stage_timers is not None:
+        h = ctypes.c_void_p()
+        _check(lib.msa_prefill_timed(*args, ctypes.byref(h)), "msa_prefill_timed")
+        stage_timers.append((h, len(PREFILL_STAGES)))
+    elif stage_ms is None:
         _check(lib.msa_prefill(*args), "msa_prefill")
     else:
         ms = (ctypes.c_float * len(PREFILL_STAGES))()
@@ -261,7 +276,7 @@ def decode_workspace_bytes(p: MsaParams, batch: int, max_ctx: int) -> int:
 def decode(q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, *, topk=16, block_size=128,
            softmax_scale=None, want_sel=False, want_lse=False,
            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-           stage_ms: Optional[list] = None):
+           stage_ms: Optional[list] = None, stage_timers: Optional[list] = None):
     """One decode step. q [B,Hq,d], q_idx [B,G,d_idx], k_cache/v_cache
     [B,max_ctx,G,d], k_idx_cache [B,max_ctx,d_idx] (bf16), ctx_lens int32 [B]
     on the device (the new token is row ctx_lens[b]-1). Returns (out, sel, lse)."""
@@ -286,13 +301,30 @@ def decode(q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, *, topk=16, block_
     args = (ctypes.byref(p), B, max_ctx, _ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache),
             _ptr(k_idx_cache), _ptr(ctx_lens), _ptr(out), _ptr(sel), _ptr(lse),
             _ptr(workspace), nbytes, _stream(dev))
-    if stage_ms is None:
+    if stage_timers is not None:
+        h = ctypes.c_void_p()
+        _check(lib.msa_decode_timed(*args, ctypes.byref(h)), "msa_decode_timed")
+        stage_timers.append((h, len(DECODE_STAGES)))
+    elif stage_ms is None:
         _check(lib.msa_decode(*args), "msa_decode")
     else:
         ms = (ctypes.c_float * len(DECODE_STAGES))()
         _check(lib.msa_decode_profiled(*args, ms), "msa_decode_profiled")
         stage_ms.extend(float(x) for x in ms)
     return out, sel, lse
+
+
+def read_stage_timers(timers: list) -> list:
+    """Per-stage milliseconds of each handle that prefill/decode appended to
+    `timers` (waits for each call's last event; every handle is released)."""
+    lib = load()
+    res = []
+    for h, n in timers:
+        ms = (ctypes.c_float * n)()
+        _check(lib.msa_stage_timer_read(h, ms), "msa_stage_timer_read")
+        res.append([float(x) for x in ms])
+    timers.clear()
+    return res
 
 
 def decode_noalloc(q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, *, topk=16, block_size=128,

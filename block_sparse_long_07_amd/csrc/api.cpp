@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <new>
 #include <vector>
 
 #include "api_internal.h"
@@ -477,6 +478,52 @@ msa_status msa_prefill(const msa_params* p, int32_t batch, int64_t seq_len, cons
                      stream, nullptr);
 }
 
+}  // extern "C"
+
+// Stage events of a *_timed call, read (and released) by msa_stage_timer_read.
+struct msa_stage_timer {
+  std::vector<hipEvent_t> ev;
+  int nstage;
+};
+
+namespace {
+
+msa_status keep_timer(std::vector<hipEvent_t>& ev, int nstage, msa_status st, msa_stage_timer** timer) {
+  *timer = nullptr;
+  if (st == MSA_OK) {
+    msa_stage_timer* t = new (std::nothrow) msa_stage_timer{std::move(ev), nstage};
+    if (t) {
+      *timer = t;
+      return MSA_OK;
+    }
+    st = MSA_ERR_HIP;
+  }
+  for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_prefill_timed(const msa_params* p, int32_t batch, int64_t seq_len, const void* q, const void* k,
+                             const void* v, const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
+                             float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                             msa_stage_timer** timer) {
+  if (!timer) return MSA_ERR_INVALID_ARG;
+  std::vector<hipEvent_t> ev;
+  msa_status st = run_prefill(p, batch, seq_len, q, k, v, q_idx, k_idx, out, sel_out, lse_out, workspace,
+                              workspace_bytes, stream, &ev);
+  return keep_timer(ev, 5, st, timer);
+}
+
+msa_status msa_stage_timer_read(msa_stage_timer* timer, float* stage_ms) {
+  if (!timer || !stage_ms) return MSA_ERR_INVALID_ARG;
+  msa_status st = collect(timer->ev, timer->nstage, stage_ms, MSA_OK);
+  delete timer;
+  return st;
+}
+
 msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len, const void* q,
                                 const void* k, const void* v, const void* q_idx, const void* k_idx, void* out,
                                 int32_t* sel_out, float* lse_out, void* workspace, size_t workspace_bytes,
@@ -622,6 +669,17 @@ msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_c
   msa_status st = run_decode(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out,
                              lse_out, workspace, workspace_bytes, stream, &ev);
   return collect(ev, 2, stage_ms, st);
+}
+
+msa_status msa_decode_timed(const msa_params* p, int32_t batch, int64_t max_ctx, const void* q, const void* q_idx,
+                            const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                            const int32_t* ctx_lens, void* out, int32_t* sel_out, float* lse_out, void* workspace,
+                            size_t workspace_bytes, void* stream, msa_stage_timer** timer) {
+  if (!timer) return MSA_ERR_INVALID_ARG;
+  std::vector<hipEvent_t> ev;
+  msa_status st = run_decode(p, batch, max_ctx, q, q_idx, k_cache, v_cache, k_idx_cache, ctx_lens, out, sel_out,
+                             lse_out, workspace, workspace_bytes, stream, &ev);
+  return keep_timer(ev, 2, st, timer);
 }
 
 size_t msa_index_kl_workspace_bytes(const msa_params* p, int64_t seq_len) {

@@ -244,13 +244,34 @@ msa_status msa_decode_noalloc(const msa_params* p, int32_t batch, int64_t max_ct
  *                selected blocks of each sequence and group (one kernel:
  *                each workgroup ranks its own row, then merges the blocks
  *                as they stream)
- * stage_ms must not be NULL (MSA_ERR_INVALID_ARG). */
+ * stage_ms must not be NULL (MSA_ERR_INVALID_ARG).
+ *
+ * The *_timed variants record the same stage events but return at once,
+ * without synchronising (so back-to-back calls keep the GPU busy): *timer
+ * receives a handle that msa_stage_timer_read later turns into stage_ms
+ * (waiting for the call's last event) and releases. Every handle must be
+ * read exactly once; on an error status no handle is returned. */
 msa_status msa_prefill_profiled(const msa_params* p, int32_t batch, int64_t seq_len,
                                 const void* q, const void* k, const void* v,
                                 const void* q_idx, const void* k_idx,
                                 void* out, int32_t* sel_out, float* lse_out,
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 float* stage_ms);
+typedef struct msa_stage_timer msa_stage_timer;
+msa_status msa_prefill_timed(const msa_params* p, int32_t batch, int64_t seq_len,
+                             const void* q, const void* k, const void* v,
+                             const void* q_idx, const void* k_idx,
+                             void* out, int32_t* sel_out, float* lse_out,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             msa_stage_timer** timer);
+msa_status msa_decode_timed(const msa_params* p, int32_t batch, int64_t max_ctx,
+                            const void* q, const void* q_idx,
+                            const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                            const int32_t* ctx_lens,
+                            void* out, int32_t* sel_out, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            msa_stage_timer** timer);
+msa_status msa_stage_timer_read(msa_stage_timer* timer, float* stage_ms);
 msa_status msa_decode_profiled(const msa_params* p, int32_t batch, int64_t max_ctx,
                                const void* q, const void* q_idx,
                                const void* k_cache, const void* v_cache, const void* k_idx_cache,

@@ -51,6 +51,22 @@ def test_workspace_sizes(lib):
     assert msa.prefill_workspace_bytes(p, 1, (1 << 20) + 1) == 0
 
 
+def test_timed_entry_points_reject_before_launching(lib):
+    p = msa.params()
+    h = ctypes.c_void_p(123)
+    none = [None] * 8
+    # null timer
+    assert lib.msa_prefill_timed(ctypes.byref(p), 1, 1024, *none, None, 0, None, None) == -1
+    # bad arguments: status returned, no handle
+    assert lib.msa_prefill_timed(ctypes.byref(p), 1, 1024, *none, None, 0, None, ctypes.byref(h)) == -1
+    assert h.value is None
+    h = ctypes.c_void_p(123)
+    assert lib.msa_decode_timed(ctypes.byref(p), 0, 1024, *([None] * 9), None, 0, None, ctypes.byref(h)) == -1
+    assert h.value is None
+    ms = (ctypes.c_float * 5)()
+    assert lib.msa_stage_timer_read(None, ms) == -1
+
+
 def test_schedule_layout_within_the_workspace(lib):
     for bk, n, rows in [(128, 4096, 4096), (128, 1 << 20, 1 << 20), (32, 5000, 5000), (64, 200000, 3000)]:
         p = msa.params(block_size=bk)

@@ -123,3 +123,34 @@ def test_decode_nondefault_scale(scale):
         assert np.array_equal(sel[b].cpu().numpy(), ref["sel"]), f"seq {b}"
         compare_out(out[b], ref["out"], f"decode scale {scale} seq{b}")
         compare_lse(lse[b], ref["lse"], f"decode scale {scale} seq{b}")
+
+
+def test_timed_entry_points_match_plain_calls():
+    """msa_prefill_timed / msa_decode_timed run the same kernels as the plain
+    calls (bit-identical outputs) and hand back one timer per call whose
+    stages are positive and add up to about the call."""
+    n = 3000
+    inp = syn.PrefillInputs(n, dims(4, 16), 21, "planted", n_planted=4)
+    pre = prefill_device_inputs(inp)
+    want, _, _ = msa.prefill(*pre)
+    timers = []
+    outs = [msa.prefill(*pre, stage_timers=timers)[0].clone() for _ in range(3)]
+    runs = msa.read_stage_timers(timers)
+    assert timers == [] and len(runs) == 3
+    for o, r in zip(outs, runs):
+        assert torch.equal(o, want)
+        assert len(r) == len(msa.PREFILL_STAGES) and all(x > 0 for x in r)
+
+    B, L = 4, 5000
+    dec = syn.DecodeInputs(B, L, syn.Dims(), 22, ctx_lens=[5000, 4097, 300, 2])
+    q = torch.stack([dec.q(b, "cuda") for b in range(B)]).contiguous()
+    qi = torch.stack([dec.q_idx(b, "cuda") for b in range(B)]).contiguous()
+    kc = torch.stack([dec.k_cache(b, device="cuda") for b in range(B)]).contiguous()
+    vc = torch.stack([dec.v_cache(b, device="cuda") for b in range(B)]).contiguous()
+    kic = torch.stack([dec.k_idx_cache(b, device="cuda") for b in range(B)]).contiguous()
+    lens = torch.tensor(dec.ctx_lens, dtype=torch.int32, device="cuda")
+    want, wsel, _ = msa.decode(q, qi, kc, vc, kic, lens, want_sel=True)
+    got, gsel, _ = msa.decode(q, qi, kc, vc, kic, lens, want_sel=True, stage_timers=timers)
+    (r,) = msa.read_stage_timers(timers)
+    assert torch.equal(got, want) and torch.equal(gsel, wsel)
+    assert len(r) == len(msa.DECODE_STAGES) and all(x > 0 for x in r)
