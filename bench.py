@@ -154,9 +154,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G, window=65536):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "376b1a26f4e828c9",
-    "k_attn_prefill (KV-outer)": 5.344e9,
-    "k_attn_dense (dense + merge)": 3.937e9,
+    "source": "d532b79222db4666",
+    "k_attn_prefill (KV-outer)": 5.349e9,
+    "k_attn_dense (dense + merge)": 3.938e9,
 }
 
 
@@ -318,10 +318,15 @@ def summarize_rocprof(d):
             for r in csv.DictReader(fh):
                 if keep(r["Kernel_Name"]):
                     grid = "x".join(r.get(k, "?") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"))
-                    by[(r["Kernel_Name"][:60], grid)].append(
-                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        for (name, grid), us in sorted(by.items()):
+                    t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                    by[(r["Kernel_Name"][:60], grid)].append((t0, (t1 - t0) / 1e3))
+        for (name, grid), ev in sorted(by.items()):
+            us = [d for _, d in ev]
             lines.append(f"{name:60s} {grid:>18s} {len(us):6d} {np.mean(us):10.2f} {min(us):10.2f} {max(us):10.2f}")
+        lines.append(f"## attention dispatches in launch order, us ({os.path.basename(f)})")
+        for (name, grid), ev in sorted(by.items()):
+            if "k_attn_" in name and len(ev) <= 24:
+                lines.append(f"{name[:60]:60s} " + " ".join(f"{d:.1f}" for _, d in sorted(ev)))
     for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         lines.append(f"## counters per dispatch ({os.path.basename(f)})")
         agg = defaultdict(list)
