@@ -208,7 +208,7 @@ def read_prefill_schedule(workspace: torch.Tensor, m: MsaScheduleMap, num_kv_hea
         nbytes = count * torch.empty((), dtype=dtype).element_size()
         return workspace[off:off + nbytes].view(dtype).cpu()
 
-    info = part("tile_info", 8)
+    info = part("tile_info", 16)
     T, lists, nch, nwg, n = (int(info[i]) for i in (0, 2, 3, 4, 5))
     G, units = num_kv_heads, (n + 15) // 16
     chunk_off = part("chunk_off", lists * nch + 1)

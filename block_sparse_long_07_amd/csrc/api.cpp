@@ -79,6 +79,14 @@ int cu_count() {
   return cached[dev];
 }
 
+// Workgroups of the persistent dense pass: one per CU (a multiple of the 8
+// XCDs, at least 8, so that every XCD's range of items has one), no more
+// than the items need.
+int dense_grid(int64_t items) {
+  const int64_t cap = std::max<int64_t>(8, cu_count() / 8 * 8);
+  return (int)std::min<int64_t>(cap, std::max<int64_t>(8, (items + 7) / 8 * 8));
+}
+
 // entries of rows [a, b): G * sum_i min(k, floor(i/B_k) + 1)
 int64_t entries_in(int64_t a, int64_t b, int G, int k, int bk) {
   int64_t e = 0;
@@ -122,7 +130,7 @@ bool prefill_layout(const Shape& s, int64_t n_ctx, int64_t max_rows, PrefillLayo
   L->entries = off;    off += up((size_t)L->e_cap * sizeof(int32_t));
   L->tile_start = off; off += up((size_t)((int64_t)s.G * L->nb + 1) * sizeof(int32_t));
   L->tiles = off;      off += up((size_t)L->tile_cap * 4 * sizeof(int32_t));
-  L->tile_info = off;  off += up(8 * sizeof(int32_t));
+  L->tile_info = off;  off += up(16 * sizeof(int32_t));
   L->tile_visits = off; off += up((size_t)L->tile_cap * sizeof(int32_t));
   L->wg_trace = off;   off += up((size_t)kMaxPersistent * 4 * sizeof(int64_t));
   L->part_o = off;     off += up((size_t)L->slots * kHpg * kHeadDim * sizeof(uint16_t));
@@ -165,7 +173,7 @@ bool kl_layout(const Shape& s, int64_t N, KlLayout* L) {
   L->entries = off;    off += up((size_t)L->e_cap * sizeof(int32_t));
   L->tile_start = off; off += up((size_t)((int64_t)s.G * L->nb + 1) * sizeof(int32_t));
   L->chunks = off;     off += up((size_t)L->chunk_cap * 4 * sizeof(int32_t));
-  L->chunk_info = off; off += up(8 * sizeof(int32_t));
+  L->chunk_info = off; off += up(16 * sizeof(int32_t));
   L->part_m = off;     off += up((size_t)L->slots * sizeof(float));
   L->part_l = off;     off += up((size_t)L->slots * sizeof(float));
   L->loss_part = off;  off += up((size_t)L->slots * sizeof(float));
@@ -327,7 +335,8 @@ void prefill_window(const Shape& s, const PrefillLayout& L, const SeqIO& io, int
   LaunchAttnDense da{qw, io.k, io.v, dcnt, dlist, at<int32_t>(workspace, L.dense_qmask),
                      at<int32_t>(workspace, L.dense_slots), at<uint16_t>(workspace, L.part_o),
                      at<float>(workspace, L.part_lse), io.out + r0 * Hq * kHeadDim,
-                     io.lse ? io.lse + r0 * Hq : nullptr, n_ctx, w0, (int)Wn, nunits, G, K, s.scale_log2, s.bk};
+                     io.lse ? io.lse + r0 * Hq : nullptr, n_ctx, w0, (int)Wn, nunits, G, K, s.scale_log2, s.bk,
+                     at<int32_t>(workspace, L.tile_info), dense_grid((int64_t)nunits * G)};
   launch_attn_dense(da, hs);
   clk.mark();
 }

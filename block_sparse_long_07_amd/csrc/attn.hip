@@ -829,195 +829,290 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
 // every row's output and lse are written here, once, without atomics (the
 // second phase of the two-phase combine [pnsm, section 7]):
 //   out = o / l,   lse = (m*c + log2 l) * ln 2.
+// The grid is persistent (one workgroup per CU) and the (group, unit) items
+// are split into kXcd contiguous ranges, one per XCD, each drained through a
+// counter of its own (queue[x], zero before the pass): units that share K/V
+// blocks then meet in one L2, and while a unit's partials are merged the next
+// unit's list, slots and Q are already loading; its first block streams in
+// right after the unit's output is stored. A workgroup whose range is drained
+// takes items from the other ranges in turn. tile_info[8 + x] is range x's
+// counter (zeroed with the tile queue); tile_info[7] gets the grid size.
 template <int BK>
 __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ dense_cnt, const int32_t* __restrict__ dense_list,
     const int32_t* __restrict__ dense_qmask, const int32_t* __restrict__ dense_slots, const uint16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out, int64_t n_tokens,
-    int64_t row0, int nrows, int nunits, int G, int topk, float scale_log2) {
-  // two K/V stages, then 256 bytes per wave for the partials' lse
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage + kAttnWaves * 256];
+    int64_t row0, int nrows, int nunits, int G, int topk, float scale_log2,
+    int32_t* __restrict__ tile_info) {
+  // two K/V stages, 256 bytes per wave for the partials' lse, then the next
+  // unit's metadata (768 bytes + 256 per wave)
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage + kAttnWaves * 256 + 768 + kAttnWaves * 256];
+  __shared__ int s_next[2];
   lds_char* lds = (lds_char*)lds_raw;
-  // (group, unit) in group-major order, contiguous per XCD
-  const int item = xcd_item(blockIdx.x, nunits * G);
-  const int g = item / nunits, unit = item - g * nunits;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, qd = lane >> 4;
   const int Hq = G * kHpg;
   const int64_t rstride = (int64_t)G * kHeadDim;
   const StageOffsets soff = stage_offsets(rstride, wave);
-  const int64_t list0 = ((int64_t)g * nunits + unit) * kDenseMax;
-  const int i_rel0 = unit * 16 + wave * kAttnQN;
-  const int b_loc = (int)((row0 + unit * 16) / BK);
-  const int nsel = min(topk, b_loc + 1);
+  // items (group, unit) in group-major order, split into kXcd ranges; range
+  // r is [r*q + min(r, rm), + q + (r < rm)). XCD x = blockIdx.x mod kXcd (the
+  // dispatcher's order: only the locality depends on it) drains range x
+  // first, then the others (victim: the range it currently takes from).
+  // Claims are made by thread 0.
+  const int nitems = nunits * G;
+  const int iq = nitems / kXcd, rm = nitems % kXcd;
+  int victim = blockIdx.x % kXcd;
+  auto claim_from = [&](int r) -> int {
+    const int t = atomicAdd(tile_info + 8 + r, 1);
+    return t < iq + (r < rm ? 1 : 0) ? r * iq + min(r, rm) + t : -1;
+  };
+  // (waits for each claim: used where the result is needed at once)
+  auto claim_any = [&]() -> int {
+    for (int t = 0; t < kXcd; ++t) {
+      const int it = claim_from(victim);
+      if (it >= 0) return it;
+      victim = victim + 1 < kXcd ? victim + 1 : 0;
+    }
+    return -1;
+  };
 
-  // independent loads first: the unit's list and the rows that selected each
-  // entry (lane j holds entry j, read back with a uniform readlane; entries
-  // past the count are not used), its count, and the queries' Q
-  const int lane_blk = dense_list[list0 + lane];
-  const int lane_qm = dense_qmask[list0 + lane];
-  const int nd = dense_cnt[g * nunits + unit];  // >= 1: the unit's own block
+  // a unit's list and the rows that selected each entry (lane j holds entry
+  // j, read back with a uniform readlane; entries past the count are not
+  // used), its count and its rows' dense slots; then the queries' Q
+  int lane_blk = 0, lane_qm = 0, nd = 0;
+  int slots[kAttnQN];
   QueryGroup<kAttnQN> qg;
+  auto unit_loads = [&](int it) {
+    const int ug = it / nunits, uu = it - ug * nunits;
+    const int64_t l0 = ((int64_t)ug * nunits + uu) * kDenseMax;
+    lane_blk = dense_list[l0 + lane];
+    lane_qm = dense_qmask[l0 + lane];
+    nd = dense_cnt[ug * nunits + uu];  // >= 1: the unit's own block
 #pragma unroll
-  for (int n = 0; n < kAttnQN; ++n) {
-    const int64_t i_rel = min(i_rel0 + n, nrows - 1);
-    load_q(qg, n, q + ((i_rel * Hq) + g * kHpg + c) * kHeadDim + 8 * qd);
-  }
-  {
+    for (int n = 0; n < kAttnQN; ++n)
+      slots[n] = dense_slots[(int64_t)ug * nrows + min(uu * 16 + wave * kAttnQN + n, nrows - 1)];
+  };
+  auto unit_q = [&](int it) {
+    const int ug = it / nunits, uu = it - ug * nunits;
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) {
+      const int64_t i_rel = min(uu * 16 + wave * kAttnQN + n, nrows - 1);
+      load_q(qg, n, q + ((i_rel * Hq) + ug * kHpg + c) * kHeadDim + 8 * qd);
+    }
+  };
+  // The same metadata of the next unit copied into LDS (meta: list, row
+  // masks, count, then 256 bytes of slots per wave), so that no registers hold
+  // it during the current unit's last block and merges, and read back.
+  lds_char* meta = lds + 2 * kStage + kAttnWaves * 256;
+  auto meta_loads = [&](int it) {
+    const int ug = it / nunits, uu = it - ug * nunits;
+    const int64_t l0 = ((int64_t)ug * nunits + uu) * kDenseMax;
+    if (wave == 0) lds_dma4(dense_list + l0 + lane, meta);
+    if (wave == 1) lds_dma4(dense_qmask + l0 + lane, meta + 256);
+    if (wave == 2) lds_dma4(dense_cnt + ug * nunits + uu, meta + 512);
+    lds_dma4(dense_slots + (int64_t)ug * nrows + min(uu * 16 + wave * kAttnQN + (lane & 1), nrows - 1),
+             meta + 768 + wave * 256);
+  };
+  auto meta_read = [&]() {
+    typedef __attribute__((address_space(3))) const int lds_int;
+    lane_blk = ((lds_int*)meta)[lane];
+    lane_qm = ((lds_int*)(meta + 256))[lane];
+    nd = __builtin_amdgcn_readfirstlane(((lds_int*)(meta + 512))[0]);
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) slots[n] = ((lds_int*)(meta + 768 + wave * 256))[n];
+  };
+  // the unit's first block into stage 0 (every wave)
+  auto stage_first = [&](int it) {
+    const int ug = it / nunits;
     const int b0 = __builtin_amdgcn_readfirstlane(lane_blk);
-    const uint64_t e0 = block_elems(b0, BK, G, g);
-    stage_block_bk<BK>(lds, k + e0, v + e0, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)b0 * BK), wave,
+    const uint64_t e = block_elems(b0, BK, G, ug);
+    stage_block_bk<BK>(lds, k + e, v + e, rstride, (int)min<int64_t>(BK, n_tokens - (int64_t)b0 * BK), wave,
                        kAttnWaves, soff);
-  }
-  // slots of each query's selection computed KV-outer: the valid ones the
-  // dense pass does not cover
-  uint32_t use[kAttnQN];
-#pragma unroll
-  for (int n = 0; n < kAttnQN; ++n) {
-    const int i_rel = i_rel0 + n;
-    use[n] = 0u;
-    if (i_rel < nrows)
-      use[n] = (uint32_t)__builtin_amdgcn_readfirstlane(~dense_slots[(int64_t)g * nrows + i_rel]) &
-               ((1u << nsel) - 1u);
-  }
-  reset_state(qg);
+  };
 
-  // KV-outer partials of the wave's queries, in (query, slot) order, merged
-  // after the last block (below). Merging them between blocks instead costs
-  // more: the waves' partial counts differ, and every block's barrier then
-  // waits for the wave with the most.
-  lds_char* lse_side = lds + 2 * kStage + wave * 256;  // [region][partial][16 heads] fp32
-  // (wave-uniform bookkeeping, kept in scalar registers; slot indices fit 32
-  // bits: rows * G * topk of a window)
-  int cur_n = 0;
-  uint32_t cur_rem = use[0];
-  auto next_pair = [&](int& pn, int64_t& slot) -> bool {
+  if (tid == 0) {
+    if (blockIdx.x == 0) tile_info[7] = gridDim.x;
+    s_next[0] = claim_any();
+  }
+  __syncthreads();
+  int item = s_next[0];
+  if (item < 0) return;
+  unit_loads(item);
+  unit_q(item);
+  stage_first(item);
+  for (int par = 1;; par ^= 1) {
+    const int g = item / nunits, unit = item - g * nunits;
+    const int i_rel0 = unit * 16 + wave * kAttnQN;
+    const int b_loc = (int)((row0 + unit * 16) / BK);
+    const int nsel = min(topk, b_loc + 1);
+    // the next item from the current range, claimed now and waited for only
+    // where it is published
+    int claimed = -1;
+    if (tid == 0) claimed = claim_from(victim);
+    // slots of each query's selection computed KV-outer: the valid ones the
+    // dense pass does not cover
+    uint32_t use[kAttnQN];
 #pragma unroll
-    for (int n = 1; n < kAttnQN; ++n)
-      if (cur_rem == 0u && cur_n == n - 1) {
-        cur_n = n;
-        cur_rem = use[n];
+    for (int n = 0; n < kAttnQN; ++n)
+      use[n] = i_rel0 + n < nrows ? (uint32_t)__builtin_amdgcn_readfirstlane(~slots[n]) & ((1u << nsel) - 1u) : 0u;
+    reset_state(qg);
+
+    // KV-outer partials of the wave's queries, in (query, slot) order, merged
+    // after the last block (below). Merging them between blocks instead costs
+    // more: the waves' partial counts differ, and every block's barrier then
+    // waits for the wave with the most.
+    lds_char* lse_side = lds + 2 * kStage + wave * 256;  // [region][partial][16 heads] fp32
+    // (wave-uniform bookkeeping, kept in scalar registers; slot indices fit 32
+    // bits: rows * G * topk of a window)
+    int cur_n = 0;
+    uint32_t cur_rem = use[0];
+    auto next_pair = [&](int& pn, int64_t& slot) -> bool {
+#pragma unroll
+      for (int n = 1; n < kAttnQN; ++n)
+        if (cur_rem == 0u && cur_n == n - 1) {
+          cur_n = n;
+          cur_rem = use[n];
+        }
+      if (cur_rem == 0u) return false;
+      const int pu = __builtin_ctz(cur_rem);
+      cur_rem &= cur_rem - 1u;
+      pn = cur_n;
+      slot = (uint32_t)__builtin_amdgcn_readfirstlane(((i_rel0 + cur_n) * G + g) * topk + pu);
+      return true;
+    };
+
+    // shared older blocks (unmasked), then the unit's own block (masked)
+    for (int d = 0; d + 1 < nd; ++d) {
+      wait_loads();
+      __syncthreads();  // stage d&1 complete; stage (d+1)&1 free
+      KHalf k0;
+      if constexpr (BK == kBlock) load_k_half(k0, lds + (d & 1) * kStage);
+      // block d+1 streams into the other stage, loaded by waves 0-3 only (one
+      // per SIMD): their partners start computing while they wait for room in
+      // the memory queue
+      const int b2 = __builtin_amdgcn_readlane(lane_blk, d + 1);
+      const uint64_t e2 = block_elems(b2, BK, G, g);
+      if (wave < 4)
+        stage_block_bk<BK>(lds + ((d + 1) & 1) * kStage, k + e2, v + e2, rstride,
+                           (int)min<int64_t>(BK, n_tokens - (int64_t)b2 * BK), wave, 4, soff);
+      // queries of the wave that did not select the block are masked; a wave
+      // with none that did skips it
+      const unsigned skip =
+          ~((unsigned)__builtin_amdgcn_readlane(lane_qm, d) >> (wave * kAttnQN)) & ((1u << kAttnQN) - 1u);
+      if (skip != (1u << kAttnQN) - 1u) {
+        if constexpr (BK == kBlock)
+          attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [](int) {});
+        else
+          attend_short<false, false, BK / 16>(qg, lds + (d & 1) * kStage, nullptr, scale_log2, skip, [](int) {});
       }
-    if (cur_rem == 0u) return false;
-    const int pu = __builtin_ctz(cur_rem);
-    cur_rem &= cur_rem - 1u;
-    pn = cur_n;
-    slot = (uint32_t)__builtin_amdgcn_readfirstlane(((i_rel0 + cur_n) * G + g) * topk + pu);
-    return true;
-  };
+    }
 
-  // shared older blocks (unmasked), then the unit's own block (masked)
-  for (int d = 0; d + 1 < nd; ++d) {
-    wait_loads();
-    __syncthreads();  // stage d&1 complete; stage (d+1)&1 free
-    KHalf k0;
-    if constexpr (BK == kBlock) load_k_half(k0, lds + (d & 1) * kStage);
-    // block d+1 streams into the other stage, loaded by waves 0-3 only (one
-    // per SIMD): their partners start computing while they wait for room in
-    // the memory queue
-    const int b2 = __builtin_amdgcn_readlane(lane_blk, d + 1);
-    const uint64_t e2 = block_elems(b2, BK, G, g);
-    if (wave < 4)
-      stage_block_bk<BK>(lds + ((d + 1) & 1) * kStage, k + e2, v + e2, rstride,
-                         (int)min<int64_t>(BK, n_tokens - (int64_t)b2 * BK), wave, 4, soff);
-    // queries of the wave that did not select the block are masked; a wave
-    // with none that did skips it
-    const unsigned skip =
-        ~((unsigned)__builtin_amdgcn_readlane(lane_qm, d) >> (wave * kAttnQN)) & ((1u << kAttnQN) - 1u);
-    if (skip != (1u << kAttnQN) - 1u) {
-      if constexpr (BK == kBlock)
-        attend_block<false, false>(qg, lds + (d & 1) * kStage, k0, nullptr, scale_log2, skip, [](int) {});
+    // The partials stream through two 8 KiB LDS regions of the wave (two
+    // partials each, direct-to-LDS loads, their lse into the wave's lse_side):
+    // region 0 in the stage not holding the last block, filled while the last
+    // block is computed; region 1 in the last block's stage once every wave is
+    // done with it. Completion is tracked with vmcnt (5 loads per partial), so
+    // one region is merged while the other streams in.
+    const int last = (nd - 1) & 1;
+    lds_char* region[2] = {lds + (last ^ 1) * kStage + wave * 8192, lds + last * kStage + wave * 8192};
+    auto issue_round = [&](int reg, int& cnt, int& na, int& nb) {
+      cnt = 0;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        int pn = 0;
+        int64_t slot = 0;
+        if (!next_pair(pn, slot)) break;
+        stage_partial(part_o + slot * (kHpg * kHeadDim), region[reg] + p * 4096);
+        if (lane < kHpg) lds_dma4(part_lse + slot * kHpg + lane, lse_side + reg * 128 + p * 64);
+        if (p == 0) na = pn; else nb = pn;
+        cnt = p + 1;
+      }
+    };
+    auto wait_round = [](int cnt_in_flight) {
+      if (cnt_in_flight == 2)
+        wait_vmcnt10();
+      else if (cnt_in_flight == 1)
+        wait_vmcnt5();
       else
-        attend_short<false, false, BK / 16>(qg, lds + (d & 1) * kStage, nullptr, scale_log2, skip, [](int) {});
-    }
-  }
-
-  // The partials stream through two 8 KiB LDS regions of the wave (two
-  // partials each, direct-to-LDS loads, their lse into the wave's lse_side):
-  // region 0 in the stage not holding the last block, filled while the last
-  // block is computed; region 1 in the last block's stage once every wave is
-  // done with it. Completion is tracked with vmcnt (5 loads per partial), so
-  // one region is merged while the other streams in.
-  const int last = (nd - 1) & 1;
-  lds_char* region[2] = {lds + (last ^ 1) * kStage + wave * 8192, lds + last * kStage + wave * 8192};
-  auto issue_round = [&](int reg, int& cnt, int& na, int& nb) {
-    cnt = 0;
+        wait_vmcnt0();
+    };
+    auto merge_round = [&](int reg, int cnt, int na, int nb) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      int pn = 0;
-      int64_t slot = 0;
-      if (!next_pair(pn, slot)) break;
-      stage_partial(part_o + slot * (kHpg * kHeadDim), region[reg] + p * 4096);
-      if (lane < kHpg) lds_dma4(part_lse + slot * kHpg + lane, lse_side + reg * 128 + p * 64);
-      if (p == 0) na = pn; else nb = pn;
-      cnt = p + 1;
-    }
-  };
-  auto wait_round = [](int cnt_in_flight) {
-    if (cnt_in_flight == 2)
-      wait_vmcnt10();
-    else if (cnt_in_flight == 1)
-      wait_vmcnt5();
-    else
-      wait_vmcnt0();
-  };
-  auto merge_round = [&](int reg, int cnt, int na, int nb) {
+      for (int p = 0; p < 2; ++p) {
+        if (p >= cnt) break;
+        const float lp = *(const __attribute__((address_space(3))) float*)(lse_side + reg * 128 + p * 64 + c * 4);
+        merge_partial_into(qg, p ? nb : na, region[reg] + p * 4096, lp, scale_log2);
+      }
+      wait_lgkmcnt0();  // region read out before it is refilled
+    };
+    int cA = 0, nA0 = 0, nA1 = 0, cB = 0, nB0 = 0, nB1 = 0;
+    // the next item (waiting for the claims only once this range is drained)
+    if (tid == 0) s_next[par] = claimed >= 0 ? claimed : claim_any();
+    int next;
+    {
+      wait_loads();
+      __syncthreads();  // (also publishes s_next[par])
+      next = s_next[par];
+      // the next unit's list, row masks, count and slots stream into LDS
+      // while this unit's last block is computed
+      if (next >= 0) meta_loads(next);
+      KHalf k0;
+      if constexpr (BK == kBlock) load_k_half(k0, lds + last * kStage);
+      issue_round(0, cA, nA0, nA1);
+      int lim[kAttnQN];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if (p >= cnt) break;
-      const float lp = *(const __attribute__((address_space(3))) float*)(lse_side + reg * 128 + p * 64 + c * 4);
-      merge_partial_into(qg, p ? nb : na, region[reg] + p * 4096, lp, scale_log2);
+      for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * BK);
+      if constexpr (BK == kBlock)
+        attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [](int) {});
+      else
+        attend_short<false, true, BK / 16>(qg, lds + last * kStage, lim, scale_log2, 0u, [](int) {});
     }
-    wait_lgkmcnt0();  // region read out before it is refilled
-  };
-  int cA = 0, nA0 = 0, nA1 = 0, cB = 0, nB0 = 0, nB1 = 0;
-  {
-    wait_loads();
-    __syncthreads();
-    KHalf k0;
-    if constexpr (BK == kBlock) load_k_half(k0, lds + last * kStage);
-    issue_round(0, cA, nA0, nA1);
-    int lim[kAttnQN];
-#pragma unroll
-    for (int n = 0; n < kAttnQN; ++n) lim[n] = (int)(min(i_rel0 + n, nrows - 1) + row0 - (int64_t)b_loc * BK);
-    if constexpr (BK == kBlock)
-      attend_block<false, true>(qg, lds + last * kStage, k0, lim, scale_log2, 0u, [](int) {});
-    else
-      attend_short<false, true, BK / 16>(qg, lds + last * kStage, lim, scale_log2, 0u, [](int) {});
-  }
-  wait_lgkmcnt0();  // the last block's stage is free
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  issue_round(1, cB, nB0, nB1);
-  // rounds alternate regions; pairs are handed out in order, so an empty
-  // round means every later round is empty too
-  while (cA > 0) {
-    wait_round(cB);
-    merge_round(0, cA, nA0, nA1);
-    issue_round(0, cA, nA0, nA1);
-    if (cB == 0) break;
-    wait_round(cA);
-    merge_round(1, cB, nB0, nB1);
+    wait_lgkmcnt0();  // the last block's stage is free
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     issue_round(1, cB, nB0, nB1);
-  }
-#pragma unroll
-  for (int n = 0; n < kAttnQN; ++n) {
-    const int i_rel = i_rel0 + n;
-    if (i_rel >= nrows) continue;
-    const float l = qg.o[n][8][0];
-    const float inv = 1.0f / l;
-    uint16_t* dst = out + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      u32x2 w = {pack_bf16x2(qg.o[n][dt][0] * inv, qg.o[n][dt][1] * inv),
-                 pack_bf16x2(qg.o[n][dt][2] * inv, qg.o[n][dt][3] * inv)};
-      *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+    // rounds alternate regions; pairs are handed out in order, so an empty
+    // round means every later round is empty too
+    while (cA > 0) {
+      wait_round(cB);
+      merge_round(0, cA, nA0, nA1);
+      issue_round(0, cA, nA0, nA1);
+      if (cB == 0) break;
+      wait_round(cA);
+      merge_round(1, cB, nB0, nB1);
+      issue_round(1, cB, nB0, nB1);
     }
-    if (lse_out && qd == 0)
-      lse_out[(int64_t)i_rel * Hq + g * kHpg + c] =
-          (qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+    // every wave is done with both stages before the next unit's first block
+    // is staged (after the stores below), and every wave's copies of the next
+    // unit's metadata have landed; its Q loads meanwhile
+    wait_vmcnt0();
+    lds_barrier();
+    if (next >= 0) {
+      meta_read();
+      unit_q(next);
+    }
+#pragma unroll
+    for (int n = 0; n < kAttnQN; ++n) {
+      const int i_rel = i_rel0 + n;
+      if (i_rel >= nrows) continue;
+      const float l = qg.o[n][8][0];
+      const float inv = 1.0f / l;
+      uint16_t* dst = out + ((int64_t)i_rel * Hq + g * kHpg + c) * kHeadDim + 4 * qd;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        u32x2 w = {pack_bf16x2(qg.o[n][dt][0] * inv, qg.o[n][dt][1] * inv),
+                   pack_bf16x2(qg.o[n][dt][2] * inv, qg.o[n][dt][3] * inv)};
+        *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+      }
+      if (lse_out && qd == 0)
+        lse_out[(int64_t)i_rel * Hq + g * kHpg + c] =
+            (qg.m[n] * scale_log2 + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+    }
+    if (next < 0) break;
+    stage_first(next);
+    item = next;
   }
 }
 
@@ -1154,9 +1249,9 @@ void launch_attn_prefill(const LaunchAttnPrefill& a, hipStream_t st) {
 
 template <int BK>
 static void launch_attn_dense_bk(const LaunchAttnDense& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_dense<BK>, dim3(a.nunits * a.G), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v,
-                     a.dense_cnt, a.dense_list, a.dense_qmask, a.dense_slots, a.part_o, a.part_lse, a.out,
-                     a.lse_out, a.n_tokens, a.row0, a.nrows, a.nunits, a.G, a.topk, a.scale_log2);
+  hipLaunchKernelGGL(k_attn_dense<BK>, dim3(a.grid), dim3(kAttnWaves * 64), 0, st, a.q, a.k, a.v, a.dense_cnt,
+                     a.dense_list, a.dense_qmask, a.dense_slots, a.part_o, a.part_lse, a.out, a.lse_out, a.n_tokens,
+                     a.row0, a.nrows, a.nunits, a.G, a.topk, a.scale_log2, a.tile_info);
 }
 
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st) {

@@ -241,7 +241,8 @@ __global__ __launch_bounds__(256) void k_scan_final(const int32_t* __restrict__ 
 
 // One workgroup: per list l = g*nbw + b, tiles = ceil(count / tile_q); exclusive
 // scan into tile_start; tile_info[0] = total tiles, tile_info[1] = 0 (queue),
-// [2] = lists, [3] = chunks per list, [5] = window rows, [6] = first row.
+// [2] = lists, [3] = chunks per list, [5] = window rows, [6] = first row,
+// [8..15] = 0 (the dense pass's item counters).
 __global__ __launch_bounds__(1024) void k_tiles_count(const int32_t* __restrict__ chunkoff, int nch, int L,
                                                       int tile_q, int32_t* __restrict__ tile_start,
                                                       int32_t* __restrict__ tile_info, int nrows, int row0) {
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(1024) void k_tiles_count(const int32_t* __restrict_
     tile_info[5] = nrows;
     tile_info[6] = row0;
   }
+  if (threadIdx.x >= 8 && threadIdx.x < 16) tile_info[threadIdx.x] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_tiles_fill(const int32_t* __restrict__ tile_start,

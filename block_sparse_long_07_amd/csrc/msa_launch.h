@@ -76,8 +76,10 @@ struct LaunchCsr {
   int32_t* entries;
   int32_t* tile_start;    // [G*nbw + 1]
   int32_t* tiles;         // [T_cap][4] = (group, begin, len, block)
-  int32_t* tile_info;     // [8]: [0] tiles, [1] queue counter, [2] lists (G*nbw), [3] chunks per list,
-                          // [4] workgroups of the KV-outer pass (written by it), [5] rows, [6] row0
+  int32_t* tile_info;     // [16]: [0] tiles, [1] queue counter, [2] lists (G*nbw), [3] chunks per list,
+                          // [4] workgroups of the KV-outer pass (written by it), [5] rows, [6] row0,
+                          // [7] workgroups of the dense pass (written by it), [8..15] its per-XCD
+                          // item counters (zeroed here)
   int tile_q;             // queries per tile
   int64_t tile_cap;
   int32_t* dense_cnt;     // [G][nunits]: blocks a 16-row unit computes in the dense pass
@@ -126,6 +128,8 @@ struct LaunchAttnDense {
   int nrows, nunits, G, topk;
   float scale_log2;
   int bk;
+  int32_t* tile_info;     // [7]: grid (written), [8..15]: per-XCD item counters, zero before the pass
+  int grid;               // persistent workgroups: a multiple of kXcd (8), at least 8
 };
 void launch_attn_dense(const LaunchAttnDense& a, hipStream_t st);
 

@@ -152,9 +152,13 @@ msa_status msa_prefill_varlen(const msa_params* p, int32_t batch, int64_t max_ct
  * nbw the blocks its rows can see, nch = ceil(n / 64), units = ceil(n / 16).
  * Nothing here is read by the library after the call: writing it is harmless. */
 typedef struct {
-  int64_t tile_info;   /* int32 [8]: [0] tiles T, [1] the queue counter after the pass
+  int64_t tile_info;   /* int32 [16]: [0] tiles T, [1] the queue counter after the pass
                           (claims * claim), [2] lists = G * nbw, [3] nch,
-                          [4] workgroups of the KV-outer pass, [5] n, [6] first row */
+                          [4] workgroups of the KV-outer pass, [5] n, [6] first row,
+                          [7] workgroups of the dense pass, [8 + r] the claim counter
+                          of its item range r (r < 8; G * units items in 8 ranges
+                          of floor or ceil(G * units / 8) items, range r >= its
+                          size after the pass: failed claims count too) */
   int64_t chunk_off;   /* int32 [lists * nch + 1]: exclusive scan of the KV-outer pair
                           counts of each (group g, block b, chunk of 64 rows), list
                           l = g * nbw + b first; list l holds entries

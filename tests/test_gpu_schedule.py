@@ -8,7 +8,8 @@ pair must be computed exactly once: either listed in the reverse index of its
 reverse-index counts plus the dense pairs equals the number of selected pairs;
 the tiles cut every list into consecutive runs of at most 16 queries; the
 persistent pass computed every tile exactly once (its visit counts) and its
-workgroups together drained all tiles.
+workgroups together drained all tiles; the persistent dense pass drained its
+eight item ranges.
 
 All of this is integer bookkeeping: it is checked exactly.
 """
@@ -106,6 +107,16 @@ def check_schedule(sel: np.ndarray, sc: dict, m, bk: int) -> dict:
     assert nwg >= 1 and len(wg) == nwg
     assert int(wg[:, 1].sum()) == T
     assert (wg[:, 3] >= wg[:, 2]).all()
+    # the dense pass: a grid of a multiple of 8 workgroups drained 8 item
+    # ranges; every range's counter passed its size (each item claimed once,
+    # then at least one failed claim), which the outputs compared with the
+    # oracle confirm item by item
+    dgrid = int(info[7])
+    assert dgrid >= 8 and dgrid % 8 == 0
+    items = G * units
+    sizes = np.array([items // 8 + (r < items % 8) for r in range(8)])
+    ctr = info[8:16].astype(np.int64)
+    assert (ctr >= sizes).all(), (ctr, sizes)
     return dict(tiles=T, kv_pairs=int(chunk_off[-1]), dense_pairs=int(dense.sum()), selected=int(valid.sum()),
                 workgroups=nwg)
 
