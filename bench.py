@@ -99,7 +99,7 @@ def decode_bytes(ctx_lens, topk=TOPK, bk=BK):
 # A 16-row unit's block is computed by the dense pass when at least this many
 # of the unit's rows selected it (all of them, if the unit has fewer); the
 # library's split rule (kDenseMin in its launch header).
-DENSE_MIN = 7
+DENSE_MIN = 5
 
 
 def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G, window=65536):

@@ -77,7 +77,7 @@ def test_schedule_layout_within_the_workspace(lib):
         offs = sorted(getattr(m, f) for f in msa._SCHED_OFFSETS)
         assert len(set(offs)) == len(offs)
         assert all(0 <= o < total and o % 256 == 0 for o in offs)
-        assert (m.dense_max, m.tile_queries, m.claim, m.dense_min) == (64, 16, 4, 7)
+        assert (m.dense_max, m.tile_queries, m.claim, m.dense_min) == (64, 16, 4, 5)
     m = msa.MsaScheduleMap()
     p = msa.params()
     assert lib.msa_prefill_schedule_layout(ctypes.byref(p), 64, 64, None) == -1
