@@ -51,31 +51,56 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ sblk, 
   }
   if constexpr (KM1 > 0) {
     const float* row = sblk + r * (int64_t)nb;
-    for (int b0 = s; b0 < need; b0 += 64) {
-      // four candidates per lane per step: the loads are issued together
-      float cvs[4];
+    // Insert before the first strictly smaller score; from there on every
+    // element shifts down one place (the displaced ones keep their order, so
+    // equal scores stay in ascending index order).
+    auto insert = [&](float cv, int ci) {
+      bool shift = false;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) cvs[q] = (b0 + 16 * q < need) ? row[b0 + 16 * q] : -__builtin_inff();
+      for (int t = 0; t < KM1; ++t) {
+        shift |= cv > v[t];
+        const float nv = shift ? cv : v[t];
+        const int ni = shift ? ci : id[t];
+        cv = shift ? v[t] : cv;
+        ci = shift ? id[t] : ci;
+        v[t] = nv;
+        id[t] = ni;
+      }
+    };
+    // Long rows (k = 16, at least kFloorMin candidates in some row of the
+    // wave) also keep floor: a lower bound of the row's 15th best score so
+    // far, the second smallest of the 16 lanes' best scores (15 lanes each
+    // hold a score >= it, so no score strictly below it can be among the
+    // row's 15 best; equal scores still go through the lane's own rule). Most
+    // of their candidates then fail one compare instead of costing the wave a
+    // list insertion, which bounds this loop (without insertions it streams
+    // at the HBM rate); on shorter rows the exchange costs more than it
+    // saves. That loop runs while any lane of the wave has candidates left,
+    // so that every lane takes part in every exchange (a lane reading a
+    // disabled lane gets its own value back).
+    constexpr int kFloorMin = 2048;
+    if (KM1 == 15 && __any(need >= kFloorMin)) {
+      float floor_v = -__builtin_inff();
+      for (int b0 = s; __any(b0 < need); b0 += 64) {
+        float cvs[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float cv = cvs[q];
-        if (cv > v[KM1 - 1]) {
-          int ci = b0 + 16 * q;
-          // Insert before the first strictly smaller score; from there on every
-          // element shifts down one place (the displaced ones keep their order,
-          // so equal scores stay in ascending index order).
-          bool shift = false;
+        for (int q = 0; q < 4; ++q) cvs[q] = (b0 + 16 * q < need) ? row[b0 + 16 * q] : -__builtin_inff();
 #pragma unroll
-          for (int t = 0; t < KM1; ++t) {
-            shift |= cv > v[t];
-            const float nv = shift ? cv : v[t];
-            const int ni = shift ? ci : id[t];
-            cv = shift ? v[t] : cv;
-            ci = shift ? id[t] : ci;
-            v[t] = nv;
-            id[t] = ni;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const bool ins = (cvs[q] > v[KM1 - 1]) & (cvs[q] >= floor_v);
+          if (__any(ins) && ins) insert(cvs[q], b0 + 16 * q);  // (skipped by the wave when no lane needs it)
         }
+        floor_v = second_min_row16(v[0]);
+      }
+    } else {
+      for (int b0 = s; b0 < need; b0 += 64) {
+        // four candidates per lane per step: the loads are issued together
+        float cvs[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cvs[q] = (b0 + 16 * q < need) ? row[b0 + 16 * q] : -__builtin_inff();
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (cvs[q] > v[KM1 - 1]) insert(cvs[q], b0 + 16 * q);
       }
     }
   }

@@ -46,6 +46,27 @@ __device__ __forceinline__ void argmax_rows(float& bv, int& bi) {
   }
 }
 
+// The second smallest of x over the 16 lanes of each 16-lane row, in every
+// lane of the row: the butterfly of argmax_row16 over (smallest, second
+// smallest) pairs (two disjoint sets' pairs merge into the union's).
+template <int STEP>
+__device__ __forceinline__ void min2_step(float& m1, float& m2) {
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  const float o1 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m1), __float_as_int(m1), ctrl, 0xF, 0xF, false));
+  const float o2 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m2), __float_as_int(m2), ctrl, 0xF, 0xF, false));
+  const float lo = fminf(m1, o1), hi = fmaxf(m1, o1);
+  m2 = fminf(hi, fminf(m2, o2));
+  m1 = lo;
+}
+__device__ __forceinline__ float second_min_row16(float x) {
+  float m1 = x, m2 = __builtin_inff();
+  min2_step<0>(m1, m2);
+  min2_step<1>(m1, m2);
+  min2_step<2>(m1, m2);
+  min2_step<3>(m1, m2);
+  return m2;
+}
+
 // (score, index) a precedes b: higher score, or equal score and lower index
 __device__ __forceinline__ bool before(float av, int ai, float bv, int bi) {
   return (av > bv) | ((av == bv) & (ai < bi));

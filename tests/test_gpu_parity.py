@@ -93,6 +93,34 @@ def test_select_exact_with_ties(topk, n):
             assert got[gg, i].tolist() == want.tolist(), (i, gg)
 
 
+@pytest.mark.parametrize("dist", ["ties", "normal"])
+def test_select_long_rows_exact(dist):
+    """The many-rows selection on rows of up to 2047 candidates, where its
+    running lower bound of a row's 15th best score prunes most candidates:
+    sampled rows (the longest ones among them) against the oracle, with
+    integer scores full of ties and with continuous scores."""
+    n, G, topk = 262144, 4, 16
+    nb = n // 128
+    g = torch.Generator(device="cuda").manual_seed(7)
+    if dist == "ties":
+        scores = torch.randint(-3, 4, (n, G, nb), generator=g, device="cuda").float()
+    else:
+        scores = torch.randn((n, G, nb), generator=g, device="cuda")
+    sel = msa.select_blocks(scores, topk=topk)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(n - 64, n), np.random.default_rng(3).integers(2048, n, 192)]))
+    got = sel[:, torch.from_numpy(rows).cuda()].cpu().numpy()
+    s = scores[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    del scores, sel
+    torch.cuda.empty_cache()
+    log(f"long-row selection ({dist}): {len(rows)} rows of up to {nb - 1} candidates")
+    for j, i in enumerate(rows):
+        b_loc = int(i) // 128
+        for gg in range(G):
+            want = mo.select_blocks(s[j, gg, :b_loc], b_loc, topk)
+            assert got[gg, j].tolist() == want.tolist(), (int(i), gg)
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_prefill_tiny_all_rows(seed):
     inp = syn.PrefillInputs(2048, dims(1, 4), seed, "tiny")
