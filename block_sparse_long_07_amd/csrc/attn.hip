@@ -333,7 +333,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 //  * hook(i) lets the caller place its own memory traffic in the block:
 //    i = 0..3 at the start of the d-steps of S1, i = 4 right after them (Q is
 //    no longer read from there on), i = 5..12 at the start of the PV regions.
-template <bool FIRST, bool MASKED, int VOFF = kVOff, class QG, class H>
+//  * PRIO: the wave's issue priority over the block (s_setprio; the other
+//    wave of the SIMD takes the issue slots it leaves): kPrioNone keeps it,
+//    kPrioScores raises it through S0 .. [S1 | exp 0] and lowers it for the
+//    second half, kPrioPv raises it through the P.V regions.
+constexpr int kPrioNone = 0, kPrioScores = 1, kPrioPv = 2;
+template <bool FIRST, bool MASKED, int VOFF = kVOff, int PRIO = kPrioNone, class QG, class H>
 __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, const KHalf& k0, const int* lim,
                                              float scale_log2, unsigned skip, H hook) {
   constexpr int QN = QG::kQN;
@@ -347,6 +352,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
   bf16x8 p0[QN][2], p1[QN][2];
   float mx[QN], mc[QN];
 
+  if constexpr (PRIO == kPrioScores) __builtin_amdgcn_s_setprio(1);
   qk_half0(s0, qg.qop, k0, stage);
   // operands of the first pipelined step, read before the max and the branch
   bf16x8 ka[4], va[8];
@@ -406,6 +412,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
     });
   }
   hook(4);
+  if constexpr (PRIO == kPrioScores) __builtin_amdgcn_s_setprio(0);
   half_max<MASKED>(s1, lim, 1, mx);
 #pragma unroll
   for (int n = 0; n < QN; ++n)
@@ -440,6 +447,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
     // key step st and reads the next region's V^T operands
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) va[dt] = lds_vt<VOFF>(stage, dt, 0, c, qd);
+    if constexpr (PRIO == kPrioPv) __builtin_amdgcn_s_setprio(1);
     static_for<0, 8>([&](auto ir) {
       constexpr int r = decltype(ir)::value, st = r >> 1, hh = r & 1;
       constexpr int nst = hh ? st + 1 : st, nd0 = hh ? 0 : 4;
@@ -465,6 +473,7 @@ __device__ __forceinline__ void attend_block(QG& qg, const lds_char* stage_in, c
       for (int u = u0; u < u1; ++u) exp_unit(s1, mc, scale_log2, p1, u >> 1, u & 1);
       sched_region<(d1 - d0) * QN, (u1 - u0) * kExpValu, nst < 4 ? 8 : 0>();
     });
+    if constexpr (PRIO == kPrioPv) __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -783,7 +792,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
         if (i == 4 && next_work) fetch_q(nent, nxt.g);
       };
       if constexpr (BK == kBlock)
-        attend_block<true, false>(qg, stage, k0, nullptr, scale_log2, 0u, hook);
+        attend_block<true, false, kVOff, kPrioScores>(qg, stage, k0, nullptr, scale_log2, 0u, hook);
       else
         attend_short<true, false, BK / 16>(qg, stage, nullptr, scale_log2, 0u, hook);
 #pragma unroll
