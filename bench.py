@@ -154,9 +154,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G, window=65536):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "4f04b34ac3a97fd2",
-    "k_attn_prefill (KV-outer)": 4.192e9,
-    "k_attn_dense (dense + merge)": 3.516e9,
+    "source": "0b141c20402f20b5",
+    "k_attn_prefill (KV-outer)": 4.169e9,
+    "k_attn_dense (dense + merge)": 3.517e9,
 }
 
 
