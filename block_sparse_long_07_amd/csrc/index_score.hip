@@ -133,6 +133,11 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
       stage_kidx(lds + ((x + 1) & 1) * 16384, k_idx + (int64_t)(kb + 1) * kBlock * kIndexDim, wave,
                  stage_rows(kb + 1));
     const lds_char* st = lds + (x & 1) * 16384;
+    // issue priority up through the stage's MFMAs and down for the pooling
+    // and the writes: the other workgroups' waves on the SIMD, at other
+    // points of their own stages, fill the slots left meanwhile (1M: index
+    // scoring 2 % faster; 32K unchanged)
+    __builtin_amdgcn_s_setprio(1);
     float mx[SUB][RT];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -151,6 +156,7 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t* __rest
         mx[sb][rt] = fmaxf(fmaxf(m, acc[2]), acc[3]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
