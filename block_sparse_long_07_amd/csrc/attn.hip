@@ -4,10 +4,10 @@
 //
 // Prefill has two passes. Blocks selected by many queries of a 16-query unit
 // (the query's own block, sink-like or planted blocks, blocks a local run of
-// queries agrees on) are computed query-stationary: one workgroup per (unit,
-// group) keeps the 16 queries' Q and running softmax state in registers and
-// streams the unit's listed blocks through LDS, masking the rows that did not
-// select a block (k_attn_dense). Every other (query, block) pair goes KV-outer: a
+// queries agrees on) are computed query-stationary: for each (unit, group) a
+// workgroup of a persistent grid keeps the 16 queries' Q and running softmax
+// state in registers and streams the unit's listed blocks through LDS,
+// masking the rows that did not select a block (k_attn_dense). Every other (query, block) pair goes KV-outer: a
 // persistent grid drains the tile queue built by the reverse index, a tile being
 // (group g, KV block b, up to 16 queries that selected b); the block is staged
 // once and each wave gathers the 16 query heads of a query (4 KiB, contiguous in
@@ -672,7 +672,10 @@ constexpr int kAttnWaves = 8;
 // ahead, so no latency sits between two tiles: while tile j is computed, the
 // K/V of tile j+1 stream into the other LDS stage, the wave's entries of tile
 // j+1 and then their Q are loaded, and the descriptor of tile j+2 is read.
-// Tiles are claimed from the queue kClaim at a time, one chunk ahead.
+// Tiles are claimed from the queue kClaim at a time, one chunk ahead. Each
+// wave raises its issue priority through the scores of a block
+// (kPrioScores): its waves drift apart between tiles, and the other wave of
+// the SIMD fills the slots left meanwhile.
 template <int BK>
 __global__ __launch_bounds__(512, 1) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -830,8 +833,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
 // query-stationary (FlashAttention-style online softmax over the unit's list;
 // each block is staged once for all 16 queries, the next one streaming into
 // the other stage meanwhile). Rows that did not select a listed block are
-// masked for it; a wave whose two rows both did not skips it. One workgroup of
-// 8 waves per (unit, group), two queries per wave. The list always ends with
+// masked for it; a wave whose two rows both did not skips it. Eight waves per
+// (unit, group) item, two queries per wave. The list always ends with
 // the unit's own block, the only one that needs the causal mask. This pass
 // runs after the KV-outer pass and merges its partials (the slots of the
 // query's selection outside the unit's list) into the same online state, so
@@ -840,12 +843,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_prefill(
 //   out = o / l,   lse = (m*c + log2 l) * ln 2.
 // The grid is persistent (one workgroup per CU) and the (group, unit) items
 // are split into kXcd contiguous ranges, one per XCD, each drained through a
-// counter of its own (queue[x], zero before the pass): units that share K/V
-// blocks then meet in one L2, and while a unit's partials are merged the next
-// unit's list, slots and Q are already loading; its first block streams in
-// right after the unit's output is stored. A workgroup whose range is drained
-// takes items from the other ranges in turn. tile_info[8 + x] is range x's
-// counter (zeroed with the tile queue); tile_info[7] gets the grid size.
+// counter of its own (tile_info[8 + x], zeroed with the tile queue;
+// tile_info[7] gets the grid size): units that share K/V blocks then meet in
+// one L2. The next unit is claimed when a unit starts; its list, row masks,
+// count and slots stream into LDS during the unit's last block, its Q loads
+// while the unit's output is stored, and its first block is staged right
+// after. A workgroup whose range is drained takes items from the other
+// ranges in turn.
 template <int BK>
 __global__ __launch_bounds__(512, 1) void k_attn_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
