@@ -282,6 +282,15 @@ def projection_measure(torch, msa, n, batch, reps, d_model=D_MODEL):
     res["prefill"] = {"tokens": n, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                       "GB/s": round(nb / (ms * 1e-3) / 1e9, 1), "bound": "mfma" if t_mfma >= t_hbm else "hbm",
                       "frac": round(max(t_mfma, t_hbm) / (ms * 1e-3), 4)}
+    # measured ceiling for this shape: the vendor GEMM (torch.matmul, hipBLASLt)
+    # of the same x against the stacked weights into a plain [n, cols] output
+    # (no cache-row scatter), as a reference point for the analytic bound
+    wst = torch.cat([wq.reshape(G * DI, d_model), wk]).t()
+    ref = torch.empty((n, cols), dtype=torch.bfloat16, device=dev)
+    ms_v = _time_calls(torch, lambda: torch.matmul(x, wst, out=ref), reps)
+    res["prefill"]["vendor_gemm"] = {"ms": round(ms_v, 4), "tflops": round(fl / (ms_v * 1e-3) / 1e12, 2),
+                                     "frac": round(max(t_mfma, t_hbm) / (ms_v * 1e-3), 4),
+                                     "what": "torch.matmul (hipBLASLt) of the same shape, plain output"}
     cache = torch.zeros((batch, 4096, DI), dtype=torch.bfloat16, device=dev)
     lens = torch.full((batch,), 4096, dtype=torch.int32, device=dev)
     xd = x[:batch].contiguous()
