@@ -198,6 +198,7 @@ struct ProjectPlan {
   int64_t m_tiles;        // 128-token tiles
   int splits, stages_per_split;
   size_t part_floats;     // scratch for split partials (0: none)
+  bool ws = false;        // many tokens, d_model a multiple of 256: k_index_project_ws
 };
 ProjectPlan plan_index_project(int64_t n, int d_model, int G);
 void launch_index_project(const LaunchProject& a, hipStream_t st);

@@ -8,7 +8,11 @@
 // straight into its cache row (row(t) = t, or ctx_lens[t]-1 of sequence t in
 // decode). fp32 accumulation; outputs rounded to bf16 (nearest even).
 //
-// Workgroup: 128 tokens x NC 64-column units (all G+1 units when G+1 <= 5,
+// Many tokens with d_model a multiple of 256 (k_index_project_ws, below):
+// four loader waves keep the next double steps of x and the weights in
+// flight in registers and feed a two-slot LDS ring; four compute waves hold
+// 128 tokens x NC/4 of the columns each. Otherwise (k_index_project):
+// workgroup of 128 tokens x NC 64-column units (all G+1 units when G+1 <= 5,
 // else two parts), 8 waves as 2 (tokens) x 4 (columns); each wave holds
 // 4 x NC accumulator tiles of 16 x 16 (NC = 1 for few tokens: more
 // workgroups, each with one 64-column unit). d_model is consumed in 32-wide slices
@@ -22,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "msa_device.h"
 #include "msa_launch.h"
@@ -61,6 +66,15 @@ __device__ __forceinline__ void stage_rows(lds_char* dst, RowPtr row_ptr, int ti
       const int r = slot >> 2, p = slot & 3;
       lds_dma16(row_ptr(r) + ((p ^ ((r >> 1) & 3)) << 3), dst + s0 * 16);
     }
+  }
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
@@ -160,6 +174,162 @@ __global__ __launch_bounds__(512, 1) void k_index_project(
   }
 }
 
+// Many tokens, d_model a multiple of 64 kWsDepth: 128 tokens x NCT 64-column
+// units per workgroup, eight waves in two roles. Waves 4-7 load: each keeps
+// its quarter of the next kWsDepth double steps (64 of d_model each: x 128
+// rows and the weights 64 NCT rows of 128 bytes, every row read as one
+// 128-byte piece) in flight in registers and, one double step ahead of the
+// computation, writes a double step into a two-slot LDS ring. Waves 0-3
+// compute: wave w holds all 128 tokens against column tiles [w NCT, (w+1) NCT)
+// of 16 (8 NCT accumulator tiles) and reads its operands from the ring. One
+// barrier per double step separates the slot being read from the slot being
+// written. All loads are ordinary register loads, so the compiler's waits are
+// exact: each loader wave consumes its loads in the order it issued them,
+// with kWsDepth - 1 double steps still in flight (about 170 KiB per CU). In a
+// slot, row r's 16-byte chunk p sits at chunk p ^ f(r), f(r) = (r & 7) ^
+// ((r >> 3) & 1): the operand reads (16 consecutive rows, one chunk each) and
+// the row writes are then free of bank conflicts for 32 and for 64 banks.
+constexpr int kWsDepth = 4;
+constexpr int kWsStep = 64;                  // d_model per double step
+constexpr int kWsXBytes = kPRows * kWsStep * 2;
+constexpr int kWsX = kPRows * 8 / 256;       // 16-byte x chunks per loader lane and double step
+
+__device__ __forceinline__ int ws_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int NCT>
+__global__ __launch_bounds__(512, 1) void k_index_project_ws(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_qi, const uint16_t* __restrict__ w_ki,
+    int64_t n, int d_model, int G, uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx,
+    const int32_t* __restrict__ ctx_lens, int64_t max_ctx) {
+  constexpr int kWRows = NCT * 64;           // weight rows per workgroup
+  constexpr int kWsW = kWRows * 8 / 256;     // 16-byte weight chunks per loader lane and double step
+  constexpr int kSlot = kWsXBytes + kWRows * kWsStep * 2;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kSlot];
+  lds_char* lds = (lds_char*)lds_raw;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t m0 = (int64_t)blockIdx.x * kPRows;
+  const int col0 = (int)blockIdx.y * kWRows;
+  const int ncols = 64 * (G + 1);
+  const int nk = d_model / kWsStep;
+
+  if (wave >= 4) {
+    // loader: chunk q = 256 i + lt (lt = tid - 256) of a part is row
+    // 32 i + lt / 8, chunk lt % 8 (8 elements at 8 (lt % 8) of the double
+    // step). Weight part i lies in unit (col0 + 32 i) / 64 (col0 is a
+    // multiple of 64), rows 32 (i % 2) + lt / 8 of it; units past the last
+    // repeat it (never stored).
+    const int lt = tid - 256, lr = lt >> 3, lp = lt & 7;
+    const uint32_t dst0 = (uint32_t)(lr * 128 + ((lp ^ ws_swz(lr)) << 4));
+    const char* xbase = (const char*)(x + m0 * d_model);
+    uint32_t xo[kWsX];
+#pragma unroll
+    for (int i = 0; i < kWsX; ++i)
+      xo[i] = (uint32_t)(((min<int64_t>(m0 + 32 * i + lr, n - 1) - m0) * d_model + 8 * lp) * 2);
+    const char* wb[kWsW];
+#pragma unroll
+    for (int i = 0; i < kWsW; ++i) {
+      const int u = min(col0 / 64 + i / 2, G);
+      wb[i] = (const char*)((u < G ? w_qi + (int64_t)u * 64 * d_model : w_ki) + (int64_t)(32 * (i & 1)) * d_model);
+    }
+    const uint32_t wo = (uint32_t)((lr * d_model + 8 * lp) * 2);
+    u32x4 ring[kWsDepth][kWsX + kWsW];
+    // double step s (clamped to the last: steps past the end load valid data
+    // that is never read)
+    auto load_step = [&](int s, u32x4 (&dst)[kWsX + kWsW]) {
+      const uint32_t kb = (uint32_t)(min(s, nk - 1) * kWsStep * 2);
+#pragma unroll
+      for (int i = 0; i < kWsX; ++i) dst[i] = ld16(xbase + xo[i] + kb);
+#pragma unroll
+      for (int i = 0; i < kWsW; ++i) dst[kWsX + i] = ld16(wb[i] + wo + kb);
+    };
+    // row 32 i + lr has the swizzle of lr (32 i changes neither r & 7 nor
+    // (r >> 3) & 1)
+    auto write_step = [&](int s, const u32x4 (&src)[kWsX + kWsW]) {
+      lds_char* slot = lds + (s & 1) * kSlot + dst0;
+#pragma unroll
+      for (int i = 0; i < kWsX; ++i) *(lds_u32x4*)(slot + 4096 * i) = src[i];
+#pragma unroll
+      for (int i = 0; i < kWsW; ++i) *(lds_u32x4*)(slot + kWsXBytes + 4096 * i) = src[kWsX + i];
+    };
+    static_for<0, kWsDepth>([&](auto is) {
+      constexpr int s = decltype(is)::value;
+      load_step(s, ring[s]);
+    });
+    write_step(0, ring[0]);
+    load_step(kWsDepth, ring[0]);
+    wait_lgkmcnt0();
+    __syncthreads();  // double step 0 is in slot 0
+    // iteration g (the computation of double step g runs meanwhile): double
+    // step g+1 into slot (g+1) & 1, then its registers take g+1+kWsDepth
+    for (int g0 = 0; g0 < nk; g0 += kWsDepth) {
+      static_for<0, kWsDepth>([&](auto ij) {
+        constexpr int j = decltype(ij)::value, rs = (j + 1) % kWsDepth;
+        const int g = g0 + j;
+        write_step(g + 1, ring[rs]);
+        load_step(g + 1 + kWsDepth, ring[rs]);
+        wait_lgkmcnt0();
+        __syncthreads();  // double step g+1 is in its slot; g's slot is free
+      });
+    }
+    return;
+  }
+
+  // compute: lane (c, qd) reads row 16t + c (x) or 16 (w NCT + ct) + c
+  // (weights), logical chunk 4h + qd for half h of the double step
+  const int c = lane & 15, qd = lane >> 4, sw = ws_swz(c);
+  f32x4 acc[8][NCT];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  auto frag = [&](const lds_char* base, int row, int h) {
+    const u32x4 v = *(const lds_u32x4*)(base + row * 128 + (((4 * h + qd) ^ sw) << 4));
+    return as_bf16x8(v);
+  };
+  __syncthreads();  // double step 0 is in slot 0
+  for (int g = 0; g < nk; ++g) {
+    const lds_char* xs = lds + (g & 1) * kSlot;
+    const lds_char* wsl = xs + kWsXBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 wa[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) wa[ct] = frag(wsl, 16 * (wave * NCT + ct) + c, h);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const bf16x8 xb = frag(xs, 16 * t + c, h);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mfma16x16x32(wa[ct], xb, acc[t][ct]);
+      }
+    }
+    __syncthreads();  // this slot is read; the next double step is in the other
+  }
+
+  // lane (c, qd) of tile (t, ct): token m0 + 16t + c, stacked columns
+  // col0 + 16 (wave NCT + ct) + 4qd .. +3
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t tok = m0 + 16 * t + c;
+    if (tok >= n) continue;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int tc0 = col0 + 16 * (wave * NCT + ct);
+      if (tc0 >= ncols) continue;
+      const int gc = tc0 + 4 * qd;
+      const f32x4 v = acc[t][ct];
+      const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      uint16_t* dst;
+      if (gc < 64 * G) {
+        dst = q_idx + tok * (int64_t)(64 * G) + gc;
+      } else {
+        const int64_t row = ctx_lens ? tok * max_ctx + ctx_lens[tok] - 1 : tok;
+        dst = k_idx + row * 64 + (gc - 64 * G);
+      }
+      *reinterpret_cast<u32x2*>(dst) = o;
+    }
+  }
+}
+
 // Sum of the d_model splits' partials in split order, rounded to bf16.
 __global__ __launch_bounds__(256) void k_index_project_reduce(const float* __restrict__ part, int64_t n, int G,
                                                               int splits, uint16_t* __restrict__ q_idx,
@@ -208,6 +378,8 @@ ProjectPlan plan_index_project(int64_t n, int d_model, int G) {
     // read once (or twice)
     pl.parts = units <= 5 ? 1 : 2;
     pl.nc = (units + pl.parts - 1) / pl.parts;
+    // whole multiples of kWsDepth steps: the warp-specialised kernel
+    pl.ws = d_model % (kWsStep * kWsDepth) == 0;
   } else {
     // few tokens (decode): one 64-column unit per workgroup, d_model split
     pl.parts = units;
@@ -218,7 +390,7 @@ ProjectPlan plan_index_project(int64_t n, int d_model, int G) {
   // about two workgroups per CU; each split at least four slices deep, and the
   // fp32 partials (splits x n x columns) kept below half the weights' bytes
   int64_t splits = 1;
-  if (base < 256)
+  if (base < 256 && !pl.ws)
     splits = std::max<int64_t>(1, std::min<int64_t>({(512 + base - 1) / base, nk / 4, d_model / (4 * n)}));
   pl.stages_per_split = (int)((nk + splits - 1) / splits);
   pl.splits = (nk + pl.stages_per_split - 1) / pl.stages_per_split;
@@ -234,8 +406,25 @@ static void launch_nc(const LaunchProject& a, const ProjectPlan& pl, hipStream_t
                      a.max_ctx, part);
 }
 
+template <int NCT>
+static void launch_ws(const LaunchProject& a, const ProjectPlan& pl, hipStream_t st) {
+  hipLaunchKernelGGL(k_index_project_ws<NCT>, dim3((unsigned)pl.m_tiles, pl.parts), dim3(512), 0, st, a.x, a.w_qi,
+                     a.w_ki, a.n, a.d_model, a.G, a.q_idx, a.k_idx, a.ctx_lens, a.max_ctx);
+}
+
 void launch_index_project(const LaunchProject& a, hipStream_t st) {
   const ProjectPlan pl = plan_index_project(a.n, a.d_model, a.G);
+  if (pl.ws) {
+    switch (pl.nc) {
+      case 1: launch_ws<1>(a, pl, st); break;
+      case 2: launch_ws<2>(a, pl, st); break;
+      case 3: launch_ws<3>(a, pl, st); break;
+      case 4: launch_ws<4>(a, pl, st); break;
+      case 5: launch_ws<5>(a, pl, st); break;
+      default: break;
+    }
+    return;
+  }
   switch (pl.nc) {
     case 1: launch_nc<1>(a, pl, st); break;
     case 2: launch_nc<2>(a, pl, st); break;

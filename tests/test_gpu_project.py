@@ -62,7 +62,11 @@ def run(x, wq, wk):
 # and many (all columns, or two parts of them, per workgroup), every G
 @pytest.mark.parametrize("G,n,dm", [(4, 1, 64), (4, 129, 320), (1, 1000, 256), (8, 127, 1024), (5, 300, 128),
                                     (6, 64, 8192), (4, 33000, 128), (2, 40000, 192), (1, 9000, 64),
-                                    (3, 8200, 128), (7, 8200, 128), (8, 8200, 64), (5, 8300, 64), (6, 8200, 64)])
+                                    (3, 8200, 128), (7, 8200, 128), (8, 8200, 64), (5, 8300, 64), (6, 8200, 64),
+                                    # many tokens and d_model a multiple of 256: the warp-specialised
+                                    # kernel (all units, or two parts with the last unit clamped)
+                                    (4, 8300, 256), (1, 9000, 512), (8, 8200, 256), (6, 16500, 256),
+                                    (3, 33000, 256), (4, 8192, 768)])
 def test_integer_inputs_bit_exact(G, n, dm):
     x, wq, wk = int_inputs(G * 1000 + n, n, dm, G)
     log(f"case project int G={G} n={n} d_model={dm}")
