@@ -154,9 +154,9 @@ def pair_stats(torch, sel, n, bk=BK, d=D, hpg=HQ // G, window=65536):
 # (profiles/bench_step_hbm_bytes.txt). Valid only for the kernel sources they
 # were taken on: keyed by the hash that source_hash() computes.
 MEASURED_TRAFFIC = {
-    "source": "5a2f194388fc0724",
-    "k_attn_prefill (KV-outer)": 4.169e9,
-    "k_attn_dense (dense + merge)": 3.517e9,
+    "source": "84c9f377dc1e50b0",
+    "k_attn_prefill (KV-outer)": 4.175e9,
+    "k_attn_dense (dense + merge)": 3.520e9,
 }
 
 
