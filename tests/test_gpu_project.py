@@ -130,6 +130,29 @@ def test_decode_appends_key_at_context_end():
         assert (rest == 7.0).all(), f"seq {b}: a row other than {L - 1} changed"
 
 
+def test_decode_append_many_sequences():
+    """A decode step of 8200 sequences (enough for the many-token kernel, with
+    d_model a multiple of 256): each key lands in its own sequence's row
+    ctx_lens[b] - 1 and no other cache row changes."""
+    G, B, max_ctx, dm = 4, 8200, 3, 256
+    x, wq, wk = int_inputs(17, B, dm, G, -2, 2)
+    g = torch.Generator().manual_seed(3)
+    lt_h = torch.randint(1, max_ctx + 1, (B,), generator=g, dtype=torch.int32)
+    cache = torch.full((B, max_ctx, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    log(f"case project decode B={B} d_model={dm}")
+    qi = msa.index_project_decode(x.cuda(), wq.cuda(), wk.cuda(), cache, lt_h.cuda())
+    torch.cuda.synchronize()
+    q, k = po.index_project(f64(x), f64(wq), f64(wk))
+    assert np.array_equal(f64(qi), po.round_bf16(q))
+    c = f64(cache)
+    lens = lt_h.numpy().astype(np.int64)
+    rows = np.arange(B)
+    assert np.array_equal(c[rows, lens - 1], po.round_bf16(k))
+    untouched = np.ones((B, max_ctx), dtype=bool)
+    untouched[rows, lens - 1] = False
+    assert (c[untouched] == 7.0).all(), "a row other than ctx_lens - 1 changed"
+
+
 def test_projection_feeds_prefill_selection_exactly():
     """Hidden states -> projections -> prefill: with {-1, 0, 1} inputs and
     d_model 64 the projected heads are small integers (exact in bf16), so the
