@@ -80,7 +80,7 @@ def test_integer_inputs_bit_exact(G, n, dm):
     assert bad.size == 0, f"k_idx differs at {bad[:5].tolist()}"
 
 
-@pytest.mark.parametrize("G,n,dm", [(4, 64, 8192), (4, 33024, 2048), (3, 500, 6144)])
+@pytest.mark.parametrize("G,n,dm", [(4, 64, 8192), (4, 33024, 2048), (3, 500, 6144), (8, 8200, 1024), (1, 16500, 512)])
 def test_normal_inputs_within_bound(G, n, dm):
     x, wq, wk = normal_inputs(7 + n, n, dm, G)
     log(f"case project normal G={G} n={n} d_model={dm}")
